@@ -1,0 +1,211 @@
+"""Python binding of libattnres (AttnRes depth aggregation on MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attnres.h``.  PyTorch supplies
+device memory and the current stream.  There is no fallback: if the library
+is not built, importing this module raises.
+
+Layouts (see the header): ``hist [n_hist, T, d]`` (bf16 or fp32), pseudo-queries
+``w [n_q, d]`` fp32 (row j is read ``q_begin + j``), ``out [n_q, T, d]``,
+``lse [n_q, T]`` fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import _build
+
+LIBRARY = _build.LIBRARY
+
+F32, BF16 = 0, 1
+FULL, BLOCK = 0, 1
+
+STATUS = {0: "ATTNRES_OK", 1: "ATTNRES_ERR_INVALID_ARG", 2: "ATTNRES_ERR_UNSUPPORTED",
+          3: "ATTNRES_ERR_ALIGN", 4: "ATTNRES_ERR_WORKSPACE", 5: "ATTNRES_ERR_HIP"}
+
+# every symbol include/attnres.h declares
+EXPORTS = ["attnres_full_fwd", "attnres_block_fwd", "attnres_bwd", "attnres_bwd_workspace_bytes",
+           "attnres_block_index_table", "attnres_status_string", "attnres_last_error"]
+
+if not os.path.exists(LIBRARY):
+    raise ImportError(f"libattnres.so is not built ({LIBRARY}); run __graft_entry__.build()")
+
+_lib = ctypes.CDLL(LIBRARY)
+
+_i64, _f32, _int, _vp, _sz = (ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
+                              ctypes.c_size_t)
+_lib.attnres_full_fwd.restype = _int
+_lib.attnres_full_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp, _i64,
+                                  _vp, _int, _vp, _vp]
+_lib.attnres_block_fwd.restype = _int
+_lib.attnres_block_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp,
+                                   _int, _vp, _vp]
+_lib.attnres_bwd.restype = _int
+_lib.attnres_bwd.argtypes = [_int, _i64, _vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp,
+                             _vp, _int, _vp, _int, _vp, _vp, _sz, _vp]
+_lib.attnres_bwd_workspace_bytes.restype = _sz
+_lib.attnres_bwd_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _i64, _i64, _i64]
+_lib.attnres_block_index_table.restype = _int
+_lib.attnres_block_index_table.argtypes = [_i64, _i64, _i64, _i64, _vp]
+_lib.attnres_status_string.restype = ctypes.c_char_p
+_lib.attnres_status_string.argtypes = [_int]
+_lib.attnres_last_error.restype = ctypes.c_char_p
+_lib.attnres_last_error.argtypes = []
+
+
+class AttnResError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def last_error() -> str:
+    return _lib.attnres_last_error().decode()
+
+
+def status_string(status: int) -> str:
+    return _lib.attnres_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise AttnResError(status, last_error())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _torch_dtype(code: int):
+    import torch
+    return torch.float32 if code == F32 else torch.bfloat16
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require(t, name, *, dtype=None, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def full_fwd(hist, w, *, q_begin: int = 0, n_q: int | None = None, eps: float = 1e-6,
+             rinv=None, rinv_valid_rows: int = 0, out=None, out_dtype=None, lse=None,
+             want_lse: bool = True):
+    """Full AttnRes reads q_begin .. q_begin+n_q-1.  Returns (out, lse)."""
+    import torch
+    _require(hist, "hist")
+    n_hist, T, d = hist.shape
+    n_q = n_hist - q_begin if n_q is None else n_q
+    _require(w, "w", dtype=torch.float32, shape=(n_q, d))
+    odt = _dtype_code(hist) if out_dtype is None else (F32 if out_dtype == torch.float32 else BF16)
+    if out is None:
+        out = torch.empty((n_q, T, d), dtype=_torch_dtype(odt), device=hist.device)
+    else:
+        _require(out, "out", shape=(n_q, T, d))
+        odt = _dtype_code(out)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, T), dtype=torch.float32, device=hist.device)
+    if lse is not None:
+        _require(lse, "lse", dtype=torch.float32, shape=(n_q, T))
+    if rinv is not None:
+        _require(rinv, "rinv", dtype=torch.float32, shape=(n_hist, T))
+    _check(_lib.attnres_full_fwd(_ptr(hist), _dtype_code(hist), n_hist, T, d, _ptr(w), q_begin,
+                                 n_q, eps, _ptr(rinv), rinv_valid_rows, _ptr(out), odt, _ptr(lse),
+                                 _stream(hist)))
+    return out, lse
+
+
+def block_fwd(hist, w, S: int, *, q_begin: int = 0, n_q: int | None = None, eps: float = 1e-6,
+              out=None, out_dtype=None, lse=None, want_lse: bool = True):
+    """Block AttnRes reads (block size S), two-phase.  Returns (out, lse)."""
+    import torch
+    _require(hist, "hist")
+    n_hist, T, d = hist.shape
+    n_q = n_hist - q_begin if n_q is None else n_q
+    _require(w, "w", dtype=torch.float32, shape=(n_q, d))
+    odt = _dtype_code(hist) if out_dtype is None else (F32 if out_dtype == torch.float32 else BF16)
+    if out is None:
+        out = torch.empty((n_q, T, d), dtype=_torch_dtype(odt), device=hist.device)
+    else:
+        _require(out, "out", shape=(n_q, T, d))
+        odt = _dtype_code(out)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, T), dtype=torch.float32, device=hist.device)
+    if lse is not None:
+        _require(lse, "lse", dtype=torch.float32, shape=(n_q, T))
+    _check(_lib.attnres_block_fwd(_ptr(hist), _dtype_code(hist), n_hist, T, d, S, _ptr(w),
+                                  q_begin, n_q, eps, _ptr(out), odt, _ptr(lse), _stream(hist)))
+    return out, lse
+
+
+def bwd_workspace_bytes(variant: int, S: int, n_hist: int, T: int, d: int, q_begin: int,
+                        n_q: int) -> int:
+    return int(_lib.attnres_bwd_workspace_bytes(variant, S, n_hist, T, d, q_begin, n_q))
+
+
+def bwd(variant: int, hist, w, lse, dout, *, S: int = 1, q_begin: int = 0, eps: float = 1e-6,
+        dhist=None, dhist_dtype=None, dw=None, workspace=None):
+    """Gradients of sum(out * dout) w.r.t. hist and w.  Returns (dhist, dw)."""
+    import torch
+    _require(hist, "hist")
+    n_hist, T, d = hist.shape
+    n_q = dout.shape[0]
+    _require(w, "w", dtype=torch.float32, shape=(n_q, d))
+    _require(lse, "lse", dtype=torch.float32, shape=(n_q, T))
+    _require(dout, "dout", shape=(n_q, T, d))
+    ddt = _dtype_code(hist) if dhist_dtype is None else (F32 if dhist_dtype == torch.float32 else BF16)
+    if dhist is None:
+        dhist = torch.empty((n_hist, T, d), dtype=_torch_dtype(ddt), device=hist.device)
+    else:
+        _require(dhist, "dhist", shape=(n_hist, T, d))
+        ddt = _dtype_code(dhist)
+    if dw is None:
+        dw = torch.empty((n_q, d), dtype=torch.float32, device=hist.device)
+    _require(dw, "dw", dtype=torch.float32, shape=(n_q, d))
+    need = bwd_workspace_bytes(variant, S, n_hist, T, d, q_begin, n_q)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=hist.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.attnres_bwd(variant, S, _ptr(hist), _dtype_code(hist), n_hist, T, d, _ptr(w),
+                            q_begin, n_q, eps, _ptr(lse), _ptr(dout), _dtype_code(dout),
+                            _ptr(dhist), ddt, _ptr(dw), _ptr(workspace), ws_bytes,
+                            _stream(hist)))
+    return dhist, dw
+
+
+def block_index_table(n_hist: int, S: int, q_begin: int = 0, n_q: int | None = None) -> np.ndarray:
+    """[n_q, 3] int32: (completed blocks, partial begin row, partial end row)."""
+    n_q = n_hist - q_begin if n_q is None else n_q
+    out = np.zeros((max(n_q, 0), 3), dtype=np.int32)
+    _check(_lib.attnres_block_index_table(n_hist, S, q_begin, n_q,
+                                          out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def raw():
+    """The ctypes handle of the C library (for tests of the raw ABI)."""
+    return _lib

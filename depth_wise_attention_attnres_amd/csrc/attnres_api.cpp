@@ -1,0 +1,180 @@
+// attnres_api.cpp -- C-ABI front end of libattnres: argument validation on
+// the host (before any HIP call), the Block index table, status strings and
+// the thread-local error detail, then dispatch to the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <cinttypes>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "attnres.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return ATTNRES_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_dtype(int dt) { return dt == ATTNRES_F32 || dt == ATTNRES_BF16; }
+
+// checks shared by every entry point; returns ATTNRES_OK or an error status
+int check_common(const char* fn, const void* hist, int hist_dt, int64_t n_hist, int64_t T,
+                 int64_t d, const float* w, int64_t q_begin, int64_t n_q, float eps) {
+    if (!valid_dtype(hist_dt)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad hist dtype %d", fn, hist_dt);
+    if (n_hist < 1) return fail(ATTNRES_ERR_INVALID_ARG, "%s: n_hist must be >= 1 (got %" PRId64 ")", fn, n_hist);
+    if (T < 0) return fail(ATTNRES_ERR_INVALID_ARG, "%s: T must be >= 0 (got %" PRId64 ")", fn, T);
+    if (d < 1) return fail(ATTNRES_ERR_INVALID_ARG, "%s: d must be >= 1 (got %" PRId64 ")", fn, d);
+    if (q_begin < 0 || n_q < 0 || q_begin + n_q > n_hist)
+        return fail(ATTNRES_ERR_INVALID_ARG,
+                    "%s: reads [%" PRId64 ", %" PRId64 ") outside the history of %" PRId64 " rows",
+                    fn, q_begin, q_begin + n_q, n_hist);
+    if (!(eps >= 0.f) || !std::isfinite(eps))
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+    if (d % 8 != 0) return fail(ATTNRES_ERR_ALIGN, "%s: d = %" PRId64 " is not a multiple of 8", fn, d);
+    if (d > attnres::kMaxD)
+        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: d = %" PRId64 " exceeds %d", fn, d, attnres::kMaxD);
+    if (n_hist > (int64_t)1 << 20)
+        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: n_hist = %" PRId64 " too large", fn, n_hist);
+    // every element offset must fit int64 comfortably
+    if (T > ((int64_t)1 << 40) / (n_hist * d))
+        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: history of %" PRId64 " x %" PRId64 " x %" PRId64 " too large",
+                    fn, n_hist, T, d);
+    if (T > 0 && n_q > 0) {
+        if (hist == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: hist is NULL", fn);
+        if (w == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: w is NULL", fn);
+        if (!aligned(hist, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: hist is not 16-byte aligned", fn);
+        if (!aligned(w, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: w is not 16-byte aligned", fn);
+    }
+    return ATTNRES_OK;
+}
+
+int hip_status(const char* fn, hipError_t e) {
+    if (e != hipSuccess)
+        return fail(ATTNRES_ERR_HIP, "%s: %s (%s)", fn, hipGetErrorName(e), hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attnres_status_string(int status) {
+    switch (status) {
+        case ATTNRES_OK: return "ATTNRES_OK: success";
+        case ATTNRES_ERR_INVALID_ARG: return "ATTNRES_ERR_INVALID_ARG: invalid argument";
+        case ATTNRES_ERR_UNSUPPORTED: return "ATTNRES_ERR_UNSUPPORTED: size not supported";
+        case ATTNRES_ERR_ALIGN: return "ATTNRES_ERR_ALIGN: d % 8 != 0 or misaligned pointer";
+        case ATTNRES_ERR_WORKSPACE: return "ATTNRES_ERR_WORKSPACE: workspace missing or too small";
+        case ATTNRES_ERR_HIP: return "ATTNRES_ERR_HIP: HIP runtime error";
+        default: return "unknown attnres status";
+    }
+}
+
+const char* attnres_last_error(void) { return g_last_error; }
+
+int attnres_block_index_table(int64_t n_hist, int64_t S, int64_t q_begin, int64_t n_q,
+                              int32_t* out) {
+    const char* fn = "attnres_block_index_table";
+    if (n_hist < 1 || n_hist > INT32_MAX) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad n_hist", fn);
+    if (S < 1) return fail(ATTNRES_ERR_INVALID_ARG, "%s: S must be >= 1", fn);
+    if (q_begin < 0 || n_q < 0 || q_begin + n_q > n_hist)
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: reads outside the history", fn);
+    if (n_q > 0 && out == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    for (int64_t j = 0; j < n_q; ++j) {
+        const int64_t l = q_begin + j;
+        const int64_t m = l / S;
+        out[3 * j + 0] = (int32_t)m;
+        out[3 * j + 1] = (int32_t)(m * S + 1);
+        out[3 * j + 2] = (int32_t)(l + 1);
+    }
+    return ok();
+}
+
+int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
+                     int64_t d, const float* w, int64_t q_begin, int64_t n_q, float eps,
+                     float* rinv, int64_t rinv_valid_rows, void* out, attnres_dtype out_dtype,
+                     float* lse, hipStream_t stream) {
+    const char* fn = "attnres_full_fwd";
+    int st = check_common(fn, hist, hist_dtype, n_hist, T, d, w, q_begin, n_q, eps);
+    if (st != ATTNRES_OK) return st;
+    if (!valid_dtype(out_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad out dtype %d", fn, (int)out_dtype);
+    if (rinv_valid_rows < 0 || rinv_valid_rows > n_hist)
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: rinv_valid_rows = %" PRId64 " outside [0, n_hist]", fn,
+                    rinv_valid_rows);
+    if (rinv == nullptr && rinv_valid_rows != 0)
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: rinv_valid_rows > 0 needs a rinv cache", fn);
+    if (T == 0 || n_q == 0) return ok();
+    if (out == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (!aligned(out, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: out is not 16-byte aligned", fn);
+    if (lse != nullptr && !aligned(lse, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse is not 4-byte aligned", fn);
+    if (rinv != nullptr && !aligned(rinv, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: rinv is not 4-byte aligned", fn);
+
+    attnres::FullFwdParams p;
+    p.hist = hist;
+    p.w = w;
+    p.rinv = rinv;
+    p.out = out;
+    p.lse = lse;
+    p.T = T;
+    p.d = (int)d;
+    p.nc = (int)(d / 8);
+    p.n_hist = (int)n_hist;
+    p.q_begin = (int)q_begin;
+    p.n_q = (int)n_q;
+    p.rinv_valid = (int)rinv_valid_rows;
+    p.eps = eps;
+    p.inv_d = 1.0f / (float)d;
+    return hip_status(fn, attnres::launch_full_fwd(p, hist_dtype, out_dtype, stream));
+}
+
+int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
+                      int64_t d, int64_t S, const float* w, int64_t q_begin, int64_t n_q,
+                      float eps, void* out, attnres_dtype out_dtype, float* lse,
+                      hipStream_t stream) {
+    const char* fn = "attnres_block_fwd";
+    int st = check_common(fn, hist, hist_dtype, n_hist, T, d, w, q_begin, n_q, eps);
+    if (st != ATTNRES_OK) return st;
+    if (S < 1) return fail(ATTNRES_ERR_INVALID_ARG, "%s: S must be >= 1 (got %" PRId64 ")", fn, S);
+    if (!valid_dtype(out_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad out dtype %d", fn, (int)out_dtype);
+    if (T == 0 || n_q == 0) return ok();
+    if (out == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (!aligned(out, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: out is not 16-byte aligned", fn);
+    if (lse != nullptr && !aligned(lse, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse is not 4-byte aligned", fn);
+    (void)stream;
+    return fail(ATTNRES_ERR_UNSUPPORTED, "%s: not built yet", fn);
+}
+
+size_t attnres_bwd_workspace_bytes(attnres_variant variant, int64_t S, int64_t n_hist, int64_t T,
+                                   int64_t d, int64_t q_begin, int64_t n_q) {
+    (void)variant; (void)S; (void)n_hist; (void)T; (void)d; (void)q_begin; (void)n_q;
+    return 0;
+}
+
+int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dtype hist_dtype,
+                int64_t n_hist, int64_t T, int64_t d, const float* w, int64_t q_begin, int64_t n_q,
+                float eps, const float* lse, const void* dout, attnres_dtype dout_dtype, void* dhist,
+                attnres_dtype dhist_dtype, float* dw, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+    (void)variant; (void)S; (void)hist; (void)hist_dtype; (void)n_hist; (void)T; (void)d; (void)w;
+    (void)q_begin; (void)n_q; (void)eps; (void)lse; (void)dout; (void)dout_dtype; (void)dhist;
+    (void)dhist_dtype; (void)dw; (void)workspace; (void)workspace_bytes; (void)stream;
+    return fail(ATTNRES_ERR_UNSUPPORTED, "attnres_bwd: not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+// device_common.hpp -- gfx950 device helpers shared by the AttnRes kernels.
+//
+// Data movement is in 16-byte chunks of 8 elements along d: a bf16 chunk is
+// one dwordx4 load, an fp32 chunk two.  A "token group" (TG) of LPT lanes
+// (LPT in {16, 32, 64}) owns one token; lane `ln` of the group owns chunks
+// ln, ln + LPT, ln + 2 LPT, ... so that one load instruction of the group
+// touches LPT * 16 contiguous bytes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnres {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// element types
+
+struct bf16_t {
+    uint16_t bits;
+};
+
+// native clang vectors (the nontemporal builtins need them)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// buffer addressing.  Every row access goes through a buffer resource whose
+// base is wave-uniform (SGPRs) and whose range check turns out-of-range lanes
+// into zero loads and dropped stores: a lane whose chunk lies past d, or whose
+// token lies past T, is given the offset kOOB.
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr uint32_t kOOB = 0x40000000u;   // >= every num_records we build
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9-family raw buffer, 32-bit data
+constexpr int kAuxNT = 2;                // non-temporal cache policy
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+    const uint32_t n = bytes < kOOB ? (uint32_t)bytes : kOOB;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
+                                             (int)kRsrcWord3);
+}
+
+// 8 elements of a history / gradient row
+template <typename T> struct Chunk;
+
+template <> struct Chunk<bf16_t> {
+    u32x4 v;  // 8 bf16, little-endian pairs
+    __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
+    template <int AUX = 0>
+    __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
+        v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    }
+    __device__ __forceinline__ void to_float(float (&f)[8]) const {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f[2 * q] = __uint_as_float(v[q] << 16);
+            f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
+        }
+    }
+};
+
+template <> struct Chunk<float> {
+    u32x4 a, b;
+    __device__ __forceinline__ void zero() {
+        a = u32x4{0u, 0u, 0u, 0u};
+        b = a;
+    }
+    template <int AUX = 0>
+    __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
+        a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+        b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, AUX);
+    }
+    __device__ __forceinline__ void to_float(float (&f)[8]) const {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f[q] = __uint_as_float(a[q]);
+            f[4 + q] = __uint_as_float(b[q]);
+        }
+    }
+};
+
+// round-to-nearest-even fp32 -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950)
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float float2_v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    float2_v f = {lo, hi};
+    bf16x2_v b = __builtin_convertvector(f, bf16x2_v);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+template <int AUX = 0>
+__device__ __forceinline__ void store_chunk(bf16_t*, rsrc_t r, uint32_t off, const float (&f)[8]) {
+    u32x4 v = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+               pack_bf16x2(f[6], f[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, AUX);
+}
+
+template <int AUX = 0>
+__device__ __forceinline__ void store_chunk(float*, rsrc_t r, uint32_t off, const float (&f)[8]) {
+    u32x4 a = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+               __float_as_uint(f[3])};
+    u32x4 b = {__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
+               __float_as_uint(f[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, AUX);
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, off + 16, 0, AUX);
+}
+
+__device__ __forceinline__ float load_f32(rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void store_f32(rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane sums inside a token group of LPT lanes (all lanes get the sum).
+// Within a 16-lane row: DPP butterflies (xor 1, xor 2, half-row mirror, row
+// mirror); across rows: the gfx950 row-swap permutes.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+// sum over lanes l and l ^ 16 (rows 0<->1, 2<->3)
+__device__ __forceinline__ float swap16_sum(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// sum over lanes l and l ^ 32 (upper and lower half of the wave)
+__device__ __forceinline__ float swap32_sum(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int LPT>
+__device__ __forceinline__ float tg_sum(float v) {
+    static_assert(LPT == 16 || LPT == 32 || LPT == 64, "token group of 16, 32 or 64 lanes");
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);
+    if constexpr (LPT >= 32) v = swap16_sum(v);
+    if constexpr (LPT >= 64) v = swap32_sum(v);
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+}  // namespace attnres

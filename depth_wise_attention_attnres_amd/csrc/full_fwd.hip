@@ -1,0 +1,207 @@
+// full_fwd.hip -- Full AttnRes forward on gfx950.
+//
+// One read l of one token ("DepthBench reading notes" sec. 2.3): scores
+// s_i = r(v_i) (w_l . v_i) over rows i = 0..l, softmax over depth, and
+// h_l = sum_i softmax_i v_i.  The kernel streams the rows of each token once
+// per read, in depth order, with an online softmax (running max m, running
+// sum Z, fp32 accumulator), so every row is read from HBM once per read and
+// nothing but the output is written.  The RMS scale r(v_i) comes from the
+// caller's cache when valid, else from the sum of squares of the row already
+// in registers (and is then written back to the cache).
+//
+// Thread mapping: a token group (TG) of LPT lanes per token, NCH 16-byte
+// chunks per lane (see device_common.hpp); 256-thread blocks hold 256/LPT
+// consecutive tokens.  Row accesses are buffer loads from a wave-uniform row
+// base; loads of the next PF rows are in flight while a row is consumed.  The
+// max is rescaled lazily: only when a new score exceeds it.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace attnres {
+
+template <typename TI, typename TO, int LPT, int NCH, int PF>
+__global__ __launch_bounds__(256) void full_fwd_stream_kernel(FullFwdParams p) {
+    constexpr int TPB = 256 / LPT;  // tokens per block
+    const int ln = threadIdx.x % LPT;
+    const int64_t tok0 = (int64_t)blockIdx.x * TPB;
+    const int tl = threadIdx.x / LPT;  // token within the block
+    const int64_t t = tok0 + tl;
+    if (t >= p.T) return;  // whole token groups leave together
+
+    const int64_t row_elems = p.T * (int64_t)p.d;            // elements between rows
+    const uint64_t blk_elems = (uint64_t)(p.T - tok0) * p.d;  // this block's tokens to the end
+    const TI* hist_blk = static_cast<const TI*>(p.hist) + tok0 * p.d;
+    TO* out_blk = static_cast<TO*>(p.out) + tok0 * p.d;
+
+    // byte offsets of this lane's chunks inside the block's slice of a row;
+    // chunks past d get kOOB (loads read zeros, stores are dropped)
+    uint32_t in_off[NCH], out_off[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int ch = c * LPT + ln;
+        const uint32_t e = (uint32_t)(tl * p.d + ch * 8);
+        in_off[c] = ch < p.nc ? e * (uint32_t)sizeof(TI) : kOOB;
+        out_off[c] = ch < p.nc ? e * (uint32_t)sizeof(TO) : kOOB;
+    }
+    const uint32_t tok_f32_off = (uint32_t)tl * 4u;
+
+    for (int j = 0; j < p.n_q; ++j) {
+        const int l = p.q_begin + j;
+        float wv[NCH][8];
+        {
+            const rsrc_t wr = make_rsrc(p.w + (int64_t)j * p.d, (uint64_t)p.d * 4);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const uint32_t off = in_off[c] == kOOB ? kOOB : (uint32_t)((c * LPT + ln) * 32);
+                Chunk<float> ch;
+                ch.load(wr, off);
+                ch.to_float(wv[c]);
+            }
+        }
+
+        float acc[NCH][8];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+        float m2 = -INFINITY;  // running max of scores, log2 domain
+        float Z = 0.f;         // running sum of exp2(s2 - m2)
+
+        // ring of PF prefetched rows (and their cached scales)
+        Chunk<TI> buf[PF][NCH];
+        float rbuf[PF];
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            rbuf[u] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) buf[u][c].zero();
+        }
+        auto issue = [&](int u, int i) {
+            const rsrc_t rr = make_rsrc(hist_blk + i * row_elems, blk_elems * sizeof(TI));
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) buf[u][c].load(rr, in_off[c]);
+            if (i < p.rinv_valid) {
+                const rsrc_t cr = make_rsrc(p.rinv + (int64_t)i * p.T + tok0, (uint64_t)(p.T - tok0) * 4);
+                rbuf[u] = load_f32(cr, tok_f32_off);
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < PF; ++u)
+            if (u <= l) issue(u, u);
+
+        for (int i0 = 0; i0 <= l; i0 += PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const int i = i0 + u;
+                if (i > l) break;
+                float xf[NCH][8];
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) buf[u][c].to_float(xf[c]);
+                const float rc = rbuf[u];
+                if (i + PF <= l) issue(u, i + PF);
+
+                const bool need_sq = i >= p.rinv_valid;  // uniform over the grid
+                float dp = 0.f, sq = 0.f;
+                if (need_sq) {
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            dp = fmaf(wv[c][e], xf[c][e], dp);
+                            sq = fmaf(xf[c][e], xf[c][e], sq);
+                        }
+                    dp = tg_sum<LPT>(dp);
+                    sq = tg_sum<LPT>(sq);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) dp = fmaf(wv[c][e], xf[c][e], dp);
+                    dp = tg_sum<LPT>(dp);
+                }
+                float r = rc;
+                if (need_sq) {
+                    r = fast_rsqrt(fmaf(sq, p.inv_d, p.eps));
+                    // cache row i is written once per call, by the first read of
+                    // the call that sees it
+                    const int owner = i - p.q_begin > 0 ? i - p.q_begin : 0;
+                    if (p.rinv != nullptr && j == owner && ln == 0)
+                        p.rinv[(int64_t)i * p.T + t] = r;
+                }
+                const float s2 = r * dp * kLog2e;
+                if (s2 > m2) {  // new running max: rescale what is accumulated
+                    const float cs = fast_exp2(m2 - s2);
+                    Z *= cs;
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[c][e] *= cs;
+                    m2 = s2;
+                }
+                const float pw = fast_exp2(s2 - m2);
+                Z += pw;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[c][e] = fmaf(pw, xf[c][e], acc[c][e]);
+            }
+        }
+
+        const float inv_z = 1.0f / Z;
+        const rsrc_t orr = make_rsrc(out_blk + (int64_t)j * row_elems, blk_elems * sizeof(TO));
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = acc[c][e] * inv_z;
+            store_chunk((TO*)nullptr, orr, out_off[c], o);
+        }
+        if (p.lse != nullptr && ln == 0) p.lse[(int64_t)j * p.T + t] = (m2 + fast_log2(Z)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launch selection
+
+namespace {
+
+template <typename TI, typename TO, int LPT, int NCH, int PF>
+hipError_t launch_stream(const FullFwdParams& p, hipStream_t stream) {
+    constexpr int TPB = 256 / LPT;
+    const int64_t blocks = (p.T + TPB - 1) / TPB;
+    hipLaunchKernelGGL((full_fwd_stream_kernel<TI, TO, LPT, NCH, PF>), dim3((unsigned)blocks),
+                       dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename TI, typename TO>
+hipError_t dispatch_stream(const FullFwdParams& p, hipStream_t stream) {
+    // LPT = 64 lanes per token, NCH chunks per lane: one token per wave
+    const int nch = (p.nc + 63) / 64;
+    switch (nch) {
+        case 1: return launch_stream<TI, TO, 64, 1, 4>(p, stream);
+        case 2: return launch_stream<TI, TO, 64, 2, 4>(p, stream);
+        case 3: return launch_stream<TI, TO, 64, 3, 3>(p, stream);
+        case 4: return launch_stream<TI, TO, 64, 4, 2>(p, stream);
+        case 5: return launch_stream<TI, TO, 64, 5, 2>(p, stream);
+        case 6: return launch_stream<TI, TO, 64, 6, 2>(p, stream);
+        case 7: return launch_stream<TI, TO, 64, 7, 2>(p, stream);
+        case 8: return launch_stream<TI, TO, 64, 8, 1>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_full_fwd(const FullFwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
+                           hipStream_t stream) {
+    if (hist_dt == ATTNRES_BF16 && out_dt == ATTNRES_BF16)
+        return dispatch_stream<bf16_t, bf16_t>(p, stream);
+    if (hist_dt == ATTNRES_BF16 && out_dt == ATTNRES_F32)
+        return dispatch_stream<bf16_t, float>(p, stream);
+    if (hist_dt == ATTNRES_F32 && out_dt == ATTNRES_F32)
+        return dispatch_stream<float, float>(p, stream);
+    return dispatch_stream<float, bf16_t>(p, stream);
+}
+
+}  // namespace attnres

@@ -1,0 +1,172 @@
+/*
+ * attnres.h -- C ABI of libattnres, the MI355X (gfx950) implementation of the
+ * Attention Residuals (AttnRes) depth aggregation.
+ *
+ * The operation (cited by page title and section):
+ *   "DepthBench reading notes" (arXiv 2609.32534 notes), sec. 2.3 "Full
+ *   AttnRes": for one token, with v_0 the embedding and v_i the raw output of
+ *   sublayer i, a read with learned pseudo-query w scores every earlier source
+ *   by e_i = w^T RMSNorm(v_i) (no 1/sqrt(d), temperature 1), takes a softmax
+ *   over depth and returns z = sum_i a_i v_i over the raw values.
+ *   "LLMRes" post (wln20), section "Kimi AttnRes": the same read with the
+ *   query independent of the input, keys = values = earlier outputs, and the
+ *   Block variant: additive sums inside a block, attention over block
+ *   summaries.
+ *   DataCamp "Attention Residuals explained", block section and the
+ *   "two-phase computation" bullet: a Block read attends over the embedding,
+ *   the completed block summaries and the running partial sum of the current
+ *   block; phase 1 batches the reads of a block over the frozen sources,
+ *   phase 2 merges the partial sum with an online softmax.
+ *
+ * Conventions used by every entry point:
+ *   hist   [n_hist][T][d]  history rows: row 0 is the embedding, row i >= 1 the
+ *                          output of sublayer i; d fastest, tokens next.
+ *   w      [n_q][d] fp32   pseudo-queries of the reads this call computes; row j
+ *                          belongs to read l = q_begin + j.  Any per-read gain of
+ *                          the key RMSNorm is folded into w by the caller
+ *                          (w * g), since r(x) (g o x) . w = r(x) x . (g o w).
+ *   read l sees history rows 0..l: read 0 returns the embedding, read n_hist-1
+ *                          is the final (LM-head) read over everything.
+ *   RMSNorm of a key x:    r(x) = 1 / sqrt(sum_k x_k^2 / d + eps), unit gain.
+ *   out    [n_q][T][d]     h_l for each read of the call.
+ *   lse    [n_q][T] fp32   log-sum-exp of the read's scores (for the backward);
+ *                          may be NULL.
+ *   Block size S counts sublayer outputs: block c (c >= 1) is rows
+ *   (c-1)S+1 .. cS.  Read l with m = floor(l/S) sees v_0, the block sums
+ *   b_1..b_m, and the partial sum p_l = v_{mS+1} + ... + v_l when l mod S != 0.
+ *   Block sums and partial sums are kept in fp32, never rounded to bf16.
+ *
+ * Memory and execution:
+ *   * All tensor pointers are device pointers owned by the caller; the library
+ *     allocates no device memory and keeps no state between calls apart from
+ *     the thread-local error string.  The backward's scratch is caller-supplied.
+ *   * d must be a multiple of 8 (8 <= d <= 4096); hist, out, dout, dhist and w
+ *     must be 16-byte aligned, lse / rinv / dw 4-byte aligned.
+ *   * Calls validate every argument on the host before any launch and return
+ *     synchronously on error; on success the work is enqueued on `stream`
+ *     (asynchronous).  Outputs must not alias inputs.
+ *   * T == 0 or n_q == 0 is a valid empty call: nothing is launched.
+ *   * NaN / Inf inputs propagate; they are not checked.
+ *   * Thread-safe: calls share no mutable state.
+ *
+ * Status: every entry point returns an attnres_status; attnres_last_error()
+ * gives a human-readable detail of the last failure on the calling thread.
+ */
+#ifndef ATTNRES_H_
+#define ATTNRES_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attnres_dtype {
+    ATTNRES_F32 = 0,
+    ATTNRES_BF16 = 1
+} attnres_dtype;
+
+typedef enum attnres_status {
+    ATTNRES_OK = 0,
+    ATTNRES_ERR_INVALID_ARG = 1, /* a size, index, null pointer or dtype is wrong */
+    ATTNRES_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels handle     */
+    ATTNRES_ERR_ALIGN = 3,       /* d % 8 != 0 or a pointer is misaligned         */
+    ATTNRES_ERR_WORKSPACE = 4,   /* backward workspace missing or too small       */
+    ATTNRES_ERR_HIP = 5          /* a HIP launch or runtime call failed           */
+} attnres_status;
+
+typedef enum attnres_variant {
+    ATTNRES_FULL = 0,
+    ATTNRES_BLOCK = 1
+} attnres_variant;
+
+/*
+ * Full AttnRes forward ("DepthBench reading notes" sec. 2.3; "LLMRes",
+ * "Kimi AttnRes"): for j in [0, n_q) and every token, read l = q_begin + j
+ * over history rows 0..l.
+ *
+ *   hist, hist_dtype   [n_hist][T][d], F32 or BF16
+ *   w                  [n_q][d] fp32
+ *   q_begin, n_q       reads l = q_begin .. q_begin + n_q - 1 (q_begin + n_q <= n_hist)
+ *   eps                RMSNorm epsilon (>= 0)
+ *   rinv               optional [n_hist][T] fp32 cache of r(v_i) per (row, token).
+ *                      Rows i < rinv_valid_rows are read from it and trusted;
+ *                      rows rinv_valid_rows <= i < q_begin + n_q are computed in
+ *                      the same pass and written to it, so a model that calls
+ *                      read by read (q_begin = l, n_q = 1, rinv_valid_rows = l)
+ *                      normalises every history row exactly once.  NULL: all
+ *                      scales are computed on the fly (rinv_valid_rows must be 0).
+ *   out, out_dtype     [n_q][T][d], F32 or BF16 (rounded once, to nearest even)
+ *   lse                optional [n_q][T] fp32
+ */
+int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
+                     int64_t T, int64_t d, const float* w, int64_t q_begin,
+                     int64_t n_q, float eps, float* rinv, int64_t rinv_valid_rows,
+                     void* out, attnres_dtype out_dtype, float* lse,
+                     hipStream_t stream);
+
+/*
+ * Block AttnRes forward, two-phase ("DepthBench reading notes" sec. 2.5;
+ * "LLMRes", Block paragraph; DataCamp, block section and "two-phase
+ * computation"): reads l = q_begin .. q_begin + n_q - 1 with block size S
+ * (S >= 1; S = 1 is Full AttnRes).  The raw history is read once; block sums
+ * and the partial sum are built on chip in fp32.  Arguments as in
+ * attnres_full_fwd, without the rinv cache.
+ */
+int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
+                      int64_t T, int64_t d, int64_t S, const float* w,
+                      int64_t q_begin, int64_t n_q, float eps, void* out,
+                      attnres_dtype out_dtype, float* lse, hipStream_t stream);
+
+/*
+ * Backward of attnres_full_fwd (variant ATTNRES_FULL) or attnres_block_fwd
+ * (ATTNRES_BLOCK, block size S) for the reads q_begin .. q_begin + n_q - 1.
+ * The pages state no gradient; this is the derivative of the forward
+ * (keys and values are the same tensors, so each row gets a value-path and a
+ * score-path term; block and partial sums pass their gradient to every row
+ * they contain).  Gradients are of sum(out * dout).
+ *
+ *   lse                [n_q][T] fp32 from the forward (required)
+ *   dout, dout_dtype   [n_q][T][d], F32 or BF16
+ *   dhist, dhist_dtype [n_hist][T][d], F32 or BF16: overwritten; rows no read of
+ *                      the call sees are set to zero
+ *   dw                 [n_q][d] fp32: overwritten (summed over tokens in a fixed
+ *                      order, so results are bitwise reproducible)
+ *   workspace          device scratch of at least attnres_bwd_workspace_bytes()
+ *                      bytes, 256-byte aligned; contents on entry are ignored
+ */
+int attnres_bwd(attnres_variant variant, int64_t S, const void* hist,
+                attnres_dtype hist_dtype, int64_t n_hist, int64_t T, int64_t d,
+                const float* w, int64_t q_begin, int64_t n_q, float eps,
+                const float* lse, const void* dout, attnres_dtype dout_dtype,
+                void* dhist, attnres_dtype dhist_dtype, float* dw, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace attnres_bwd needs for these sizes (0 on invalid sizes). */
+size_t attnres_bwd_workspace_bytes(attnres_variant variant, int64_t S, int64_t n_hist,
+                                   int64_t T, int64_t d, int64_t q_begin, int64_t n_q);
+
+/*
+ * Block index table (host only, no GPU work): for each read l = q_begin + j,
+ * writes out[3j + 0] = m = floor(l / S) (completed blocks),
+ * out[3j + 1] = first row of the partial sum (mS + 1),
+ * out[3j + 2] = one past its last row (l + 1; empty when equal to out[3j + 1]).
+ * `out` is host memory of 3 * n_q int32.
+ */
+int attnres_block_index_table(int64_t n_hist, int64_t S, int64_t q_begin, int64_t n_q,
+                              int32_t* out);
+
+/* Static description of a status code. */
+const char* attnres_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* attnres_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNRES_H_ */

@@ -16,3 +16,12 @@ def pytest_configure(config):
 def oracle():
     import oracle as _oracle
     return _oracle
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # name the case before any GPU work starts, so a run that dies mid-test
+    # still says which case it was in
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu case] {request.node.nodeid}", flush=True)
+    yield

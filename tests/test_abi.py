@@ -1,0 +1,143 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and rejects every invalid argument on the host before touching the GPU.
+No compute call is made here (there is no GPU in this container)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnres.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIPERR = 0, 1, 2, 3, 4, 5
+F32, BF16 = 0, 1
+
+# fake, well-aligned device addresses: validation never dereferences them
+P = 1 << 20
+P2 = 2 << 20
+P3 = 3 << 20
+
+
+@pytest.fixture(scope="module")
+def ar():
+    import depth_wise_attention_attnres_amd as ar
+    return ar
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(attnres_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for name in ["attnres_full_fwd", "attnres_block_fwd", "attnres_bwd"]:
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(ar):
+    lib = ctypes.CDLL(ar.LIBRARY)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert sorted(ar.EXPORTS) == declared_symbols()
+
+
+def _full(ar, hist=P, hdt=BF16, n_hist=4, T=16, d=64, w=P2, q_begin=0, n_q=4, eps=1e-6,
+          rinv=None, rvalid=0, out=P3, odt=BF16, lse=None):
+    return ar.raw().attnres_full_fwd(hist, hdt, n_hist, T, d, w, q_begin, n_q, eps, rinv, rvalid,
+                                     out, odt, lse, None)
+
+
+def test_full_fwd_validation(ar):
+    assert _full(ar, d=12) == ALIGN
+    assert "multiple of 8" in ar.last_error()
+    assert _full(ar, d=0) == INVALID
+    assert _full(ar, d=8192) == UNSUPPORTED
+    assert _full(ar, n_hist=0) == INVALID
+    assert _full(ar, T=-1) == INVALID
+    assert _full(ar, q_begin=1, n_q=4) == INVALID
+    assert "outside the history" in ar.last_error()
+    assert _full(ar, q_begin=-1) == INVALID
+    assert _full(ar, n_q=-1) == INVALID
+    assert _full(ar, hdt=7) == INVALID
+    assert _full(ar, odt=3) == INVALID
+    assert _full(ar, hist=None) == INVALID
+    assert _full(ar, w=None) == INVALID
+    assert _full(ar, out=None) == INVALID
+    assert _full(ar, hist=P + 8) == ALIGN
+    assert _full(ar, w=P2 + 4) == ALIGN
+    assert _full(ar, out=P3 + 2) == ALIGN
+    assert _full(ar, lse=P + 2) == ALIGN
+    assert _full(ar, rinv=P + 1, rvalid=0) == ALIGN
+    assert _full(ar, rinv=None, rvalid=2) == INVALID
+    assert _full(ar, rinv=P, rvalid=5) == INVALID
+    assert _full(ar, eps=-1.0) == INVALID
+    assert _full(ar, eps=float("inf")) == INVALID
+    assert _full(ar, eps=float("nan")) == INVALID
+    assert _full(ar, T=1 << 40) == UNSUPPORTED
+
+
+def test_empty_calls_launch_nothing(ar):
+    # T == 0 or n_q == 0: valid, returns before any HIP call
+    assert _full(ar, T=0) == OK
+    assert _full(ar, n_q=0) == OK
+    assert _full(ar, T=0, hist=None, w=None, out=None) == OK
+    assert ar.last_error() == ""
+    assert ar.raw().attnres_block_fwd(P, BF16, 4, 0, 64, 2, P2, 0, 4, 1e-6, P3, BF16, None,
+                                      None) == OK
+
+
+def test_block_fwd_validation(ar):
+    lib = ar.raw()
+    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 0, P2, 0, 9, 1e-6, P3, BF16, None, None) == INVALID
+    assert "S must be" in ar.last_error()
+    assert lib.attnres_block_fwd(P, BF16, 9, 16, 60, 2, P2, 0, 9, 1e-6, P3, BF16, None, None) == ALIGN
+    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 2, P2, 5, 9, 1e-6, P3, BF16, None, None) == INVALID
+    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 2, P2, 0, 9, 1e-6, None, BF16, None, None) == INVALID
+    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 2, P2, 0, 9, 1e-6, P3 + 4, BF16, None, None) == ALIGN
+
+
+def test_status_strings(ar):
+    for code, name in ar.STATUS.items():
+        assert ar.status_string(code).startswith(name)
+    assert "unknown" in ar.status_string(99)
+
+
+def test_last_error_is_thread_local(ar):
+    import threading
+    assert _full(ar, d=12) == ALIGN
+    seen = {}
+
+    def other():
+        seen["msg"] = ar.last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "multiple of 8" in ar.last_error()
+
+
+# ---------------------------------------------------------------------------
+# Block index table: bit-exact against the oracle's independent indexing
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 8, 16, 64, 100])
+def test_block_index_table_matches_oracle(ar, oracle, S):
+    n_hist = 141
+    tab = ar.block_index_table(n_hist, S)
+    assert tab.dtype == np.int32 and tab.shape == (n_hist, 3)
+    for l in range(n_hist):
+        assert tuple(int(x) for x in tab[l]) == oracle.block_sources(l, S), (S, l)
+    sub = ar.block_index_table(n_hist, S, q_begin=37, n_q=20)
+    assert np.array_equal(sub, tab[37:57])
+
+
+def test_block_index_table_validation(ar):
+    lib = ar.raw()
+    buf = (ctypes.c_int32 * 30)()
+    assert lib.attnres_block_index_table(10, 0, 0, 10, buf) == INVALID
+    assert lib.attnres_block_index_table(10, 2, 5, 6, buf) == INVALID
+    assert lib.attnres_block_index_table(10, 2, 0, 10, None) == INVALID
+    assert lib.attnres_block_index_table(10, 2, 0, 0, None) == OK
