@@ -138,6 +138,9 @@ int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
     p.q_begin = (int)q_begin;
     p.n_q = (int)n_q;
     p.rinv_valid = (int)rinv_valid_rows;
+    p.S = 1;
+    p.hist_dt = hist_dtype;
+    p.out_dt = out_dtype;
     p.eps = eps;
     p.inv_d = 1.0f / (float)d;
     return hip_status(fn, attnres::launch_full_fwd(p, hist_dtype, out_dtype, stream));
@@ -156,8 +159,26 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
     if (out == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if (!aligned(out, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: out is not 16-byte aligned", fn);
     if (lse != nullptr && !aligned(lse, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse is not 4-byte aligned", fn);
-    (void)stream;
-    return fail(ATTNRES_ERR_UNSUPPORTED, "%s: not built yet", fn);
+
+    attnres::BlockFwdParams p;
+    p.hist = hist;
+    p.w = w;
+    p.rinv = nullptr;
+    p.out = out;
+    p.lse = lse;
+    p.T = T;
+    p.d = (int)d;
+    p.nc = (int)(d / 8);
+    p.n_hist = (int)n_hist;
+    p.q_begin = (int)q_begin;
+    p.n_q = (int)n_q;
+    p.rinv_valid = 0;
+    p.S = (int)(S < n_hist ? S : n_hist);  // S >= n_hist behaves like S = n_hist
+    p.hist_dt = hist_dtype;
+    p.out_dt = out_dtype;
+    p.eps = eps;
+    p.inv_d = 1.0f / (float)d;
+    return hip_status(fn, attnres::launch_block_fwd(p, hist_dtype, out_dtype, stream));
 }
 
 size_t attnres_bwd_workspace_bytes(attnres_variant variant, int64_t S, int64_t n_hist, int64_t T,

@@ -9,6 +9,12 @@
 // caller's cache when valid, else from the sum of squares of the row already
 // in registers (and is then written back to the cache).
 //
+// The same kernel serves Block reads with many blocks (BLOCK = true): the
+// sources of read l are then v_0, the block sums and the partial sum, each
+// formed on the fly in fp32 from the raw rows it covers and scored when its
+// last row has been added ("DepthBench reading notes" sec. 2.5; DataCamp,
+// block section).
+//
 // Thread mapping: a token group (TG) of LPT lanes per token, NCH 16-byte
 // chunks per lane (see device_common.hpp); 256-thread blocks hold 256/LPT
 // consecutive tokens.  Row accesses are buffer loads from a wave-uniform row
@@ -19,8 +25,8 @@
 
 namespace attnres {
 
-template <typename TI, typename TO, int LPT, int NCH, int PF>
-__global__ __launch_bounds__(256) void full_fwd_stream_kernel(FullFwdParams p) {
+template <typename TI, typename TO, int LPT, int NCH, int PF, bool BLOCK>
+__global__ __launch_bounds__(256) void full_fwd_stream_kernel(FwdParams p) {
     constexpr int TPB = 256 / LPT;  // tokens per block
     const int ln = threadIdx.x % LPT;
     const int64_t tok0 = (int64_t)blockIdx.x * TPB;
@@ -66,6 +72,11 @@ __global__ __launch_bounds__(256) void full_fwd_stream_kernel(FullFwdParams p) {
             for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
         float m2 = -INFINITY;  // running max of scores, log2 domain
         float Z = 0.f;         // running sum of exp2(s2 - m2)
+        float run[BLOCK ? NCH : 1][8];  // Block: the fp32 sum being formed
+#pragma unroll
+        for (int c = 0; c < (BLOCK ? NCH : 1); ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) run[c][e] = 0.f;
 
         // ring of PF prefetched rows (and their cached scales)
         Chunk<TI> buf[PF][NCH];
@@ -100,7 +111,27 @@ __global__ __launch_bounds__(256) void full_fwd_stream_kernel(FullFwdParams p) {
                 const float rc = rbuf[u];
                 if (i + PF <= l) issue(u, i + PF);
 
-                const bool need_sq = i >= p.rinv_valid;  // uniform over the grid
+                if constexpr (BLOCK) {
+                    // v_0 is a source of its own; other rows join the running
+                    // sum, which becomes a source when its block closes or at
+                    // the read's own row (the partial sum)
+                    if (i > 0) {
+#pragma unroll
+                        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                run[c][e] += xf[c][e];
+                                xf[c][e] = run[c][e];
+                            }
+                        if (i % p.S != 0 && i != l) continue;
+#pragma unroll
+                        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) run[c][e] = 0.f;
+                    }
+                }
+
+                const bool need_sq = BLOCK || i >= p.rinv_valid;  // uniform over the grid
                 float dp = 0.f, sq = 0.f;
                 if (need_sq) {
 #pragma unroll
@@ -125,7 +156,7 @@ __global__ __launch_bounds__(256) void full_fwd_stream_kernel(FullFwdParams p) {
                     // cache row i is written once per call, by the first read of
                     // the call that sees it
                     const int owner = i - p.q_begin > 0 ? i - p.q_begin : 0;
-                    if (p.rinv != nullptr && j == owner && ln == 0)
+                    if (!BLOCK && p.rinv != nullptr && j == owner && ln == 0)
                         p.rinv[(int64_t)i * p.T + t] = r;
                 }
                 const float s2 = r * dp * kLog2e;
@@ -165,28 +196,28 @@ __global__ __launch_bounds__(256) void full_fwd_stream_kernel(FullFwdParams p) {
 
 namespace {
 
-template <typename TI, typename TO, int LPT, int NCH, int PF>
-hipError_t launch_stream(const FullFwdParams& p, hipStream_t stream) {
+template <typename TI, typename TO, int LPT, int NCH, int PF, bool BLOCK>
+hipError_t launch_stream(const FwdParams& p, hipStream_t stream) {
     constexpr int TPB = 256 / LPT;
     const int64_t blocks = (p.T + TPB - 1) / TPB;
-    hipLaunchKernelGGL((full_fwd_stream_kernel<TI, TO, LPT, NCH, PF>), dim3((unsigned)blocks),
-                       dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((full_fwd_stream_kernel<TI, TO, LPT, NCH, PF, BLOCK>),
+                       dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename TI, typename TO>
-hipError_t dispatch_stream(const FullFwdParams& p, hipStream_t stream) {
+template <typename TI, typename TO, bool BLOCK>
+hipError_t dispatch_stream(const FwdParams& p, hipStream_t stream) {
     // LPT = 64 lanes per token, NCH chunks per lane: one token per wave
     const int nch = (p.nc + 63) / 64;
     switch (nch) {
-        case 1: return launch_stream<TI, TO, 64, 1, 4>(p, stream);
-        case 2: return launch_stream<TI, TO, 64, 2, 4>(p, stream);
-        case 3: return launch_stream<TI, TO, 64, 3, 3>(p, stream);
-        case 4: return launch_stream<TI, TO, 64, 4, 2>(p, stream);
-        case 5: return launch_stream<TI, TO, 64, 5, 2>(p, stream);
-        case 6: return launch_stream<TI, TO, 64, 6, 2>(p, stream);
-        case 7: return launch_stream<TI, TO, 64, 7, 2>(p, stream);
-        case 8: return launch_stream<TI, TO, 64, 8, 1>(p, stream);
+        case 1: return launch_stream<TI, TO, 64, 1, 4, BLOCK>(p, stream);
+        case 2: return launch_stream<TI, TO, 64, 2, 4, BLOCK>(p, stream);
+        case 3: return launch_stream<TI, TO, 64, 3, 3, BLOCK>(p, stream);
+        case 4: return launch_stream<TI, TO, 64, 4, 2, BLOCK>(p, stream);
+        case 5: return launch_stream<TI, TO, 64, 5, 2, BLOCK>(p, stream);
+        case 6: return launch_stream<TI, TO, 64, 6, 2, BLOCK>(p, stream);
+        case 7: return launch_stream<TI, TO, 64, 7, 2, BLOCK>(p, stream);
+        case 8: return launch_stream<TI, TO, 64, 8, 1, BLOCK>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -196,12 +227,22 @@ hipError_t dispatch_stream(const FullFwdParams& p, hipStream_t stream) {
 hipError_t launch_full_fwd(const FullFwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
                            hipStream_t stream) {
     if (hist_dt == ATTNRES_BF16 && out_dt == ATTNRES_BF16)
-        return dispatch_stream<bf16_t, bf16_t>(p, stream);
+        return dispatch_stream<bf16_t, bf16_t, false>(p, stream);
     if (hist_dt == ATTNRES_BF16 && out_dt == ATTNRES_F32)
-        return dispatch_stream<bf16_t, float>(p, stream);
+        return dispatch_stream<bf16_t, float, false>(p, stream);
     if (hist_dt == ATTNRES_F32 && out_dt == ATTNRES_F32)
-        return dispatch_stream<float, float>(p, stream);
-    return dispatch_stream<float, bf16_t>(p, stream);
+        return dispatch_stream<float, float, false>(p, stream);
+    return dispatch_stream<float, bf16_t, false>(p, stream);
+}
+
+hipError_t launch_block_stream(const BlockFwdParams& p, hipStream_t stream) {
+    if (p.hist_dt == ATTNRES_BF16 && p.out_dt == ATTNRES_BF16)
+        return dispatch_stream<bf16_t, bf16_t, true>(p, stream);
+    if (p.hist_dt == ATTNRES_BF16 && p.out_dt == ATTNRES_F32)
+        return dispatch_stream<bf16_t, float, true>(p, stream);
+    if (p.hist_dt == ATTNRES_F32 && p.out_dt == ATTNRES_F32)
+        return dispatch_stream<float, float, true>(p, stream);
+    return dispatch_stream<float, bf16_t, true>(p, stream);
 }
 
 }  // namespace attnres
