@@ -44,7 +44,7 @@ _lib.attnres_block_fwd.restype = _int
 _lib.attnres_block_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp,
                                    _int, _vp, _vp]
 _lib.attnres_bwd.restype = _int
-_lib.attnres_bwd.argtypes = [_int, _i64, _vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp,
+_lib.attnres_bwd.argtypes = [_int, _i64, _vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32,
                              _vp, _int, _vp, _int, _vp, _vp, _sz, _vp]
 _lib.attnres_bwd_workspace_bytes.restype = _sz
 _lib.attnres_bwd_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _i64, _i64, _i64]
@@ -167,15 +167,15 @@ def bwd_workspace_bytes(variant: int, S: int, n_hist: int, T: int, d: int, q_beg
     return int(_lib.attnres_bwd_workspace_bytes(variant, S, n_hist, T, d, q_begin, n_q))
 
 
-def bwd(variant: int, hist, w, lse, dout, *, S: int = 1, q_begin: int = 0, eps: float = 1e-6,
+def bwd(variant: int, hist, w, dout, *, S: int = 1, q_begin: int = 0, eps: float = 1e-6,
         dhist=None, dhist_dtype=None, dw=None, workspace=None):
-    """Gradients of sum(out * dout) w.r.t. hist and w.  Returns (dhist, dw)."""
+    """Gradients of sum(out * dout) w.r.t. hist and w for the reads
+    q_begin .. q_begin + n_q - 1 (n_q = dout.shape[0]).  Returns (dhist, dw)."""
     import torch
     _require(hist, "hist")
     n_hist, T, d = hist.shape
     n_q = dout.shape[0]
     _require(w, "w", dtype=torch.float32, shape=(n_q, d))
-    _require(lse, "lse", dtype=torch.float32, shape=(n_q, T))
     _require(dout, "dout", shape=(n_q, T, d))
     ddt = _dtype_code(hist) if dhist_dtype is None else (F32 if dhist_dtype == torch.float32 else BF16)
     if dhist is None:
@@ -191,7 +191,7 @@ def bwd(variant: int, hist, w, lse, dout, *, S: int = 1, q_begin: int = 0, eps: 
         workspace = torch.empty(need, dtype=torch.uint8, device=hist.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.attnres_bwd(variant, S, _ptr(hist), _dtype_code(hist), n_hist, T, d, _ptr(w),
-                            q_begin, n_q, eps, _ptr(lse), _ptr(dout), _dtype_code(dout),
+                            q_begin, n_q, eps, _ptr(dout), _dtype_code(dout),
                             _ptr(dhist), ddt, _ptr(dw), _ptr(workspace), ws_bytes,
                             _stream(hist)))
     return dhist, dw

@@ -183,19 +183,81 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
 
 size_t attnres_bwd_workspace_bytes(attnres_variant variant, int64_t S, int64_t n_hist, int64_t T,
                                    int64_t d, int64_t q_begin, int64_t n_q) {
-    (void)variant; (void)S; (void)n_hist; (void)T; (void)d; (void)q_begin; (void)n_q;
-    return 0;
+    if (variant != ATTNRES_FULL && variant != ATTNRES_BLOCK) return 0;
+    if (variant == ATTNRES_FULL) S = 1;
+    if (S < 1 || n_hist < 1 || T < 0 || d < 1 || q_begin < 0 || n_q < 0 || q_begin + n_q > n_hist)
+        return 0;
+    if (S > n_hist) S = n_hist;
+    return (size_t)attnres::bwd_layout(S, n_hist, T, d, n_q).bytes;
 }
 
 int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dtype hist_dtype,
                 int64_t n_hist, int64_t T, int64_t d, const float* w, int64_t q_begin, int64_t n_q,
-                float eps, const float* lse, const void* dout, attnres_dtype dout_dtype, void* dhist,
+                float eps, const void* dout, attnres_dtype dout_dtype, void* dhist,
                 attnres_dtype dhist_dtype, float* dw, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
-    (void)variant; (void)S; (void)hist; (void)hist_dtype; (void)n_hist; (void)T; (void)d; (void)w;
-    (void)q_begin; (void)n_q; (void)eps; (void)lse; (void)dout; (void)dout_dtype; (void)dhist;
-    (void)dhist_dtype; (void)dw; (void)workspace; (void)workspace_bytes; (void)stream;
-    return fail(ATTNRES_ERR_UNSUPPORTED, "attnres_bwd: not built yet");
+    const char* fn = "attnres_bwd";
+    if (variant != ATTNRES_FULL && variant != ATTNRES_BLOCK)
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad variant %d", fn, (int)variant);
+    int st = check_common(fn, hist, hist_dtype, n_hist, T, d, w, q_begin, n_q, eps);
+    if (st != ATTNRES_OK) return st;
+    if (variant == ATTNRES_BLOCK && S < 1)
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: S must be >= 1 (got %" PRId64 ")", fn, S);
+    if (variant == ATTNRES_FULL) S = 1;
+    if (S > n_hist) S = n_hist;  // S >= n_hist behaves like S = n_hist
+    if (!valid_dtype(dout_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad dout dtype", fn);
+    if (!valid_dtype(dhist_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad dhist dtype", fn);
+    if (T == 0) return ok();
+    if (dhist == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: dhist is NULL", fn);
+    if (!aligned(dhist, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: dhist is not 16-byte aligned", fn);
+    if (n_q > 0) {
+        if (dout == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: dout is NULL", fn);
+        if (dw == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: dw is NULL", fn);
+        if (!aligned(dout, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: dout is not 16-byte aligned", fn);
+        if (!aligned(dw, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: dw is not 4-byte aligned", fn);
+    }
+    const attnres::BwdLayout L = attnres::bwd_layout(S, n_hist, T, d, n_q);
+    if (n_q > 0) {
+        if (workspace == nullptr || workspace_bytes < (size_t)L.bytes)
+            return fail(ATTNRES_ERR_WORKSPACE, "%s: workspace of %zu bytes, %" PRId64 " needed", fn,
+                        workspace_bytes, L.bytes);
+        if (!aligned(workspace, 256)) return fail(ATTNRES_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
+    }
+
+    attnres::BwdParams p;
+    p.hist = hist;
+    p.dout = dout;
+    p.dhist = dhist;
+    p.w = w;
+    p.dw = dw;
+    p.T = T;
+    p.d = (int)d;
+    p.nc = (int)(d / 8);
+    p.n_hist = (int)n_hist;
+    p.q_begin = (int)q_begin;
+    p.n_q = (int)n_q;
+    p.S = (int)S;
+    p.nh8 = (int)L.nh8;
+    p.n_blk = (int)L.n_blk;
+    p.nx = (int)L.nx;
+    p.eps = eps;
+    p.inv_d = 1.0f / (float)d;
+    p.hist_dt = hist_dtype;
+    p.dout_dt = dout_dtype;
+    p.dhist_dt = dhist_dtype;
+    char* ws = static_cast<char*>(workspace);
+    p.ws_a1 = reinterpret_cast<float*>(ws + L.off_a1);
+    p.ws_a2 = reinterpret_cast<float*>(ws + L.off_a2);
+    p.ws_a2t = reinterpret_cast<float*>(ws + L.off_a2t);
+    p.ws_c3 = reinterpret_cast<float*>(ws + L.off_c3);
+    p.ws_kappa = reinterpret_cast<float*>(ws + L.off_kappa);
+    p.ws_dwpart = reinterpret_cast<float*>(ws + L.off_dwpart);
+    if (n_q == 0) {
+        // no read: every history row gets a zero gradient
+        return hip_status(fn, attnres::launch_fill_zero(
+                                  dhist, n_hist * T * d * (dhist_dtype == ATTNRES_BF16 ? 2 : 4), stream));
+    }
+    return hip_status(fn, attnres::launch_bwd(p, (int)L.n_chunks, stream));
 }
 
 }  // extern "C"

@@ -160,6 +160,29 @@ __device__ __forceinline__ float tg_sum(float v) {
     return v;
 }
 
+// max over a token group of LPT lanes (every lane gets the max)
+__device__ __forceinline__ float swap16_max(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                              false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                              false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <int LPT>
+__device__ __forceinline__ float tg_max(float v) {
+    static_assert(LPT == 16 || LPT == 32 || LPT == 64, "token group of 16, 32 or 64 lanes");
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));
+    if constexpr (LPT >= 32) v = swap16_max(v);
+    if constexpr (LPT >= 64) v = swap32_max(v);
+    return v;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }

@@ -44,4 +44,37 @@ hipError_t launch_block_fwd(const BlockFwdParams& p, attnres_dtype hist_dt, attn
 // streaming Block kernel (one pass over rows 0..l per read, sums formed on the fly)
 hipError_t launch_block_stream(const BlockFwdParams& p, hipStream_t stream);
 
+// Backward workspace layout (byte offsets; every region 256-byte aligned).
+struct BwdLayout {
+    int64_t nh8;       // history rows rounded up to 8 (row length of A1 / A2)
+    int64_t n_blk;     // v_0 + every block, complete or not
+    int64_t nx;        // most sources a read can see
+    int64_t n_chunks;  // token chunks of the dw partial sums
+    int64_t off_a1, off_a2, off_a2t, off_c3, off_kappa, off_dwpart;
+    int64_t bytes;
+};
+BwdLayout bwd_layout(int64_t S, int64_t n_hist, int64_t T, int64_t d, int64_t n_q);
+
+struct BwdParams {
+    const void* hist;   // [n_hist][T][d]
+    const void* dout;   // [n_q][T][d]
+    void* dhist;        // [n_hist][T][d]
+    const float* w;     // [n_q][d]
+    float* dw;          // [n_q][d]
+    int64_t T;
+    int d, nc, n_hist, q_begin, n_q, S;
+    int nh8, n_blk, nx;
+    float eps, inv_d;
+    attnres_dtype hist_dt, dout_dt, dhist_dt;
+    float* ws_a1;       // [T][n_q][nh8]   alpha of the source holding each row
+    float* ws_a2;       // [T][n_q][nh8]   ds * r of that source
+    float* ws_a2t;      // [T][n_hist][n_q] the same, transposed
+    float* ws_c3;       // [T][n_blk]      sum over reads of ds r^2 s / d per v_0 / block
+    float* ws_kappa;    // [T][n_q]        ds r^2 s / d of each read's partial sum
+    float* ws_dwpart;   // [n_chunks][n_q][d]
+};
+hipError_t launch_bwd(const BwdParams& p, int n_chunks, hipStream_t stream);
+// zero `bytes` (a multiple of 4) of device memory with a kernel
+hipError_t launch_fill_zero(void* dst, int64_t bytes, hipStream_t stream);
+
 }  // namespace attnres

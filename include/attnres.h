@@ -129,7 +129,8 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
  * score-path term; block and partial sums pass their gradient to every row
  * they contain).  Gradients are of sum(out * dout).
  *
- *   lse                [n_q][T] fp32 from the forward (required)
+ *   (no lse argument: the softmax of each read is renormalised over its own
+ *   recomputed scores, so a read with one source gets weight exactly 1)
  *   dout, dout_dtype   [n_q][T][d], F32 or BF16
  *   dhist, dhist_dtype [n_hist][T][d], F32 or BF16: overwritten; rows no read of
  *                      the call sees are set to zero
@@ -141,7 +142,7 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
 int attnres_bwd(attnres_variant variant, int64_t S, const void* hist,
                 attnres_dtype hist_dtype, int64_t n_hist, int64_t T, int64_t d,
                 const float* w, int64_t q_begin, int64_t n_q, float eps,
-                const float* lse, const void* dout, attnres_dtype dout_dtype,
+                const void* dout, attnres_dtype dout_dtype,
                 void* dhist, attnres_dtype dhist_dtype, float* dw, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
 

@@ -141,3 +141,40 @@ def test_block_index_table_validation(ar):
     assert lib.attnres_block_index_table(10, 2, 5, 6, buf) == INVALID
     assert lib.attnres_block_index_table(10, 2, 0, 10, None) == INVALID
     assert lib.attnres_block_index_table(10, 2, 0, 0, None) == OK
+
+
+def _bwd(ar, variant=0, S=1, hist=P, hdt=BF16, n_hist=4, T=16, d=64, w=P2, q_begin=0, n_q=4,
+         eps=1e-6, dout=P, gdt=BF16, dhist=P2, ddt=BF16, dw=P3, ws=P, ws_bytes=1 << 40):
+    return ar.raw().attnres_bwd(variant, S, hist, hdt, n_hist, T, d, w, q_begin, n_q, eps,
+                                dout, gdt, dhist, ddt, dw, ws, ws_bytes, None)
+
+
+def test_bwd_validation(ar):
+    assert _bwd(ar, variant=2) == INVALID
+    assert _bwd(ar, variant=1, S=0) == INVALID
+    assert _bwd(ar, d=12) == ALIGN
+    assert _bwd(ar, q_begin=2) == INVALID
+    assert _bwd(ar, dout=None) == INVALID
+    assert "dout" in ar.last_error()
+    assert _bwd(ar, dhist=None) == INVALID
+    assert _bwd(ar, dw=None) == INVALID
+    assert _bwd(ar, gdt=5) == INVALID
+    assert _bwd(ar, ddt=5) == INVALID
+    assert _bwd(ar, dhist=P2 + 8) == ALIGN
+    assert _bwd(ar, ws=None) == WORKSPACE
+    assert _bwd(ar, ws_bytes=16) == WORKSPACE
+    assert "needed" in ar.last_error()
+    assert _bwd(ar, ws=P + 64) == ALIGN
+    assert _bwd(ar, T=0) == OK
+
+
+def test_bwd_workspace_size(ar):
+    lib = ar.raw()
+    full = lib.attnres_bwd_workspace_bytes(0, 1, 49, 16384, 1024, 0, 49)
+    block = lib.attnres_bwd_workspace_bytes(1, 4, 49, 16384, 1024, 0, 49)
+    assert full > 0 and block > 0 and full % 256 == 0
+    # Full ignores S; Block with S = 1 needs the same layout as Full
+    assert lib.attnres_bwd_workspace_bytes(0, 7, 49, 16384, 1024, 0, 49) == full
+    assert lib.attnres_bwd_workspace_bytes(1, 1, 49, 16384, 1024, 0, 49) == full
+    assert lib.attnres_bwd_workspace_bytes(0, 1, 49, 16384, 1024, 10, 49) == 0  # reads past the history
+    assert lib.attnres_bwd_workspace_bytes(2, 1, 49, 16384, 1024, 0, 49) == 0

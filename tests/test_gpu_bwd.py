@@ -1,0 +1,100 @@
+"""GPU parity of attnres_bwd (Full and Block) against the fp64 oracle's
+backward, which is itself pinned by finite differences on the CPU."""
+import numpy as np
+import pytest
+import torch
+
+from parity import check_out, check_rel, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+FULL, BLOCK = 0, 1
+
+
+@pytest.fixture(scope="module")
+def ar():
+    import depth_wise_attention_attnres_amd as ar
+    return ar
+
+
+def _case(n_hist, T, d, seed, dtype, w_sigma=0.3, n_q=None, q_begin=0):
+    rng = np.random.default_rng(seed)
+    n_q = n_hist - q_begin if n_q is None else n_q
+    hist = rng.standard_normal((n_hist, T, d)).astype(np.float32)
+    w = (rng.standard_normal((n_q, d)) * w_sigma).astype(np.float32)
+    dout = rng.standard_normal((n_q, T, d)).astype(np.float32)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    h = torch.from_numpy(hist).to(DEV).to(tdt)
+    g = torch.from_numpy(dout).to(DEV).to(tdt)
+    return h, torch.from_numpy(w).to(DEV), g
+
+
+def _run(ar, variant, S, h, w, g, q_begin=0, dhist_dtype=None):
+    dh, dw = ar.bwd(variant, h, w, g, S=S, q_begin=q_begin, dhist_dtype=dhist_dtype)
+    torch.cuda.synchronize()
+    return dh, dw
+
+
+def _check(ar, oracle, variant, S, h, w, g, dtype, q_begin=0, dhist_dtype=None):
+    dh, dw = _run(ar, variant, S, h, w, g, q_begin=q_begin, dhist_dtype=dhist_dtype)
+    ref_dh, ref_dw = oracle.bwd(variant, to_f64(h), to_f64(w), to_f64(g), S=S, q_begin=q_begin)
+    out_dt = dtype if dhist_dtype is None else ("f32" if dhist_dtype == torch.float32 else "bf16")
+    if out_dt == "f32":
+        check_rel(to_f64(dh), ref_dh, 1e-5, "dhist")
+    else:
+        check_out(to_f64(dh)[None], ref_dh[None], "bf16", what="dhist")
+    check_rel(to_f64(dw), ref_dw, 1e-5, "dw")
+
+
+CASES = [(1, 3, 8, 1), (2, 5, 16, 1), (9, 37, 64, 1), (9, 37, 64, 2), (13, 21, 136, 3),
+         (17, 40, 256, 4), (17, 20, 256, 40), (25, 19, 520, 8), (33, 11, 1024, 4),
+         (20, 13, 896, 7), (70, 5, 64, 1), (70, 6, 72, 5), (7, 45, 2048, 3)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_hist,T,d,S", CASES)
+def test_bwd_matches_oracle(ar, oracle, dtype, n_hist, T, d, S):
+    h, w, g = _case(n_hist, T, d, seed=n_hist * 7 + d + S, dtype=dtype)
+    variant = FULL if S == 1 else BLOCK
+    _check(ar, oracle, variant, S, h, w, g, dtype)
+    if S == 1:  # Block with S = 1 is Full
+        _check(ar, oracle, BLOCK, 1, h, w, g, dtype)
+
+
+@pytest.mark.parametrize("variant,S,n_hist,q_begin,n_q", [(FULL, 1, 12, 4, 5), (FULL, 1, 12, 11, 1),
+                                                          (BLOCK, 3, 17, 5, 7), (BLOCK, 4, 17, 0, 3),
+                                                          (BLOCK, 2, 30, 21, 9)])
+def test_bwd_read_subsets(ar, oracle, variant, S, n_hist, q_begin, n_q):
+    h, w, g = _case(n_hist, 9, 128, seed=q_begin * 3 + n_q, dtype="f32", n_q=n_q, q_begin=q_begin)
+    _check(ar, oracle, variant, S, h, w, g, "f32", q_begin=q_begin)
+
+
+def test_bwd_bf16_history_fp32_gradient(ar, oracle):
+    h, w, g = _case(17, 23, 192, seed=5, dtype="bf16")
+    _check(ar, oracle, BLOCK, 4, h, w, g, "bf16", dhist_dtype=torch.float32)
+
+
+def test_bwd_is_deterministic(ar):
+    h, w, g = _case(25, 300, 512, seed=6, dtype="bf16")
+    a = _run(ar, BLOCK, 4, h, w, g)
+    b = _run(ar, BLOCK, 4, h, w, g)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("variant,S", [(FULL, 1), (BLOCK, 4)])
+def test_bwd_workload_sampled(ar, oracle, variant, S):
+    # the 48-sublayer, d = 1024, 4 x 4096-token workload: dhist of sampled
+    # tokens from the full-size call; dw from a call on a token subset
+    from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs, token_sample
+    wl = WORKLOADS["fwdbwd_L24_d1024"]
+    h, w, g = device_inputs(wl, DEV)
+    dh, dw = _run(ar, variant, S, h, w, g)
+    idx = token_sample(wl.T, 128, seed=wl.seed)
+    ti = torch.from_numpy(idx).to(DEV)
+    hs, gs = h.index_select(1, ti).contiguous(), g.index_select(1, ti).contiguous()
+    ref_dh, ref_dw = oracle.bwd(variant, to_f64(hs), to_f64(w), to_f64(gs), S=S)
+    stats = check_out(to_f64(dh.index_select(1, ti))[None], ref_dh[None], "bf16", what="dhist")
+    _, dw_sub = _run(ar, variant, S, hs, w, gs)
+    check_rel(to_f64(dw_sub), ref_dw, 1e-5, "dw (token subset)")
+    print(f"bwd {variant} S={S}: {stats}", flush=True)
