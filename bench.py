@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the Block 128K and forward+backward measurements")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the AttnRes aggregation "
@@ -210,7 +212,77 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, hist, w)
+    if not args.no_extra:
+        del hist, out, rinv, lse, src
+        torch.cuda.empty_cache()
+        result["extra"] = extra_measurements(dev)
     print(json.dumps(result), flush=True)
+
+
+def _time(fn, stream, reps, warm):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def extra_measurements(dev):
+    """The other rows of the hot path at their workload sizes: the Block
+    two-phase forward over a 128K-token S=8 history (one call), and the Full
+    and Block (S=4) forward + backward of the L=24 / d=1024 workload."""
+    import torch
+    import depth_wise_attention_attnres_amd as ar
+    from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs
+
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    wl = WORKLOADS["block_S8_d2048_128k"]
+    h, w, _ = device_inputs(wl, dev)
+    n, T, d = h.shape
+    out = torch.empty_like(h)
+    lse = torch.empty((n, T), dtype=torch.float32, device=dev)
+    ms = _time(lambda: ar.block_fwd(h, w, wl.S, out=out, lse=lse), stream, 5, 2)
+    nbytes = (n * T * d * 2) * 2 + n * T * 4
+    res[wl.name] = {"what": "Block AttnRes two-phase forward, all 65 reads in one call, S=8",
+                    "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                    "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
+                    "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "algorithmic_bytes": nbytes}
+    del h, w, out, lse
+    torch.cuda.empty_cache()
+
+    wl = WORKLOADS["fwdbwd_L24_d1024"]
+    h, w, g = device_inputs(wl, dev)
+    n, T, d = h.shape
+    out = torch.empty_like(h)
+    lse = torch.empty((n, T), dtype=torch.float32, device=dev)
+    dh = torch.empty_like(h)
+    dw = torch.empty((n, d), dtype=torch.float32, device=dev)
+    for name, variant, S in [("full", ar.FULL, 1), ("block_S4", ar.BLOCK, wl.S)]:
+        ws = torch.empty(ar.bwd_workspace_bytes(variant, S, n, T, d, 0, n), dtype=torch.uint8,
+                         device=dev)
+        if variant == ar.FULL:
+            fwd = lambda: ar.full_fwd(h, w, out=out, lse=lse)
+        else:
+            fwd = lambda: ar.block_fwd(h, w, S, out=out, lse=lse)
+        bwd = lambda: ar.bwd(variant, h, w, g, S=S, dhist=dh, dw=dw, workspace=ws)
+        ms_f = _time(fwd, stream, 5, 2)
+        ms_b = _time(bwd, stream, 3, 1)
+        res[f"{wl.name}_{name}"] = {
+            "what": f"{name} forward (all reads, one call) + backward, bf16 in/out, fp32 dw",
+            "fwd_ms": ms_f, "bwd_ms": ms_b,
+            "fwd_bwd_tokens_per_s": T / ((ms_f + ms_b) * 1e-3),
+            "fwd_algorithmic_GBps": (2 * n * T * d * 2) / (ms_f * 1e-3) / 1e9,
+        }
+        del ws
+    return res
 
 
 if __name__ == "__main__":

@@ -12,7 +12,7 @@
 //   M = max(M1, s_p), A = Z1 e^(M1 - M), B = e^(s_p - M),
 //   h = (sum_c e^(s_c - M) x_c + B p) / (A + B),  lse = M + log(A + B).
 //
-// Mapping: one workgroup of NW waves per token; lane `ln` owns the 16-byte
+// Mapping: one workgroup of nw waves per token; lane `ln` owns the 16-byte
 // chunk ln of d (8 elements), so the whole raw history of the token is read
 // exactly once, in depth order, and the fp32 sources live in registers
 // (NSRC x 8 VGPRs per lane).  Reads are processed in chunks of at most CR
@@ -21,12 +21,13 @@
 //       then requested (the rows of this chunk are dead);
 //   A2  per-lane partial dots (queries double-buffered from L2), summed over
 //       each 16-lane row with DPP butterflies; each row's sums go to LDS;
-//   A3  one lane per value adds the row sums (fixed order);
-//   A4  one lane per read forms scores, the phase-1 softmax and the phase-2
-//       merge, and publishes the coefficients;
+//   A3  wave 0, one 16-lane row per read and one lane per source: adds the
+//       row sums (fixed order), forms scores, the phase-1 max and sum over
+//       the frozen sources, merges the partial sum by the log-sum-exp rule,
+//       and publishes the coefficients;
 //   B   every lane forms its chunk of the outputs from register sources.
 // The chunk body is instantiated per block group G, so every loop over
-// sources has a compile-time bound.  Three workgroup barriers per chunk.
+// sources has a compile-time bound.  Two workgroup barriers per chunk.
 // Block sums are fp32 and never rounded.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -44,50 +45,55 @@ template <typename TI, int NSRC, int CR>
 struct BlockState {
     float src[NSRC][8];   // v_0, b_1, b_2, ... (fp32)
     float part_sum[8];    // running partial sum of the current block
-    Chunk<TI> rows[CR];   // raw rows of the chunk (then of the next chunk)
-    Chunk<float> wbuf[2]; // pseudo-queries, double-buffered
+    Chunk<TI> rows[CR];     // raw rows of the chunk (then of the next chunk)
+    Chunk<float> wbuf[2];   // pseudo-queries, double-buffered
 };
 
-// Shared-memory layout of one workgroup.
-template <int NW, int NSRC, int CR>
+// Shared-memory layout of one workgroup (nw waves, 4 * nw 16-lane rows).
+template <int NSRC, int CR>
 struct BlockShared {
-    static constexpr int kRowSlots = 4 * NW;  // 16-lane rows in the workgroup
-    float* part;  // [kVals][kRowSlots] row sums
+    int row_slots;  // 16-lane rows in the workgroup
+    float* part;  // [kVals][row_slots] row sums
     float* fin;   // [kVals] totals
     float* coef;  // [CR][kStride] output coefficients (slot NSRC: the partial)
     float* rs;    // [NSRC] RMS scale of each source
 };
 
 // Everything one chunk does, for a chunk of block group G (sources 0..G).
-// l0: first read of the chunk, n: reads in the chunk, nl0/nl1: next chunk.
-template <typename TI, typename TO, int NW, int NSRC, int CR, int G>
+// l0: first read of the chunk, n: reads in the chunk, [nl0, nl1): next chunk.
+// The output dtype is a uniform branch at the store.
+template <typename TI, int NSRC, int CR, int G>
 __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<TI, NSRC, CR>& st,
-                                            const BlockShared<NW, NSRC, CR>& sh, int64_t t,
+                                            const BlockShared<NSRC, CR>& sh, int64_t t,
                                             int l0, int n, int nl0, int nl1,
-                                            const TI* hist_tok, TO* out_tok, uint32_t in_off,
-                                            uint32_t out_off, uint32_t w_off) {
+                                            const TI* hist_tok, void* out_tok, uint32_t in_off,
+                                            uint32_t w_off) {
     constexpr int kStride = BlockLds<NSRC, CR>::kStride;
     constexpr int kVals = BlockLds<NSRC, CR>::kVals;
     constexpr int kSq = CR * kStride;
-    constexpr int kRowSlots = 4 * NW;
+    const int kRowSlots = sh.row_slots;
     const int tid = threadIdx.x;
     const int row_slot = tid >> 4;
     const int64_t row_elems = p.T * (int64_t)p.d;
     const uint64_t tok_in_bytes = (uint64_t)p.d * sizeof(TI);
-    const uint64_t tok_out_bytes = (uint64_t)p.d * sizeof(TO);
     const int S = p.S;
     const bool new_src = (l0 == G * S);   // row l0 closes block G (or is v_0)
+    const int ln = threadIdx.x;
+    const uint32_t out_off_bf = ln < p.nc ? (uint32_t)(ln * 16) : kOOB;  // bf16 chunk; fp32 is twice
 
     auto issue_w = [&](int slot, int l) {
         const rsrc_t wr = make_rsrc(p.w + (int64_t)(l - p.q_begin) * p.d, (uint64_t)p.d * 4);
         st.wbuf[slot].load(wr, w_off);
     };
-    const int k_first = p.q_begin > l0 ? p.q_begin - l0 : 0;  // first read with an output
-    if (k_first < n) {  // slot chosen by branch so the buffer index stays compile-time
-        if (k_first & 1)
-            issue_w(1, l0 + k_first);
+    // the first query of the chunk was requested by the previous chunk (or
+    // before the loop); its slot is the parity of its read index in the chunk.
+    // A chunk without output reads passes the request on to the next chunk.
+    if (l0 + n <= p.q_begin && nl0 < p.q_begin + p.n_q) {
+        const int nk = p.q_begin > nl0 ? p.q_begin - nl0 : 0;
+        if (nk & 1)
+            issue_w(1, nl0 + nk);
         else
-            issue_w(0, l0 + k_first);
+            issue_w(0, nl0 + nk);
     }
 
     // ---- A1: the new source and the partial sums -------------------------
@@ -145,7 +151,16 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
         if (k < n && l >= p.q_begin) {
             float wv[8];
             st.wbuf[k & 1].to_float(wv);
-            if (k + 1 < n) issue_w((k + 1) & 1, l + 1);
+            if (k + 1 < n) {
+                issue_w((k + 1) & 1, l + 1);
+            } else if (nl0 < p.q_begin + p.n_q) {
+                // last read of the chunk: request the next chunk's first query
+                const int nk = p.q_begin > nl0 ? p.q_begin - nl0 : 0;
+                if (nk & 1)
+                    issue_w(1, nl0 + nk);
+                else
+                    issue_w(0, nl0 + nk);
+            }
             constexpr int kV = G + 3;  // G+1 frozen-source dots, partial dot, partial sumsq
             float v[kV];
 #pragma unroll
@@ -182,60 +197,56 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
     }
     __syncthreads();
 
-    // ---- A3: totals over the row sums (fixed order) -----------------------
-    for (int u = tid; u < kVals; u += 64 * NW) {
-        const f32x4* q = reinterpret_cast<const f32x4*>(sh.part + u * kRowSlots);
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < kRowSlots / 4; ++r) {
-            const f32x4 a = q[r];
-            s += a[0];
-            s += a[1];
-            s += a[2];
-            s += a[3];
-        }
-        sh.fin[u] = s;
-    }
-    __syncthreads();
-
-    // ---- A4: scores, phase-1 softmax, phase-2 merge (one lane per read) ---
-    if (tid < n && l0 + tid >= p.q_begin) {
-        const int k = tid;
+    // ---- A3: scores, phase-1 softmax and phase-2 merge on wave 0 ----------
+    // Lane (k, c) = (tid / 16, tid % 16) handles source c of read k, so each
+    // 16-lane DPP row is one read: c <= G are the frozen sources, c = G + 1 is
+    // the partial sum.  Row sums of the dots are added in a fixed order.
+    static_assert(CR <= 4 && NSRC + 1 <= 16, "one 16-lane row per read");
+    if (tid < 64) {
+        const int k = tid >> 4, c = tid & 15;
         const int l = l0 + k;
-        const float* f = sh.fin + k * kStride;
-        float s2[G + 1];
-        float M1 = -INFINITY;
-#pragma unroll
-        for (int c = 0; c <= G; ++c) {
-            const float r = (new_src && c == G) ? fast_rsqrt(fmaf(sh.fin[kSq], p.inv_d, p.eps))
+        const bool read_ok = k < n && l >= p.q_begin;
+        auto total = [&](int idx) {
+            const f32x4* q = reinterpret_cast<const f32x4*>(sh.part + idx * kRowSlots);
+            float s = 0.f;
+            for (int r = 0; r < kRowSlots / 4; ++r) {
+                const f32x4 a = q[r];
+                s += a[0];
+                s += a[1];
+                s += a[2];
+                s += a[3];
+            }
+            return s;
+        };
+        const bool has_p = read_ok && l != G * S;
+        float s2 = -INFINITY;  // score (log2 units) of a frozen source
+        float sp = -INFINITY;  // score of the partial sum
+        if (read_ok && c <= G) {
+            const float r = (new_src && c == G) ? fast_rsqrt(fmaf(total(kSq), p.inv_d, p.eps))
                                                 : sh.rs[c];
-            s2[c] = r * f[c] * kLog2e;
-            M1 = fmaxf(M1, s2[c]);
+            s2 = r * total(k * kStride + c) * kLog2e;
         }
-        float Z1 = 0.f;
-#pragma unroll
-        for (int c = 0; c <= G; ++c) {
-            s2[c] = fast_exp2(s2[c] - M1);
-            Z1 += s2[c];
+        if (has_p && c == G + 1) {
+            const float rp = fast_rsqrt(fmaf(total(k * kStride + NSRC + 1), p.inv_d, p.eps));
+            sp = rp * total(k * kStride + NSRC) * kLog2e;
         }
-        float M = M1, A = Z1, B = 0.f;
-        if (l != G * S) {
-            const float rp = fast_rsqrt(fmaf(f[NSRC + 1], p.inv_d, p.eps));
-            const float sp = rp * f[NSRC] * kLog2e;
-            M = fmaxf(M1, sp);
-            A = Z1 * fast_exp2(M1 - M);
-            B = fast_exp2(sp - M);
-        }
+        const float M1 = tg_max<16>(s2);                  // phase 1: frozen sources
+        const float e = c <= G ? fast_exp2(s2 - M1) : 0.f;
+        const float Z1 = tg_sum<16>(e);
+        const float spr = tg_max<16>(sp);                 // phase 2: merge the partial
+        const float M = fmaxf(M1, spr);
+        const float A = Z1 * fast_exp2(M1 - M);
+        const float B = has_p ? fast_exp2(spr - M) : 0.f;
         const float inv = 1.0f / (A + B);
-        const float scale1 = fast_exp2(M1 - M) * inv;  // e^(s_c - M1) -> e^(s_c - M) / (A + B)
-        float* cf = sh.coef + k * kStride;
-#pragma unroll
-        for (int c = 0; c <= G; ++c) cf[c] = s2[c] * scale1;
-        cf[NSRC] = B * inv;
-        if (p.lse != nullptr)
-            p.lse[(int64_t)(l - p.q_begin) * p.T + t] = (M + fast_log2(A + B)) * kLn2;
+        if (read_ok) {
+            float* cf = sh.coef + k * kStride;
+            if (c <= G) cf[c] = e * fast_exp2(M1 - M) * inv;
+            if (c == G + 1) cf[NSRC] = B * inv;
+            if (c == 0 && p.lse != nullptr)
+                p.lse[(int64_t)(l - p.q_begin) * p.T + t] = (M + fast_log2(A + B)) * kLn2;
+        }
+        if (new_src && tid == G) sh.rs[G] = fast_rsqrt(fmaf(total(kSq), p.inv_d, p.eps));
     }
-    if (new_src && tid == 0) sh.rs[G] = fast_rsqrt(fmaf(sh.fin[kSq], p.inv_d, p.eps));
     __syncthreads();
 
     // ---- B: outputs ------------------------------------------------------
@@ -254,42 +265,49 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] = fmaf(a, st.src[c][e], o[e]);
             }
-            const rsrc_t orr = make_rsrc(out_tok + (int64_t)(l - p.q_begin) * row_elems, tok_out_bytes);
-            store_chunk((TO*)nullptr, orr, out_off, o);
+            if (p.out_dt == ATTNRES_BF16) {
+                const rsrc_t orr = make_rsrc(static_cast<bf16_t*>(out_tok) + (int64_t)(l - p.q_begin) * row_elems,
+                                             (uint64_t)p.d * 2);
+                store_chunk((bf16_t*)nullptr, orr, out_off_bf, o);
+            } else {
+                const rsrc_t orr = make_rsrc(static_cast<float*>(out_tok) + (int64_t)(l - p.q_begin) * row_elems,
+                                             (uint64_t)p.d * 4);
+                store_chunk((float*)nullptr, orr, out_off_bf * 2, o);
+            }
         }
     }
 }
 
-template <typename TI, typename TO, int NW, int NSRC, int CR, int G = 0>
+template <typename TI, int NSRC, int CR, int G = 0>
 __device__ __forceinline__ void block_chunk_dispatch(int g, const BlockFwdParams& p,
                                                      BlockState<TI, NSRC, CR>& st,
-                                                     const BlockShared<NW, NSRC, CR>& sh, int64_t t,
+                                                     const BlockShared<NSRC, CR>& sh, int64_t t,
                                                      int l0, int n, int nl0, int nl1,
-                                                     const TI* hist_tok, TO* out_tok,
-                                                     uint32_t in_off, uint32_t out_off,
-                                                     uint32_t w_off) {
+                                                     const TI* hist_tok, void* out_tok,
+                                                     uint32_t in_off, uint32_t w_off) {
     if constexpr (G < NSRC) {
         if (g == G)
-            block_chunk<TI, TO, NW, NSRC, CR, G>(p, st, sh, t, l0, n, nl0, nl1, hist_tok, out_tok,
-                                                 in_off, out_off, w_off);
+            block_chunk<TI, NSRC, CR, G>(p, st, sh, t, l0, n, nl0, nl1, hist_tok, out_tok, in_off,
+                                         w_off);
         else
-            block_chunk_dispatch<TI, TO, NW, NSRC, CR, G + 1>(g, p, st, sh, t, l0, n, nl0, nl1,
-                                                              hist_tok, out_tok, in_off, out_off,
-                                                              w_off);
+            block_chunk_dispatch<TI, NSRC, CR, G + 1>(g, p, st, sh, t, l0, n, nl0, nl1, hist_tok,
+                                                      out_tok, in_off, w_off);
     }
 }
 
-// Two workgroups per CU (two waves per SIMD) keep one token's barrier phases
-// overlapped with another's loads and arithmetic: cap registers at 256.
-template <typename TI, typename TO, int NW, int NSRC, int CR>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+// Two waves per SIMD keep one token's barrier phases overlapped with
+// another's loads and arithmetic: registers are capped at 256.  The workgroup
+// has nw = blockDim.x / 64 waves (1, 2, 4 or 8).
+template <typename TI, int NSRC, int CR>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void block_fwd_twophase_kernel(BlockFwdParams p) {
     constexpr int kStride = BlockLds<NSRC, CR>::kStride;
     constexpr int kVals = BlockLds<NSRC, CR>::kVals;
-    constexpr int kRowSlots = 4 * NW;
+    const int kRowSlots = blockDim.x / 16;
 
     extern __shared__ float lds[];
-    BlockShared<NW, NSRC, CR> sh;
+    BlockShared<NSRC, CR> sh;
+    sh.row_slots = kRowSlots;
     sh.part = lds;
     sh.fin = sh.part + kVals * kRowSlots;
     sh.coef = sh.fin + kVals;
@@ -298,9 +316,8 @@ void block_fwd_twophase_kernel(BlockFwdParams p) {
     const int ln = threadIdx.x;                   // chunk index of d owned by this lane
     const int64_t t = blockIdx.x;                 // token
     const TI* hist_tok = static_cast<const TI*>(p.hist) + t * p.d;
-    TO* out_tok = static_cast<TO*>(p.out) + t * p.d;
+    void* out_tok = static_cast<char*>(p.out) + t * p.d * (p.out_dt == ATTNRES_BF16 ? 2 : 4);
     const uint32_t in_off = ln < p.nc ? (uint32_t)(ln * 8 * sizeof(TI)) : kOOB;
-    const uint32_t out_off = ln < p.nc ? (uint32_t)(ln * 8 * sizeof(TO)) : kOOB;
     const uint32_t w_off = ln < p.nc ? (uint32_t)(ln * 32) : kOOB;
     const int q_end = p.q_begin + p.n_q;
     const int S = p.S;
@@ -330,11 +347,21 @@ void block_fwd_twophase_kernel(BlockFwdParams p) {
             const rsrc_t rr = make_rsrc(hist_tok + (int64_t)k * row_elems, (uint64_t)p.d * sizeof(TI));
             st.rows[k].load(rr, in_off);
         }
+    {
+        const int nk = p.q_begin > 0 ? p.q_begin : 0;  // first read with an output
+        if (nk < l1) {
+            const rsrc_t wr = make_rsrc(p.w + (int64_t)(nk - p.q_begin) * p.d, (uint64_t)p.d * 4);
+            if (nk & 1)
+                st.wbuf[1].load(wr, w_off);
+            else
+                st.wbuf[0].load(wr, w_off);
+        }
+    }
     while (l0 < q_end) {
         const int nl0 = l1;
         const int nl1 = nl0 < q_end ? chunk_end(nl0) : nl0;
-        block_chunk_dispatch<TI, TO, NW, NSRC, CR>(l0 / S, p, st, sh, t, l0, l1 - l0, nl0, nl1,
-                                                   hist_tok, out_tok, in_off, out_off, w_off);
+        block_chunk_dispatch<TI, NSRC, CR>(l0 / S, p, st, sh, t, l0, l1 - l0, nl0, nl1, hist_tok,
+                                           out_tok, in_off, w_off);
         l0 = nl0;
         l1 = nl1;
     }
@@ -345,37 +372,33 @@ void block_fwd_twophase_kernel(BlockFwdParams p) {
 
 namespace {
 
-template <typename TI, typename TO, int NW, int NSRC, int CR>
-hipError_t launch_twophase(const BlockFwdParams& p, hipStream_t stream) {
+template <typename TI, int NSRC, int CR>
+hipError_t launch_twophase(const BlockFwdParams& p, int nw, hipStream_t stream) {
     constexpr int kStride = BlockLds<NSRC, CR>::kStride;
     constexpr int kVals = BlockLds<NSRC, CR>::kVals;
-    const size_t lds = sizeof(float) * (kVals * 4 * NW + kVals + CR * kStride + NSRC);
-    hipLaunchKernelGGL((block_fwd_twophase_kernel<TI, TO, NW, NSRC, CR>), dim3((unsigned)p.T),
-                       dim3(64 * NW), lds, stream, p);
+    const size_t lds = sizeof(float) * (kVals * 4 * nw + kVals + CR * kStride + NSRC);
+    hipLaunchKernelGGL((block_fwd_twophase_kernel<TI, NSRC, CR>), dim3((unsigned)p.T),
+                       dim3(64 * nw), lds, stream, p);
     return hipGetLastError();
 }
 
-template <typename TI, typename TO, int NW>
-hipError_t dispatch_nsrc(const BlockFwdParams& p, int nsrc, hipStream_t stream) {
-    // reads per chunk: as many as the registers allow without spilling
-    // (sources, partial sums and the chunk's rows all live in VGPRs)
-    if (nsrc <= 5)
-        return p.S >= 8 ? launch_twophase<TI, TO, NW, 5, 8>(p, stream)
-                        : launch_twophase<TI, TO, NW, 5, 4>(p, stream);
-    if (nsrc <= 9) return launch_twophase<TI, TO, NW, 9, 4>(p, stream);
-    return launch_twophase<TI, TO, NW, 13, 4>(p, stream);
+template <typename TI>
+hipError_t dispatch_nsrc(const BlockFwdParams& p, int nsrc, int nw, hipStream_t stream) {
+    // four reads per chunk: one 16-lane row per read in the coefficient step
+    if (nsrc <= 5) return launch_twophase<TI, 5, 4>(p, nw, stream);
+    if (nsrc <= 9) return launch_twophase<TI, 9, 4>(p, nw, stream);
+    return launch_twophase<TI, 13, 4>(p, nw, stream);
 }
 
-template <typename TI, typename TO>
+template <typename TI>
 hipError_t dispatch_block(const BlockFwdParams& p, hipStream_t stream) {
     // sources a read of this call can see: v_0 plus the completed blocks
     const int last = p.q_begin + p.n_q - 1;
     const int nsrc = 1 + last / p.S;
     if (nsrc <= kBlockMaxRegSources) {
-        if (p.nc <= 64) return dispatch_nsrc<TI, TO, 1>(p, nsrc, stream);
-        if (p.nc <= 128) return dispatch_nsrc<TI, TO, 2>(p, nsrc, stream);
-        if (p.nc <= 256) return dispatch_nsrc<TI, TO, 4>(p, nsrc, stream);
-        return dispatch_nsrc<TI, TO, 8>(p, nsrc, stream);
+        // one lane per 16-byte chunk of d: 1, 2, 4 or 8 waves per token
+        const int nw = p.nc <= 64 ? 1 : p.nc <= 128 ? 2 : p.nc <= 256 ? 4 : 8;
+        return dispatch_nsrc<TI>(p, nsrc, nw, stream);
     }
     // many blocks: stream the raw rows per read and form the sums on the fly
     return launch_block_stream(p, stream);
@@ -385,13 +408,9 @@ hipError_t dispatch_block(const BlockFwdParams& p, hipStream_t stream) {
 
 hipError_t launch_block_fwd(const BlockFwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
                             hipStream_t stream) {
-    if (hist_dt == ATTNRES_BF16 && out_dt == ATTNRES_BF16)
-        return dispatch_block<bf16_t, bf16_t>(p, stream);
-    if (hist_dt == ATTNRES_BF16 && out_dt == ATTNRES_F32)
-        return dispatch_block<bf16_t, float>(p, stream);
-    if (hist_dt == ATTNRES_F32 && out_dt == ATTNRES_F32)
-        return dispatch_block<float, float>(p, stream);
-    return dispatch_block<float, bf16_t>(p, stream);
+    (void)out_dt;  // carried in p.out_dt, a uniform branch at the store
+    return hist_dt == ATTNRES_BF16 ? dispatch_block<bf16_t>(p, stream)
+                                   : dispatch_block<float>(p, stream);
 }
 
 }  // namespace attnres

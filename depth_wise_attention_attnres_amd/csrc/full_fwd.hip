@@ -25,9 +25,12 @@
 
 namespace attnres {
 
+// Workgroup size of the streaming kernel (tokens per workgroup = threads / LPT).
+constexpr int kStreamThreads = 256;
+
 template <typename TI, typename TO, int LPT, int NCH, int PF, bool BLOCK>
-__global__ __launch_bounds__(256) void full_fwd_stream_kernel(FwdParams p) {
-    constexpr int TPB = 256 / LPT;  // tokens per block
+__global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdParams p) {
+    constexpr int TPB = kStreamThreads / LPT;  // tokens per block
     const int ln = threadIdx.x % LPT;
     const int64_t tok0 = (int64_t)blockIdx.x * TPB;
     const int tl = threadIdx.x / LPT;  // token within the block
@@ -198,10 +201,10 @@ namespace {
 
 template <typename TI, typename TO, int LPT, int NCH, int PF, bool BLOCK>
 hipError_t launch_stream(const FwdParams& p, hipStream_t stream) {
-    constexpr int TPB = 256 / LPT;
+    constexpr int TPB = kStreamThreads / LPT;
     const int64_t blocks = (p.T + TPB - 1) / TPB;
     hipLaunchKernelGGL((full_fwd_stream_kernel<TI, TO, LPT, NCH, PF, BLOCK>),
-                       dim3((unsigned)blocks), dim3(256), 0, stream, p);
+                       dim3((unsigned)blocks), dim3(kStreamThreads), 0, stream, p);
     return hipGetLastError();
 }
 
