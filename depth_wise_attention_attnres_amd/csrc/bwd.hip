@@ -18,12 +18,12 @@
 //          - sum over reads whose partial holds row i of kappa_l p_l
 //   dw_l = sum_t sum_i A2[t][l][i] v_{t,i}.
 // Kernels:
-//   bwd_scores  one wave per token: streams each read's sources once (block
-//               sums formed on the fly in fp32), reduces the three dots per
-//               source across the wave, renormalises the softmax over the
-//               read's own scores (so a single source gets alpha = 1 exactly),
-//               forms ds, and writes A1, A2 (row-major and transposed), C3 and
-//               kappa to the workspace.
+//   bwd_scores  one wave per token: streams the token's rows once per pass of
+//               R reads (block sums formed on the fly in fp32), reduces the
+//               score and gradient dots of every source for the pass's reads
+//               across the wave, renormalises each read's softmax over its own
+//               scores (a single source gets alpha = 1 exactly), forms ds, and
+//               writes A1, A2 (row-major and transposed), C3 and kappa.
 //   bwd_dhist   one wave per (token, 128-column slice of d): accumulates
 //               dv for 64-row tiles in registers (coefficients are uniform
 //               across the wave, so they come through the scalar cache),
@@ -79,22 +79,27 @@ __device__ __forceinline__ int src_of(int l, int i, int S) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// bwd_scores: one wave (= one workgroup) per token.
+// bwd_scores: one wave (= one workgroup) per token.  Reads are processed R
+// at a time: one pass over the token's rows 0..l_max forms every source once
+// (v_0, block sums, the partial sums of the pass's reads) and scores it
+// against all reads of the pass that see it, so the rows are streamed
+// n_q / R times instead of n_q times.
 
-template <typename TI, typename TG, int NCH, int PF>
+template <typename TI, typename TG, int NCH, int PF, int R>
 __global__ __launch_bounds__(64) void bwd_scores_kernel(BwdParams p) {
     const int ln = threadIdx.x;
     const int64_t t = blockIdx.x;
     const int S = p.S;
 
     extern __shared__ float lds[];
-    float* v_alpha = lds;                 // [nx] per source of the current read
-    float* v_a = v_alpha + p.nx;
-    float* v_r = v_a + p.nx;
-    float* v_s = v_r + p.nx;
-    float* c1s = v_s + p.nx;
-    float* c2s = c1s + p.nx;
-    float* c3acc = c2s + p.nx;            // [n_blk] summed over reads
+    // per read of the pass and source: a = g.x, r, s (score); then alpha, c1, c2
+    float* v_a = lds;                      // [R][nx]
+    float* v_r = v_a + R * p.nx;
+    float* v_s = v_r + R * p.nx;
+    float* v_alpha = v_s + R * p.nx;
+    float* c1s = v_alpha + R * p.nx;
+    float* c2s = c1s + R * p.nx;
+    float* c3acc = c2s + R * p.nx;         // [n_blk] summed over reads
 
     for (int i = ln; i < p.n_blk; i += 64) c3acc[i] = 0.f;
 
@@ -115,23 +120,29 @@ __global__ __launch_bounds__(64) void bwd_scores_kernel(BwdParams p) {
     float* A2 = p.ws_a2 + t * (int64_t)p.n_q * p.nh8;
     float* A2T = p.ws_a2t + t * (int64_t)p.n_hist * p.n_q;
 
-    for (int lq = 0; lq < p.n_q; ++lq) {
-        const int l = p.q_begin + lq;
-        float wv[NCH][8], gv[NCH][8];
-        {
+    for (int lq0 = 0; lq0 < p.n_q; lq0 += R) {
+        const int nr = p.n_q - lq0 < R ? p.n_q - lq0 : R;  // reads in this pass
+        const int l_lo = p.q_begin + lq0;                 // first read of the pass
+        const int l_hi = l_lo + nr - 1;                   // last read of the pass
+        float wv[R][NCH][8], gv[R][NCH][8];
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int lq = q < nr ? lq0 + q : lq0;  // a valid row; unused when q >= nr
             const rsrc_t wr = make_rsrc(p.w + (int64_t)lq * p.d, (uint64_t)p.d * 4);
             const rsrc_t gr = make_rsrc(dout_tok + (int64_t)lq * row_elems, (uint64_t)p.d * sizeof(TG));
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 Chunk<float> wc;
                 wc.load(wr, w_off[c]);
-                wc.to_float(wv[c]);
+                wc.to_float(wv[q][c]);
                 Chunk<TG> gc;
                 gc.load(gr, g_off[c]);
-                gc.to_float(gv[c]);
+                gc.to_float(gv[q][c]);
             }
         }
-        int nsrc = 0;
+        int nsrc[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) nsrc[q] = 0;
         float run[NCH][8];
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
@@ -150,18 +161,22 @@ __global__ __launch_bounds__(64) void bwd_scores_kernel(BwdParams p) {
         };
 #pragma unroll
         for (int u = 0; u < PF; ++u)
-            if (u <= l) issue(u, u);
+            if (u <= l_hi) issue(u, u);
 
-        for (int i0 = 0; i0 <= l; i0 += PF) {
+        for (int i0 = 0; i0 <= l_hi; i0 += PF) {
 #pragma unroll
             for (int u = 0; u < PF; ++u) {
                 const int i = i0 + u;
-                if (i > l) break;
+                if (i > l_hi) break;
                 float xf[NCH][8];
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) buf[u][c].to_float(xf[c]);
-                if (i + PF <= l) issue(u, i + PF);
-                if (i > 0) {  // rows after v_0 join the running sum of their source
+                if (i + PF <= l_hi) issue(u, i + PF);
+                // which reads of the pass see the source emitted at row i:
+                // v_0 or a block closing at i -> every read l >= i; otherwise
+                // the partial sum of read l = i (if that read is in the pass)
+                bool block_src = true;
+                if (i > 0) {
 #pragma unroll
                     for (int c = 0; c < NCH; ++c)
 #pragma unroll
@@ -169,80 +184,114 @@ __global__ __launch_bounds__(64) void bwd_scores_kernel(BwdParams p) {
                             run[c][e] += xf[c][e];
                             xf[c][e] = run[c][e];
                         }
-                    if (i % S != 0 && i != l) continue;
+                    block_src = (i % S == 0);
+                    if (!block_src && (i < l_lo || i > l_hi)) continue;
+                    if (block_src) {
 #pragma unroll
-                    for (int c = 0; c < NCH; ++c)
+                        for (int c = 0; c < NCH; ++c)
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) run[c][e] = 0.f;
+                            for (int e = 0; e < 8; ++e) run[c][e] = 0.f;
+                    }
                 }
-                float wx = 0.f, gx = 0.f, sq = 0.f;
+                float sq = 0.f;
+                float wx[R], gx[R];
+#pragma unroll
+                for (int q = 0; q < R; ++q) wx[q] = gx[q] = 0.f;
 #pragma unroll
                 for (int c = 0; c < NCH; ++c)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        wx = fmaf(wv[c][e], xf[c][e], wx);
-                        gx = fmaf(gv[c][e], xf[c][e], gx);
                         sq = fmaf(xf[c][e], xf[c][e], sq);
+#pragma unroll
+                        for (int q = 0; q < R; ++q) {
+                            wx[q] = fmaf(wv[q][c][e], xf[c][e], wx[q]);
+                            gx[q] = fmaf(gv[q][c][e], xf[c][e], gx[q]);
+                        }
                     }
-                wx = tg_sum<64>(wx);
-                gx = tg_sum<64>(gx);
                 sq = tg_sum<64>(sq);
-                const float r = fast_rsqrt(fmaf(sq, p.inv_d, p.eps));
-                if (ln == 0) {
-                    v_a[nsrc] = gx;
-                    v_r[nsrc] = r;
-                    v_s[nsrc] = r * wx;
+#pragma unroll
+                for (int q = 0; q < R; ++q) {
+                    wx[q] = tg_sum<64>(wx[q]);
+                    gx[q] = tg_sum<64>(gx[q]);
                 }
-                ++nsrc;
+                const float r = fast_rsqrt(fmaf(sq, p.inv_d, p.eps));
+#pragma unroll
+                for (int q = 0; q < R; ++q) {
+                    const int l = l_lo + q;
+                    const bool sees = q < nr && (block_src ? l >= i : l == i);
+                    if (sees) {
+                        if (ln == 0) {
+                            v_a[q * p.nx + nsrc[q]] = gx[q];
+                            v_r[q * p.nx + nsrc[q]] = r;
+                            v_s[q * p.nx + nsrc[q]] = r * wx[q];
+                        }
+                        ++nsrc[q];
+                    }
+                }
             }
         }
         __syncthreads();
 
-        // softmax over the read's sources (lanes hold sources ln, ln + 64, ...)
-        float mx = -INFINITY;
-        for (int xs = ln; xs < nsrc; xs += 64) mx = fmaxf(mx, v_s[xs]);
-        mx = tg_max<64>(mx);
-        float z = 0.f;
-        for (int xs = ln; xs < nsrc; xs += 64) {
-            const float e = fast_exp2((v_s[xs] - mx) * kLog2e);
-            v_alpha[xs] = e;
-            z += e;
-        }
-        z = tg_sum<64>(z);
-        const float inv_z = 1.0f / z;
-        float delta = 0.f;
-        for (int xs = ln; xs < nsrc; xs += 64) {
-            const float alpha = v_alpha[xs] * inv_z;
-            v_alpha[xs] = alpha;
-            delta = fmaf(alpha, v_a[xs], delta);
-        }
-        delta = tg_sum<64>(delta);
+        for (int q = 0; q < nr; ++q) {
+            const int lq = lq0 + q;
+            const int l = l_lo + q;
+            const int ns = nsrc[q];
+            float* va = v_a + q * p.nx;
+            float* vr = v_r + q * p.nx;
+            float* vs = v_s + q * p.nx;
+            float* val = v_alpha + q * p.nx;
+            float* cc1 = c1s + q * p.nx;
+            float* cc2 = c2s + q * p.nx;
+            // softmax over the read's sources (lanes hold sources ln, ln + 64, ...)
+            float mx = -INFINITY;
+            for (int xs = ln; xs < ns; xs += 64) mx = fmaxf(mx, vs[xs]);
+            mx = tg_max<64>(mx);
+            float z = 0.f;
+            for (int xs = ln; xs < ns; xs += 64) {
+                const float e = fast_exp2((vs[xs] - mx) * kLog2e);
+                val[xs] = e;
+                z += e;
+            }
+            z = tg_sum<64>(z);
+            const float inv_z = 1.0f / z;
+            float delta = 0.f;
+            for (int xs = ln; xs < ns; xs += 64) {
+                const float alpha = val[xs] * inv_z;
+                val[xs] = alpha;
+                delta = fmaf(alpha, va[xs], delta);
+            }
+            delta = tg_sum<64>(delta);
 
-        const int m = l / S;
-        for (int xs = ln; xs < nsrc; xs += 64) {
-            const float alpha = v_alpha[xs], r = v_r[xs];
-            const float ds = alpha * (v_a[xs] - delta);
-            c1s[xs] = alpha;
-            c2s[xs] = ds * r;
-            const float c3 = ds * r * r * v_s[xs] * p.inv_d;
-            if (xs <= m)
-                c3acc[xs] += c3;  // v_0 or a block sum: same lane for a slot on every read
-            else
-                p.ws_kappa[t * p.n_q + lq] = c3;  // the partial sum of this read
+            const int m = l / S;
+            for (int xs = ln; xs < ns; xs += 64) {
+                const float alpha = val[xs], r = vr[xs];
+                const float ds = alpha * (va[xs] - delta);
+                cc1[xs] = alpha;
+                cc2[xs] = ds * r;
+                const float c3 = ds * r * r * vs[xs] * p.inv_d;
+                if (xs <= m)
+                    c3acc[xs] += c3;  // v_0 or a block sum: same lane for a slot on every read
+                else
+                    p.ws_kappa[t * p.n_q + lq] = c3;  // the partial sum of this read
+            }
+            if (ln == 0 && l % S == 0) p.ws_kappa[t * p.n_q + lq] = 0.f;  // no partial
         }
-        if (ln == 0 && l % S == 0) p.ws_kappa[t * p.n_q + lq] = 0.f;  // no partial
         __syncthreads();
 
-        for (int i = ln; i < p.nh8; i += 64) {
-            float c1 = 0.f, c2 = 0.f;
-            if (i <= l) {
-                const int xs = src_of(l, i, S);
-                c1 = c1s[xs];
-                c2 = c2s[xs];
+        for (int q = 0; q < nr; ++q) {
+            const int lq = lq0 + q;
+            const int l = l_lo + q;
+            for (int i = ln; i < p.nh8; i += 64) {
+                float c1 = 0.f, c2 = 0.f;
+                if (i <= l) {
+                    const int xs = src_of(l, i, S);
+                    c1 = c1s[q * p.nx + xs];
+                    c2 = c2s[q * p.nx + xs];
+                }
+                A1[(int64_t)lq * p.nh8 + i] = c1;
+                A2[(int64_t)lq * p.nh8 + i] = c2;
+                if (i < p.n_hist) A2T[(int64_t)i * p.n_q + lq] = c2;
             }
-            A1[(int64_t)lq * p.nh8 + i] = c1;
-            A2[(int64_t)lq * p.nh8 + i] = c2;
-            if (i < p.n_hist) A2T[(int64_t)i * p.n_q + lq] = c2;
         }
         __syncthreads();
     }
@@ -515,22 +564,22 @@ namespace {
 
 template <typename TI, typename TG>
 hipError_t launch_scores(const BwdParams& p, hipStream_t stream) {
-    const size_t lds = sizeof(float) * (6 * (size_t)p.nx + p.n_blk);
     const int nch = (p.nc + 63) / 64;
     switch (nch) {
-#define ATTNRES_SCORES(N, PF)                                                                  \
-    case N:                                                                                    \
-        hipLaunchKernelGGL((bwd_scores_kernel<TI, TG, N, PF>), dim3((unsigned)p.T), dim3(64), \
-                           lds, stream, p);                                                    \
+#define ATTNRES_SCORES(N, PF, R)                                                          \
+    case N:                                                                               \
+        hipLaunchKernelGGL((bwd_scores_kernel<TI, TG, N, PF, R>), dim3((unsigned)p.T),   \
+                           dim3(64), sizeof(float) * (6 * (size_t)R * p.nx + p.n_blk),    \
+                           stream, p);                                                    \
         break;
-        ATTNRES_SCORES(1, 4)
-        ATTNRES_SCORES(2, 4)
-        ATTNRES_SCORES(3, 2)
-        ATTNRES_SCORES(4, 2)
-        ATTNRES_SCORES(5, 2)
-        ATTNRES_SCORES(6, 1)
-        ATTNRES_SCORES(7, 1)
-        ATTNRES_SCORES(8, 1)
+        ATTNRES_SCORES(1, 4, 4)
+        ATTNRES_SCORES(2, 2, 4)
+        ATTNRES_SCORES(3, 2, 2)
+        ATTNRES_SCORES(4, 2, 2)
+        ATTNRES_SCORES(5, 1, 1)
+        ATTNRES_SCORES(6, 1, 1)
+        ATTNRES_SCORES(7, 1, 1)
+        ATTNRES_SCORES(8, 1, 1)
 #undef ATTNRES_SCORES
         default: return hipErrorInvalidValue;
     }

@@ -27,8 +27,10 @@ namespace attnres {
 
 // Workgroup size of the streaming kernel (tokens per workgroup = threads / LPT).
 constexpr int kStreamThreads = 256;
-// Cache policy of the history loads.
-constexpr int kHistAux = 2;  // non-temporal: each row is read once per call
+// Cache policy of the history loads: a single-read call touches each row
+// once (non-temporal); with several reads the wave re-reads the token's rows
+// for every read, so they are loaded with the default policy.
+constexpr int kHistAuxOnce = 2;
 
 template <typename TI, typename TO, int LPT, int NCH, int PF, bool BLOCK>
 __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdParams p) {
@@ -94,8 +96,13 @@ __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdPara
         }
         auto issue = [&](int u, int i) {
             const rsrc_t rr = make_rsrc(hist_blk + i * row_elems, blk_elems * sizeof(TI));
+            if (p.n_q == 1) {
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) buf[u][c].template load<kHistAux>(rr, in_off[c]);
+                for (int c = 0; c < NCH; ++c) buf[u][c].template load<kHistAuxOnce>(rr, in_off[c]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) buf[u][c].load(rr, in_off[c]);
+            }
             if (i < p.rinv_valid) {
                 const rsrc_t cr = make_rsrc(p.rinv + (int64_t)i * p.T + tok0, (uint64_t)(p.T - tok0) * 4);
                 rbuf[u] = load_f32(cr, tok_f32_off);

@@ -37,12 +37,18 @@ def main():
 
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace-stats", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--stats-only", metavar="TITLE",
+                    help="write profiles/<name>.md with the kernel-trace table only")
     ap.add_argument("--name", default="full_fwd_stream_L32_d896")
     ap.add_argument("--kernel", default="full_fwd_stream_kernel")
     ap.add_argument("--commands", default="", help="text of the commands that made the CSVs")
     args = ap.parse_args()
+    if args.stats_only:
+        return stats_only(args)
+    if not (args.fetch and args.write):
+        raise SystemExit("--fetch and --write are required (or use --stats-only)")
 
     from depth_wise_attention_attnres_amd.workloads import WORKLOADS
     wl = WORKLOADS[bench.WORKLOAD]
@@ -92,7 +98,7 @@ def main():
     lines = [
         f"# {args.name}: Full AttnRes forward, read by read, L=32 / d=896 / 16384 tokens, bf16",
         "",
-        "Commands (run from /tmp with TMPDIR=/tmp on the GPU box; paths relative to the repo):",
+        "Commands (run from /tmp with TMPDIR=/tmp on the GPU box; $R = the repo root):",
         "",
         "```",
         args.commands.strip() or "(see DESIGN.md)",
@@ -135,6 +141,31 @@ def main():
     with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(rec, indent=1))
+
+
+def stats_only(args):
+    """Kernel-trace summary of every kernel in a run (no counters)."""
+    lines = [
+        f"# {args.name}: {args.stats_only}",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp on the GPU box; $R = the repo root):",
+        "",
+        "```",
+        args.commands.strip(),
+        "```",
+        "",
+        "## rocprofv3 --kernel-trace --stats",
+        "",
+        "| kernel | calls | average ns | min ns | max ns | share |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in rows(args.trace_stats):
+        name = r["Name"] if len(r["Name"]) < 110 else r["Name"][:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                     f"{r['MaxNs']} | {r['Percentage']}% |")
+    with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 if __name__ == "__main__":
