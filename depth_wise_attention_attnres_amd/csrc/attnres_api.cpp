@@ -51,6 +51,9 @@ int check_common(const char* fn, const void* hist, int hist_dt, int64_t n_hist, 
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: d = %" PRId64 " exceeds %d", fn, d, attnres::kMaxD);
     if (n_hist > (int64_t)1 << 20)
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: n_hist = %" PRId64 " too large", fn, n_hist);
+    // grids hold up to T x (d / 256) workgroups in one dimension
+    if (T > ((int64_t)1 << 27))
+        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: T = %" PRId64 " exceeds 2^27 tokens", fn, T);
     // every element offset must fit int64 comfortably
     if (T > ((int64_t)1 << 40) / (n_hist * d))
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: history of %" PRId64 " x %" PRId64 " x %" PRId64 " too large",
@@ -238,6 +241,7 @@ int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dt
     p.n_q = (int)n_q;
     p.S = (int)S;
     p.nh8 = (int)L.nh8;
+    p.nq8 = (int)L.nq8;
     p.n_blk = (int)L.n_blk;
     p.nx = (int)L.nx;
     p.eps = eps;

@@ -24,13 +24,16 @@
 //               across the wave, renormalises each read's softmax over its own
 //               scores (a single source gets alpha = 1 exactly), forms ds, and
 //               writes A1, A2 (row-major and transposed), C3 and kappa.
-//   bwd_dhist   one wave per (token, 128-column slice of d): accumulates
-//               dv for 64-row tiles in registers (coefficients are uniform
+//   bwd_dhist   one wave per (token, 256-column slice of d): accumulates
+//               dv for row tiles in registers while the reads' dout and w
+//               rows stream through a prefetch ring (coefficients are uniform
 //               across the wave, so they come through the scalar cache),
 //               then adds the source-coupling terms with a forward (prefix)
 //               and a backward (suffix) pass over each block, and stores dhist.
 //   bwd_dw_part one wave per (128-column slice, chunk of 32 tokens):
-//               per-chunk partial dw for 64-read tiles.
+//               per-chunk partial dw for tiles of 32 reads on the matrix cores
+//               (fp32 MFMA), the chunk's (token, row) pairs streamed through a
+//               prefetch ring.
 //   bwd_dw_sum  fixed-order sum of the partials (bitwise reproducible).
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -39,32 +42,44 @@ namespace attnres {
 
 namespace {
 
-constexpr int kSlice = 128;   // columns of d per wave in bwd_dhist / bwd_dw_part
-constexpr int kRowTile = 64;  // rows (or reads) accumulated in registers at once
+constexpr int kSlice = 256;  // columns of d per wave in bwd_dhist / bwd_dw_part (4 per lane)
+constexpr int kDwSlice = 128;  // columns of d per wave in bwd_dw_part (32 lanes x 4 per pair)
 constexpr int kChunkTokens = 32;
 
-// two consecutive elements of a row
-template <typename T> struct Pair;
-template <> struct Pair<bf16_t> {
-    __device__ __forceinline__ static void load(rsrc_t r, uint32_t off, float& a, float& b) {
-        const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-        a = __uint_as_float(u << 16);
-        b = __uint_as_float(u & 0xffff0000u);
+// four consecutive elements of a row
+template <typename T> struct Quad;
+template <> struct Quad<bf16_t> {
+    typedef uint32_t raw_t __attribute__((ext_vector_type(2)));
+    raw_t raw;
+    __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
+        raw = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     }
-    __device__ __forceinline__ static void store(rsrc_t r, uint32_t off, float a, float b) {
-        __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a, b), r, off, 0, 0);
+    __device__ __forceinline__ void load(const bf16_t* ptr) { raw = *reinterpret_cast<const raw_t*>(ptr); }
+    __device__ __forceinline__ void to_float(float* f) const {
+        f[0] = __uint_as_float(raw[0] << 16);
+        f[1] = __uint_as_float(raw[0] & 0xffff0000u);
+        f[2] = __uint_as_float(raw[1] << 16);
+        f[3] = __uint_as_float(raw[1] & 0xffff0000u);
+    }
+    __device__ __forceinline__ static void store(rsrc_t r, uint32_t off, const float* f) {
+        const raw_t u = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
     }
 };
-template <> struct Pair<float> {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    __device__ __forceinline__ static void load(rsrc_t r, uint32_t off, float& a, float& b) {
-        const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-        a = __uint_as_float(u[0]);
-        b = __uint_as_float(u[1]);
+template <> struct Quad<float> {
+    u32x4 raw;
+    __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
+        raw = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     }
-    __device__ __forceinline__ static void store(rsrc_t r, uint32_t off, float a, float b) {
-        const u32x2 u = {__float_as_uint(a), __float_as_uint(b)};
-        __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+    __device__ __forceinline__ void load(const float* ptr) { raw = *reinterpret_cast<const u32x4*>(ptr); }
+    __device__ __forceinline__ void to_float(float* f) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(raw[e]);
+    }
+    __device__ __forceinline__ static void store(rsrc_t r, uint32_t off, const float* f) {
+        const u32x4 u = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                         __float_as_uint(f[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(u, r, off, 0, 0);
     }
 };
 
@@ -118,7 +133,12 @@ __global__ __launch_bounds__(64) void bwd_scores_kernel(BwdParams p) {
 
     float* A1 = p.ws_a1 + t * (int64_t)p.n_q * p.nh8;
     float* A2 = p.ws_a2 + t * (int64_t)p.n_q * p.nh8;
-    float* A2T = p.ws_a2t + t * (int64_t)p.n_hist * p.n_q;
+    float* A2T = p.ws_a2t + t * (int64_t)p.n_hist * p.nq8;
+    // the padding reads n_q .. nq8-1 of A2T are zero
+    for (int k = ln; k < p.n_hist * (p.nq8 - p.n_q); k += 64) {
+        const int i = k / (p.nq8 - p.n_q);
+        A2T[(int64_t)i * p.nq8 + p.n_q + k % (p.nq8 - p.n_q)] = 0.f;
+    }
 
     for (int lq0 = 0; lq0 < p.n_q; lq0 += R) {
         const int nr = p.n_q - lq0 < R ? p.n_q - lq0 : R;  // reads in this pass
@@ -290,7 +310,7 @@ __global__ __launch_bounds__(64) void bwd_scores_kernel(BwdParams p) {
                 }
                 A1[(int64_t)lq * p.nh8 + i] = c1;
                 A2[(int64_t)lq * p.nh8 + i] = c2;
-                if (i < p.n_hist) A2T[(int64_t)i * p.n_q + lq] = c2;
+                if (i < p.n_hist) A2T[(int64_t)i * p.nq8 + lq] = c2;
             }
         }
         __syncthreads();
@@ -299,14 +319,19 @@ __global__ __launch_bounds__(64) void bwd_scores_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dhist: one wave per (128-column slice, token).
+// bwd_dhist: one wave per (token, 256-column slice); lane owns 4 columns.
+// Rows are handled in tiles of RT accumulated in registers; the reads' dout
+// and w rows stream through a ring of PF prefetched loads.
 
-template <typename TI, typename TG, typename TO>
+template <typename TI, typename TG, typename TO, int RT, int PF>
 __global__ __launch_bounds__(64) void bwd_dhist_kernel(BwdParams p) {
     const int ln = threadIdx.x;
-    const int e0 = blockIdx.y * kSlice + 2 * ln;  // this lane's two columns
-    const int64_t t = blockIdx.x;
-    const bool valid = e0 < p.d;
+    // slices of one token are neighbours in dispatch order, so the token's
+    // coefficients are fetched from HBM once and then served by L2
+    const int slices = (p.d + kSlice - 1) / kSlice;
+    const int64_t t = blockIdx.x / slices;
+    const int e0 = (int)(blockIdx.x % slices) * kSlice + 4 * ln;  // this lane's four columns
+    const bool valid = e0 < p.d;                   // d % 8 == 0: all four or none
     const int S = p.S;
     const int q_end = p.q_begin + p.n_q;
 
@@ -319,45 +344,65 @@ __global__ __launch_bounds__(64) void bwd_dhist_kernel(BwdParams p) {
     const uint32_t o_off = valid ? (uint32_t)(e0 * sizeof(TO)) : kOOB;
     const uint32_t w_off = valid ? (uint32_t)(e0 * 4) : kOOB;
 
-    const float* __restrict__ A1 = p.ws_a1 + t * (int64_t)p.n_q * p.nh8;
-    const float* __restrict__ A2 = p.ws_a2 + t * (int64_t)p.n_q * p.nh8;
-    const float* __restrict__ C3 = p.ws_c3 + t * p.n_blk;
-    const float* __restrict__ kap = p.ws_kappa + t * p.n_q;
+    const cf32_ptr A1 = const_view(p.ws_a1 + t * (int64_t)p.n_q * p.nh8);
+    const cf32_ptr A2 = const_view(p.ws_a2 + t * (int64_t)p.n_q * p.nh8);
+    const cf32_ptr C3 = const_view(p.ws_c3 + t * p.n_blk);
+    const cf32_ptr kap = const_view(p.ws_kappa + t * p.n_q);
 
-    auto load_row = [&](int i, float& a, float& b) {
+    auto load_row = [&](int i, float* v) {
         const rsrc_t rr = make_rsrc(hist_tok + i * row_elems, (uint64_t)p.d * sizeof(TI));
-        Pair<TI>::load(rr, h_off, a, b);
+        Quad<TI> q;
+        q.load(rr, h_off);
+        q.to_float(v);
     };
     // kappa of read l (0 for reads outside the call)
     auto kappa = [&](int l) { return (l >= p.q_begin && l < q_end) ? kap[l - p.q_begin] : 0.f; };
 
-    for (int rt0 = 0; rt0 < p.n_hist; rt0 += kRowTile) {
-        float dv[kRowTile][2];
+    __shared__ float coef_t[RT];
+    for (int rt0 = 0; rt0 < p.n_hist; rt0 += RT) {
+        float dv[RT][4];
 #pragma unroll
-        for (int i = 0; i < kRowTile; ++i) dv[i][0] = dv[i][1] = 0.f;
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dv[i][e] = 0.f;
 
         // value path and query path: sum over the reads that see a row of the tile
         const int lq0 = rt0 > p.q_begin ? rt0 - p.q_begin : 0;
-        for (int lq = lq0; lq < p.n_q; ++lq) {
-            const int l = p.q_begin + lq;
-            float g0, g1, w0, w1;
-            {
-                const rsrc_t gr = make_rsrc(dout_tok + (int64_t)lq * row_elems, (uint64_t)p.d * sizeof(TG));
-                Pair<TG>::load(gr, g_off, g0, g1);
-                const rsrc_t wr = make_rsrc(p.w + (int64_t)lq * p.d, (uint64_t)p.d * 4);
-                Pair<float>::load(wr, w_off, w0, w1);
-            }
-            const float* a1 = A1 + (int64_t)lq * p.nh8 + rt0;
-            const float* a2 = A2 + (int64_t)lq * p.nh8 + rt0;
+        const int n_l = p.n_q - lq0;
+        Quad<TG> gq[PF];
+        Quad<float> wq[PF];
+        auto issue = [&](int u, int lq) {
+            const rsrc_t gr = make_rsrc(dout_tok + (int64_t)lq * row_elems, (uint64_t)p.d * sizeof(TG));
+            gq[u].load(gr, g_off);
+            const rsrc_t wr = make_rsrc(p.w + (int64_t)lq * p.d, (uint64_t)p.d * 4);
+            wq[u].load(wr, w_off);
+        };
 #pragma unroll
-            for (int q8 = 0; q8 < kRowTile / 8; ++q8) {
-                if (rt0 + 8 * q8 <= l) {  // rows past l have zero coefficients
+        for (int u = 0; u < PF; ++u)
+            if (u < n_l) issue(u, lq0 + u);
+        for (int j0 = 0; j0 < n_l; j0 += PF) {
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const int i = 8 * q8 + q;
-                        const float c1 = a1[i], c2 = a2[i];
-                        dv[i][0] = fmaf(c1, g0, fmaf(c2, w0, dv[i][0]));
-                        dv[i][1] = fmaf(c1, g1, fmaf(c2, w1, dv[i][1]));
+            for (int u = 0; u < PF; ++u) {
+                const int j = j0 + u;
+                if (j >= n_l) break;
+                const int lq = lq0 + j;
+                const int l = p.q_begin + lq;
+                float g[4], w[4];
+                gq[u].to_float(g);
+                wq[u].to_float(w);
+                if (j + PF < n_l) issue(u, lq + PF);
+                const cf32_ptr a1 = A1 + (int64_t)lq * p.nh8 + rt0;
+                const cf32_ptr a2 = A2 + (int64_t)lq * p.nh8 + rt0;
+#pragma unroll
+                for (int q8 = 0; q8 < RT / 8; ++q8) {
+                    if (rt0 + 8 * q8 <= l) {  // rows past l have zero coefficients
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const int i = 8 * q8 + q;
+                            const float c1 = a1[i], c2 = a2[i];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) dv[i][e] = fmaf(c1, g[e], fmaf(c2, w[e], dv[i][e]));
+                        }
                     }
                 }
             }
@@ -369,7 +414,7 @@ __global__ __launch_bounds__(64) void bwd_dhist_kernel(BwdParams p) {
         // Lc the last read whose partial sum holds row m (K = 0 past Lc).  Split
         // into a forward pass (m <= j: (C3[c] + K(j)) times the prefix sum) and
         // a backward pass (m > j: suffix of (C3[c] + K(m)) v_m).
-        const int rt1 = rt0 + kRowTile < p.n_hist ? rt0 + kRowTile : p.n_hist;  // tile end
+        const int rt1 = rt0 + RT < p.n_hist ? rt0 + RT : p.n_hist;  // tile end
         auto block_of = [&](int j) { return j == 0 ? 0 : (j - 1) / S + 1; };
         auto block_first = [&](int c) { return c == 0 ? 0 : (c - 1) * S + 1; };
         auto block_last = [&](int c) {
@@ -385,126 +430,211 @@ __global__ __launch_bounds__(64) void bwd_dhist_kernel(BwdParams p) {
             }
             return C3[c] + K;
         };
-        __shared__ float coef_t[kRowTile];
-        if (rt0 + ln < rt1) coef_t[ln] = coef_of(rt0 + ln);
+        for (int k = ln; k < RT; k += 64)
+            if (rt0 + k < rt1) coef_t[k] = coef_of(rt0 + k);
         __syncthreads();
 
+        // the tile's rows, eight at a time (rows past the tile read zeros)
+        auto load_group = [&](int g0, Quad<TI>* xr) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int j = rt0 + g0 + q;
+                const int jr = j < rt1 ? j : rt1 - 1;
+                const rsrc_t rr = make_rsrc(hist_tok + jr * row_elems, (uint64_t)p.d * sizeof(TI));
+                xr[q].load(rr, j < rt1 ? h_off : kOOB);
+            }
+        };
+
         // forward pass: prefix sums within blocks
-        float pf0 = 0.f, pf1 = 0.f;
+        float pf[4] = {0.f, 0.f, 0.f, 0.f};
         {
             const int c = block_of(rt0);
             for (int m = block_first(c); m < rt0; ++m) {  // rows of the block in earlier tiles
-                float u0, u1;
-                load_row(m, u0, u1);
-                pf0 += u0;
-                pf1 += u1;
+                float u[4];
+                load_row(m, u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pf[e] += u[e];
             }
         }
 #pragma unroll
-        for (int ii = 0; ii < kRowTile; ++ii) {
-            const int j = rt0 + ii;
-            if (j < rt1) {
-                if (ii > 0 && j == block_first(block_of(j))) pf0 = pf1 = 0.f;
-                float v0, v1;
-                load_row(j, v0, v1);
-                pf0 += v0;
-                pf1 += v1;
-                const float k = coef_t[ii];
-                dv[ii][0] = fmaf(-k, pf0, dv[ii][0]);
-                dv[ii][1] = fmaf(-k, pf1, dv[ii][1]);
+        for (int g0 = 0; g0 < RT; g0 += 8) {
+            if (rt0 + g0 < rt1) {
+                Quad<TI> xr[8];
+                load_group(g0, xr);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int ii = g0 + q;
+                    const int j = rt0 + ii;
+                    if (j < rt1) {
+                        if (ii > 0 && j == block_first(block_of(j)))
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) pf[e] = 0.f;
+                        float v[4];
+                        xr[q].to_float(v);
+                        const float k = coef_t[ii];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            pf[e] += v[e];
+                            dv[ii][e] = fmaf(-k, pf[e], dv[ii][e]);
+                        }
+                    }
+                }
             }
         }
         // backward pass: suffix sums within blocks
-        float bs0 = 0.f, bs1 = 0.f;
+        float bs[4] = {0.f, 0.f, 0.f, 0.f};
         {
             const int c = block_of(rt1 - 1);
             for (int m = block_last(c); m >= rt1; --m) {  // rows of the block in later tiles
-                float u0, u1;
-                load_row(m, u0, u1);
+                float u[4];
+                load_row(m, u);
                 const float k = coef_of(m);
-                bs0 = fmaf(k, u0, bs0);
-                bs1 = fmaf(k, u1, bs1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bs[e] = fmaf(k, u[e], bs[e]);
             }
         }
 #pragma unroll
-        for (int ii = kRowTile - 1; ii >= 0; --ii) {
-            const int j = rt0 + ii;
-            if (j < rt1) {
-                dv[ii][0] -= bs0;
-                dv[ii][1] -= bs1;
-                if (j == block_first(block_of(j))) {
-                    bs0 = bs1 = 0.f;
-                } else {
-                    float v0, v1;
-                    load_row(j, v0, v1);
-                    const float k = coef_t[ii];
-                    bs0 = fmaf(k, v0, bs0);
-                    bs1 = fmaf(k, v1, bs1);
+        for (int g0 = RT - 8; g0 >= 0; g0 -= 8) {
+            if (rt0 + g0 < rt1) {
+                Quad<TI> xr[8];
+                load_group(g0, xr);
+#pragma unroll
+                for (int q = 7; q >= 0; --q) {
+                    const int ii = g0 + q;
+                    const int j = rt0 + ii;
+                    if (j < rt1) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) dv[ii][e] -= bs[e];
+                        if (j == block_first(block_of(j))) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) bs[e] = 0.f;
+                        } else {
+                            float v[4];
+                            xr[q].to_float(v);
+                            const float k = coef_t[ii];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) bs[e] = fmaf(k, v[e], bs[e]);
+                        }
+                    }
                 }
             }
         }
         __syncthreads();  // coef_t is rewritten by the next tile
 
 #pragma unroll
-        for (int ii = 0; ii < kRowTile; ++ii) {
+        for (int ii = 0; ii < RT; ++ii) {
             const int j = rt0 + ii;
             if (j < rt1) {
                 const rsrc_t orr = make_rsrc(dh_tok + j * row_elems, (uint64_t)p.d * sizeof(TO));
-                Pair<TO>::store(orr, o_off, dv[ii][0], dv[ii][1]);
+                Quad<TO>::store(orr, o_off, dv[ii]);
             }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dw_part: one wave per (128-column slice, chunk of tokens).
+// bwd_dw_part: per chunk of tokens, the partial  dw[l][k] = sum over the
+// chunk's (token, row) pairs of A2T[pair][l] x[pair][k]  -- a dense
+// contraction over pairs, done on the matrix cores in fp32
+// (v_mfma_f32_32x32x2f32: D[32x32] += A[32x2] B[2x32]).
+// One wave per (128-column slice, chunk); it accumulates a tile of 32 reads.
+// Lane j (half h = j / 32, m = j % 32) supplies, for a step of two pairs:
+//   A[i = m][k = h] = x[pair 2s + h][column c0 + 4m + e]  (MFMA number e = 0..3)
+//   B[k = h][n = m] = A2T[pair 2s + h][read qt0 + m]
+// so every half-wave reads 128 contiguous columns of one history row and 32
+// contiguous coefficients.  Lane j, accumulator register r then holds
+// D[i][n = m] with i = 8 (r / 4) + 4 h + r % 4, i.e. the partial of read
+// qt0 + m at columns c0 + 4i + e.
 
-template <typename TI>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename TI, int PF>
 __global__ __launch_bounds__(64) void bwd_dw_part_kernel(BwdParams p) {
+    constexpr int QT = 32;
     const int ln = threadIdx.x;
-    const int e0 = blockIdx.x * kSlice + 2 * ln;
-    const int chunk = blockIdx.y;
-    const bool valid = e0 < p.d;
-    const uint32_t h_off = valid ? (uint32_t)(e0 * sizeof(TI)) : kOOB;
+    const int h = ln >> 5, m = ln & 31;
+    const int slices = (p.d + kDwSlice - 1) / kDwSlice;
+    const int c0 = (int)(blockIdx.x % slices) * kDwSlice;
+    const int chunk = (int)(blockIdx.x / slices);
+    const bool valid = c0 + 4 * m < p.d;  // d % 8 == 0: all four columns or none
+    const int col0 = valid ? c0 + 4 * m : 0;  // a column inside the row for lanes past d
     const int64_t row_elems = p.T * (int64_t)p.d;
     const int64_t t_lo = (int64_t)chunk * kChunkTokens;
-    const int64_t t_hi = t_lo + kChunkTokens < p.T ? t_lo + kChunkTokens : p.T;
+    const int n_tok = (int)(p.T - t_lo < kChunkTokens ? p.T - t_lo : kChunkTokens);
+    const TI* hist_chunk = static_cast<const TI*>(p.hist) + t_lo * p.d;
+    const float* a2t_chunk = p.ws_a2t + t_lo * (int64_t)p.n_hist * p.nq8;
 
-    for (int qt0 = 0; qt0 < p.n_q; qt0 += kRowTile) {
-        float acc[kRowTile][2];
+    for (int qt0 = 0; qt0 < p.n_q; qt0 += QT) {
+        const int nqt = p.n_q - qt0 < QT ? p.n_q - qt0 : QT;
+        const int n_rows = p.q_begin + qt0 + nqt;  // rows 0 .. last read of the tile
+        const int total = n_tok * n_rows;          // pairs of the chunk
+        const int n_steps = (total + 1) / 2;
+        const bool coef_ok = qt0 + m < p.nq8;      // A2T columns past nq8 belong to the next pair
+        f32x16 acc[4];
 #pragma unroll
-        for (int q = 0; q < kRowTile; ++q) acc[q][0] = acc[q][1] = 0.f;
-        const int l_max = p.q_begin + (qt0 + kRowTile < p.n_q ? qt0 + kRowTile : p.n_q) - 1;
-        for (int64_t t = t_lo; t < t_hi; ++t) {
-            const TI* hist_tok = static_cast<const TI*>(p.hist) + t * p.d;
-            const float* __restrict__ a2t = p.ws_a2t + t * (int64_t)p.n_hist * p.n_q + qt0;
-            for (int i = 0; i <= l_max; ++i) {
-                float v0, v1;
-                const rsrc_t rr = make_rsrc(hist_tok + i * row_elems, (uint64_t)p.d * sizeof(TI));
-                Pair<TI>::load(rr, h_off, v0, v1);
-                const float* a = a2t + (int64_t)i * p.n_q;
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int q8 = 0; q8 < kRowTile / 8; ++q8) {
-                    if (qt0 + 8 * q8 < p.n_q) {
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const int qq = 8 * q8 + q;
-                            const float c = qt0 + qq < p.n_q ? a[qq] : 0.f;
-                            acc[qq][0] = fmaf(c, v0, acc[qq][0]);
-                            acc[qq][1] = fmaf(c, v1, acc[qq][1]);
-                        }
-                    }
+            for (int r = 0; r < 16; ++r) acc[e][r] = 0.f;
+
+        Quad<TI> xr[PF];
+        float cr[PF];
+        bool lv[PF], lx[PF];  // coefficient live, history value live
+        int it = 0, ii = 0;  // (token, row) of pair 2s of the next step to issue
+        int s_issue = 0;
+        auto issue = [&](int u) {
+            // this lane's pair: 2s + h
+            int kt = it, ki = ii;
+            if (h) {
+                if (++ki == n_rows) {
+                    ki = 0;
+                    ++kt;
                 }
             }
-        }
-        if (valid) {
-            float* part = p.ws_dwpart + (int64_t)chunk * p.n_q * p.d;
+            const bool live = 2 * s_issue + h < total;
+            const int kt_c = live ? kt : 0, ki_c = live ? ki : 0;
+            // the pair differs between the half-waves, so these are plain
+            // 64-bit global loads (a buffer descriptor must be wave-uniform);
+            // dead lanes read a valid address and are zeroed at use
+            xr[u].load(hist_chunk + kt_c * (int64_t)p.d + ki_c * row_elems + col0);
+            const int q = coef_ok ? qt0 + m : 0;
+            cr[u] = a2t_chunk[((int64_t)kt_c * p.n_hist + ki_c) * p.nq8 + q];
+            lv[u] = live && coef_ok;  // B operand: read qt0 + m, any column
+            lx[u] = live && valid;
+            // advance by two pairs
+            ii += 2;
+            while (ii >= n_rows) {
+                ii -= n_rows;
+                ++it;
+            }
+            ++s_issue;
+        };
 #pragma unroll
-            for (int q = 0; q < kRowTile; ++q) {
-                if (qt0 + q < p.n_q) {
-                    part[(int64_t)(qt0 + q) * p.d + e0] = acc[q][0];
-                    part[(int64_t)(qt0 + q) * p.d + e0 + 1] = acc[q][1];
-                }
+        for (int u = 0; u < PF; ++u)
+            if (u < n_steps) issue(u);
+        for (int s0 = 0; s0 < n_steps; s0 += PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const int st = s0 + u;
+                if (st >= n_steps) break;
+                float v[4];
+                xr[u].to_float(v);
+                const float c = lv[u] ? cr[u] : 0.f;
+                const bool x_live = lx[u];
+                if (st + PF < n_steps) issue(u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[e] = __builtin_amdgcn_mfma_f32_32x32x2f32(x_live ? v[e] : 0.f, c, acc[e], 0, 0, 0);
+            }
+        }
+        if (m < nqt) {
+            float* part = p.ws_dwpart + ((int64_t)chunk * p.n_q + qt0 + m) * p.d;
+            const rsrc_t pr = make_rsrc(part, (uint64_t)p.d * 4);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = 8 * (r / 4) + 4 * h + r % 4;
+                const int col = c0 + 4 * i;
+                const float o[4] = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+                Quad<float>::store(pr, col < p.d ? (uint32_t)(col * 4) : kOOB, o);
             }
         }
     }
@@ -541,6 +671,7 @@ BwdLayout bwd_layout(int64_t S, int64_t n_hist, int64_t T, int64_t d, int64_t n_
     BwdLayout L;
     auto up = [](int64_t x, int64_t a) { return (x + a - 1) / a * a; };
     L.nh8 = up(n_hist, 8);
+    L.nq8 = up(n_q, 8);
     L.n_blk = 1 + (n_hist - 1 + S - 1) / S;
     L.nx = 1 + (n_hist - 1) / S + 1;
     L.n_chunks = (T + kChunkTokens - 1) / kChunkTokens;
@@ -552,7 +683,7 @@ BwdLayout bwd_layout(int64_t S, int64_t n_hist, int64_t T, int64_t d, int64_t n_
     };
     L.off_a1 = take(T * n_q * L.nh8);
     L.off_a2 = take(T * n_q * L.nh8);
-    L.off_a2t = take(T * n_hist * n_q);
+    L.off_a2t = take(T * n_hist * L.nq8);
     L.off_c3 = take(T * L.n_blk);
     L.off_kappa = take(T * n_q);
     L.off_dwpart = take(L.n_chunks * n_q * d);
@@ -589,11 +720,19 @@ hipError_t launch_scores(const BwdParams& p, hipStream_t stream) {
 template <typename TI, typename TG, typename TO>
 hipError_t launch_rest(const BwdParams& p, int n_chunks, hipStream_t stream) {
     const unsigned slices = (unsigned)((p.d + kSlice - 1) / kSlice);
-    hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO>), dim3((unsigned)p.T, slices), dim3(64), 0,
-                       stream, p);
+    if (p.n_hist <= 8)
+        hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 8, 4>), dim3((unsigned)(p.T * slices)), dim3(64),
+                           0, stream, p);
+    else if (p.n_hist <= 16)
+        hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 16, 4>), dim3((unsigned)(p.T * slices)),
+                           dim3(64), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 32, 4>), dim3((unsigned)(p.T * slices)),
+                           dim3(64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dw_part_kernel<TI>), dim3(slices, (unsigned)n_chunks), dim3(64), 0,
+    const unsigned dw_slices = (unsigned)((p.d + kDwSlice - 1) / kDwSlice);
+    hipLaunchKernelGGL((bwd_dw_part_kernel<TI, 8>), dim3(dw_slices * (unsigned)n_chunks), dim3(64), 0,
                        stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

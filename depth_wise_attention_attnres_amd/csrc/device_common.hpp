@@ -38,6 +38,13 @@ constexpr uint32_t kOOB = 0x40000000u;   // >= every num_records we build
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9-family raw buffer, 32-bit data
 constexpr int kAuxNT = 2;                // non-temporal cache policy
 
+// Read-only view of memory that a kernel never writes.  Loads through the
+// constant address space with a wave-uniform address become scalar loads,
+// which are counted apart from the vector loads, so waiting for them does
+// not drain the vector loads in flight.
+typedef const __attribute__((address_space(4))) float* cf32_ptr;
+__device__ __forceinline__ cf32_ptr const_view(const float* p) { return (cf32_ptr)p; }
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
     const uint32_t n = bytes < kOOB ? (uint32_t)bytes : kOOB;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdPara
     if (t >= p.T) return;  // whole token groups leave together
 
     const int64_t row_elems = p.T * (int64_t)p.d;            // elements between rows
-    const uint64_t blk_elems = (uint64_t)(p.T - tok0) * p.d;  // this block's tokens to the end
+    const int64_t blk_tok = p.T - tok0 < TPB ? p.T - tok0 : TPB;  // tokens of this block
+    const uint64_t blk_elems = (uint64_t)blk_tok * p.d;
     const TI* hist_blk = static_cast<const TI*>(p.hist) + tok0 * p.d;
     TO* out_blk = static_cast<TO*>(p.out) + tok0 * p.d;
 
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdPara
                 for (int c = 0; c < NCH; ++c) buf[u][c].load(rr, in_off[c]);
             }
             if (i < p.rinv_valid) {
-                const rsrc_t cr = make_rsrc(p.rinv + (int64_t)i * p.T + tok0, (uint64_t)(p.T - tok0) * 4);
+                const rsrc_t cr = make_rsrc(p.rinv + (int64_t)i * p.T + tok0, (uint64_t)blk_tok * 4);
                 rbuf[u] = load_f32(cr, tok_f32_off);
             }
         };

@@ -47,6 +47,7 @@ hipError_t launch_block_stream(const BlockFwdParams& p, hipStream_t stream);
 // Backward workspace layout (byte offsets; every region 256-byte aligned).
 struct BwdLayout {
     int64_t nh8;       // history rows rounded up to 8 (row length of A1 / A2)
+    int64_t nq8;       // reads rounded up to 8 (row length of A2T, zero padded)
     int64_t n_blk;     // v_0 + every block, complete or not
     int64_t nx;        // most sources a read can see
     int64_t n_chunks;  // token chunks of the dw partial sums
@@ -63,12 +64,12 @@ struct BwdParams {
     float* dw;          // [n_q][d]
     int64_t T;
     int d, nc, n_hist, q_begin, n_q, S;
-    int nh8, n_blk, nx;
+    int nh8, nq8, n_blk, nx;
     float eps, inv_d;
     attnres_dtype hist_dt, dout_dt, dhist_dt;
     float* ws_a1;       // [T][n_q][nh8]   alpha of the source holding each row
     float* ws_a2;       // [T][n_q][nh8]   ds * r of that source
-    float* ws_a2t;      // [T][n_hist][n_q] the same, transposed
+    float* ws_a2t;      // [T][n_hist][nq8] the same, transposed (reads past n_q are 0)
     float* ws_c3;       // [T][n_blk]      sum over reads of ds r^2 s / d per v_0 / block
     float* ws_kappa;    // [T][n_q]        ds r^2 s / d of each read's partial sum
     float* ws_dwpart;   // [n_chunks][n_q][d]

@@ -77,6 +77,9 @@ def test_full_fwd_validation(ar):
     assert _full(ar, eps=float("inf")) == INVALID
     assert _full(ar, eps=float("nan")) == INVALID
     assert _full(ar, T=1 << 40) == UNSUPPORTED
+    assert _full(ar, T=(1 << 27) + 1, d=8, n_hist=1, n_q=1) == UNSUPPORTED
+    assert "2^27" in ar.last_error()
+    assert _full(ar, T=1 << 27, d=8, n_hist=1, n_q=1, hist=None) == INVALID  # size accepted
 
 
 def test_empty_calls_launch_nothing(ar):
