@@ -538,13 +538,16 @@ __global__ __launch_bounds__(64) void bwd_dhist_kernel(BwdParams p) {
 // contraction over pairs, done on the matrix cores in fp32
 // (v_mfma_f32_32x32x2f32: D[32x32] += A[32x2] B[2x32]).
 // One wave per (128-column slice, chunk); it accumulates a tile of 32 reads.
-// Lane j (half h = j / 32, m = j % 32) supplies, for a step of two pairs:
-//   A[i = m][k = h] = x[pair 2s + h][column c0 + 4m + e]  (MFMA number e = 0..3)
-//   B[k = h][n = m] = A2T[pair 2s + h][read qt0 + m]
-// so every half-wave reads 128 contiguous columns of one history row and 32
-// contiguous coefficients.  Lane j, accumulator register r then holds
-// D[i][n = m] with i = 8 (r / 4) + 4 h + r % 4, i.e. the partial of read
-// qt0 + m at columns c0 + 4i + e.
+// A step takes one history row i and two neighbouring tokens 2u, 2u + 1 of
+// the chunk; lane j (half h = j / 32, m = j % 32) supplies
+//   A[i' = m][k = h] = x[i][token 2u + h][column c0 + 4m + e]  (MFMA e = 0..3)
+//   B[k = h][n = m]  = A2T[token 2u + h][i][read qt0 + m]
+// so a half-wave reads 128 contiguous columns of one row and 32 contiguous
+// coefficients, and the two halves differ by one token: the buffer
+// descriptors stay wave-uniform and every lane offset is fixed.  Lane j,
+// accumulator register r then holds D[i'][n = m] with
+// i' = 8 (r / 4) + 4 h + r % 4: the partial of read qt0 + m at columns
+// c0 + 4 i' + e.
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -557,19 +560,25 @@ __global__ __launch_bounds__(64) void bwd_dw_part_kernel(BwdParams p) {
     const int c0 = (int)(blockIdx.x % slices) * kDwSlice;
     const int chunk = (int)(blockIdx.x / slices);
     const bool valid = c0 + 4 * m < p.d;  // d % 8 == 0: all four columns or none
-    const int col0 = valid ? c0 + 4 * m : 0;  // a column inside the row for lanes past d
     const int64_t row_elems = p.T * (int64_t)p.d;
     const int64_t t_lo = (int64_t)chunk * kChunkTokens;
     const int n_tok = (int)(p.T - t_lo < kChunkTokens ? p.T - t_lo : kChunkTokens);
+    const int n_pairs = (n_tok + 1) / 2;  // token pairs of the chunk
     const TI* hist_chunk = static_cast<const TI*>(p.hist) + t_lo * p.d;
     const float* a2t_chunk = p.ws_a2t + t_lo * (int64_t)p.n_hist * p.nq8;
+    const int64_t a2t_tok = (int64_t)p.n_hist * p.nq8;  // floats per token of A2T
+    // fixed lane offsets inside a step's two-token window
+    const uint32_t x_off = (uint32_t)((h * p.d + c0 + 4 * m) * sizeof(TI));
+    const uint64_t x_bytes = 2 * (uint64_t)p.d * sizeof(TI);
 
     for (int qt0 = 0; qt0 < p.n_q; qt0 += QT) {
         const int nqt = p.n_q - qt0 < QT ? p.n_q - qt0 : QT;
         const int n_rows = p.q_begin + qt0 + nqt;  // rows 0 .. last read of the tile
-        const int total = n_tok * n_rows;          // pairs of the chunk
-        const int n_steps = (total + 1) / 2;
-        const bool coef_ok = qt0 + m < p.nq8;      // A2T columns past nq8 belong to the next pair
+        const int n_steps = n_rows * n_pairs;
+        // coefficient of read qt0 + m; reads past n_q are zero in A2T, columns
+        // past nq8 would belong to the next row
+        const bool coef_ok = qt0 + m < p.nq8;
+        const uint32_t c_off = (uint32_t)((h * a2t_tok + (coef_ok ? qt0 + m : 0)) * 4);
         f32x16 acc[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -578,35 +587,19 @@ __global__ __launch_bounds__(64) void bwd_dw_part_kernel(BwdParams p) {
 
         Quad<TI> xr[PF];
         float cr[PF];
-        bool lv[PF], lx[PF];  // coefficient live, history value live
-        int it = 0, ii = 0;  // (token, row) of pair 2s of the next step to issue
-        int s_issue = 0;
+        int ir = 0, iu = 0;  // (row, token pair) of the next step to issue
         auto issue = [&](int u) {
-            // this lane's pair: 2s + h
-            int kt = it, ki = ii;
-            if (h) {
-                if (++ki == n_rows) {
-                    ki = 0;
-                    ++kt;
-                }
+            const int t0 = 2 * iu;
+            const bool live = t0 + h < n_tok && valid;
+            const rsrc_t rx = make_rsrc(hist_chunk + ir * row_elems + (int64_t)t0 * p.d, x_bytes);
+            xr[u].load(rx, live ? x_off : kOOB);
+            const rsrc_t rc = make_rsrc(a2t_chunk + t0 * a2t_tok + (int64_t)ir * p.nq8,
+                                        (uint64_t)(a2t_tok + p.nq8) * 4);
+            cr[u] = load_f32(rc, (t0 + h < n_tok && coef_ok) ? c_off : kOOB);
+            if (++iu == n_pairs) {
+                iu = 0;
+                ++ir;
             }
-            const bool live = 2 * s_issue + h < total;
-            const int kt_c = live ? kt : 0, ki_c = live ? ki : 0;
-            // the pair differs between the half-waves, so these are plain
-            // 64-bit global loads (a buffer descriptor must be wave-uniform);
-            // dead lanes read a valid address and are zeroed at use
-            xr[u].load(hist_chunk + kt_c * (int64_t)p.d + ki_c * row_elems + col0);
-            const int q = coef_ok ? qt0 + m : 0;
-            cr[u] = a2t_chunk[((int64_t)kt_c * p.n_hist + ki_c) * p.nq8 + q];
-            lv[u] = live && coef_ok;  // B operand: read qt0 + m, any column
-            lx[u] = live && valid;
-            // advance by two pairs
-            ii += 2;
-            while (ii >= n_rows) {
-                ii -= n_rows;
-                ++it;
-            }
-            ++s_issue;
         };
 #pragma unroll
         for (int u = 0; u < PF; ++u)
@@ -618,23 +611,23 @@ __global__ __launch_bounds__(64) void bwd_dw_part_kernel(BwdParams p) {
                 if (st >= n_steps) break;
                 float v[4];
                 xr[u].to_float(v);
-                const float c = lv[u] ? cr[u] : 0.f;
-                const bool x_live = lx[u];
+                const float c = cr[u];
                 if (st + PF < n_steps) issue(u);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    acc[e] = __builtin_amdgcn_mfma_f32_32x32x2f32(x_live ? v[e] : 0.f, c, acc[e], 0, 0, 0);
+                    acc[e] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[e], c, acc[e], 0, 0, 0);
             }
         }
         if (m < nqt) {
             float* part = p.ws_dwpart + ((int64_t)chunk * p.n_q + qt0 + m) * p.d;
-            const rsrc_t pr = make_rsrc(part, (uint64_t)p.d * 4);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = 8 * (r / 4) + 4 * h + r % 4;
                 const int col = c0 + 4 * i;
-                const float o[4] = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-                Quad<float>::store(pr, col < p.d ? (uint32_t)(col * 4) : kOOB, o);
+                if (col < p.d) {
+                    const float o[4] = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+                    *reinterpret_cast<f32x4*>(part + col) = {o[0], o[1], o[2], o[3]};
+                }
             }
         }
     }
