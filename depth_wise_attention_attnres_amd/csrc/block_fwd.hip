@@ -21,13 +21,16 @@
 //       then requested (the rows of this chunk are dead);
 //   A2  per-lane partial dots (queries double-buffered from L2), summed over
 //       each 16-lane row with DPP butterflies; each row's sums go to LDS;
-//   A3  wave 0, one 16-lane row per read and one lane per source: adds the
-//       row sums (fixed order), forms scores, the phase-1 max and sum over
-//       the frozen sources, merges the partial sum by the log-sum-exp rule,
-//       and publishes the coefficients;
-//   B   every lane forms its chunk of the outputs from register sources.
+//   A3  every wave, one 16-lane row per read and one lane per source: adds
+//       the row sums (fixed order, so all waves agree bitwise), forms scores,
+//       the phase-1 max and sum over the frozen sources, merges the partial
+//       sum by the log-sum-exp rule, and keeps each coefficient in the lane
+//       that computed it;
+//   B   every lane forms its chunk of the outputs from register sources,
+//       fetching the coefficients with readlane.
 // The chunk body is instantiated per block group G, so every loop over
-// sources has a compile-time bound.  Two workgroup barriers per chunk.
+// sources has a compile-time bound.  One workgroup barrier per chunk (the
+// row sums are double-buffered).
 // Block sums are fp32 and never rounded.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -47,16 +50,18 @@ struct BlockState {
     float part_sum[8];    // running partial sum of the current block
     Chunk<TI> rows[CR];     // raw rows of the chunk (then of the next chunk)
     Chunk<float> wbuf[2];   // pseudo-queries, double-buffered
+    float rsv;            // RMS scale of source (lane % 16), kept by every wave
+    int buf;              // which half of the row-sum buffer this chunk uses
 };
 
-// Shared-memory layout of one workgroup (nw waves, 4 * nw 16-lane rows).
+// Shared-memory layout of one workgroup (nw waves, 4 * nw 16-lane rows): the
+// row sums of a chunk, double-buffered so that one barrier per chunk suffices
+// (a wave can only overwrite a half after every wave has passed the next
+// chunk's barrier, i.e. has finished reading it).
 template <int NSRC, int CR>
 struct BlockShared {
     int row_slots;  // 16-lane rows in the workgroup
-    float* part;  // [kVals][row_slots] row sums
-    float* fin;   // [kVals] totals
-    float* coef;  // [CR][kStride] output coefficients (slot NSRC: the partial)
-    float* rs;    // [NSRC] RMS scale of each source
+    float* part;    // [2][kVals][row_slots] row sums
 };
 
 // Everything one chunk does, for a chunk of block group G (sources 0..G).
@@ -72,6 +77,7 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
     constexpr int kVals = BlockLds<NSRC, CR>::kVals;
     constexpr int kSq = CR * kStride;
     const int kRowSlots = sh.row_slots;
+    float* const part = sh.part + st.buf * kVals * kRowSlots;
     const int tid = threadIdx.x;
     const int row_slot = tid >> 4;
     const int64_t row_elems = p.T * (int64_t)p.d;
@@ -143,7 +149,7 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
 #pragma unroll
         for (int e = 0; e < 8; ++e) sq = fmaf(st.src[G][e], st.src[G][e], sq);
         sq = tg_sum<16>(sq);
-        sh.part[kSq * kRowSlots + row_slot] = sq;
+        part[kSq * kRowSlots + row_slot] = sq;
     }
 #pragma unroll
     for (int k = 0; k < CR; ++k) {
@@ -188,7 +194,7 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
             for (int c = 0; c < kV; ++c) v[c] += dpp<kDppHalfMirror>(v[c]);
 #pragma unroll
             for (int c = 0; c < kV; ++c) v[c] += dpp<kDppMirror>(v[c]);
-            float* pp = sh.part + k * kStride * kRowSlots + row_slot;
+            float* pp = part + k * kStride * kRowSlots + row_slot;
 #pragma unroll
             for (int c = 0; c <= G; ++c) pp[c * kRowSlots] = v[c];
             pp[NSRC * kRowSlots] = v[G + 1];
@@ -197,17 +203,21 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
     }
     __syncthreads();
 
-    // ---- A3: scores, phase-1 softmax and phase-2 merge on wave 0 ----------
-    // Lane (k, c) = (tid / 16, tid % 16) handles source c of read k, so each
+    // ---- A3: scores, phase-1 softmax and phase-2 merge, in every wave --------
+    // Lane (k, c) = (lane / 16, lane % 16) handles source c of read k, so each
     // 16-lane DPP row is one read: c <= G are the frozen sources, c = G + 1 is
-    // the partial sum.  Row sums of the dots are added in a fixed order.
+    // the partial sum.  Row sums of the dots are added in a fixed order, so
+    // every wave computes bitwise the same coefficients and keeps them in a
+    // register; the outputs fetch them with readlane (no second barrier).
     static_assert(CR <= 4 && NSRC + 1 <= 16, "one 16-lane row per read");
-    if (tid < 64) {
-        const int k = tid >> 4, c = tid & 15;
+    float cv = 0.f;  // coefficient of (read k, source c)
+    {
+        const int lane = tid & 63;
+        const int k = lane >> 4, c = lane & 15;
         const int l = l0 + k;
         const bool read_ok = k < n && l >= p.q_begin;
         auto total = [&](int idx) {
-            const f32x4* q = reinterpret_cast<const f32x4*>(sh.part + idx * kRowSlots);
+            const f32x4* q = reinterpret_cast<const f32x4*>(part + idx * kRowSlots);
             float s = 0.f;
             for (int r = 0; r < kRowSlots / 4; ++r) {
                 const f32x4 a = q[r];
@@ -218,14 +228,11 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
             }
             return s;
         };
+        if (new_src && c == G) st.rsv = fast_rsqrt(fmaf(total(kSq), p.inv_d, p.eps));
         const bool has_p = read_ok && l != G * S;
         float s2 = -INFINITY;  // score (log2 units) of a frozen source
         float sp = -INFINITY;  // score of the partial sum
-        if (read_ok && c <= G) {
-            const float r = (new_src && c == G) ? fast_rsqrt(fmaf(total(kSq), p.inv_d, p.eps))
-                                                : sh.rs[c];
-            s2 = r * total(k * kStride + c) * kLog2e;
-        }
+        if (read_ok && c <= G) s2 = st.rsv * total(k * kStride + c) * kLog2e;
         if (has_p && c == G + 1) {
             const float rp = fast_rsqrt(fmaf(total(k * kStride + NSRC + 1), p.inv_d, p.eps));
             sp = rp * total(k * kStride + NSRC) * kLog2e;
@@ -238,30 +245,28 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
         const float A = Z1 * fast_exp2(M1 - M);
         const float B = has_p ? fast_exp2(spr - M) : 0.f;
         const float inv = 1.0f / (A + B);
-        if (read_ok) {
-            float* cf = sh.coef + k * kStride;
-            if (c <= G) cf[c] = e * fast_exp2(M1 - M) * inv;
-            if (c == G + 1) cf[NSRC] = B * inv;
-            if (c == 0 && p.lse != nullptr)
-                p.lse[(int64_t)(l - p.q_begin) * p.T + t] = (M + fast_log2(A + B)) * kLn2;
-        }
-        if (new_src && tid == G) sh.rs[G] = fast_rsqrt(fmaf(total(kSq), p.inv_d, p.eps));
+        if (c <= G) cv = e * fast_exp2(M1 - M) * inv;
+        if (c == G + 1) cv = B * inv;
+        if (read_ok && tid == lane && c == 0 && p.lse != nullptr)  // wave 0 stores lse
+            p.lse[(int64_t)(l - p.q_begin) * p.T + t] = (M + fast_log2(A + B)) * kLn2;
     }
-    __syncthreads();
+    st.buf ^= 1;
+    auto coef_at = [&](int lane_idx) {
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv), lane_idx));
+    };
 
     // ---- B: outputs ------------------------------------------------------
 #pragma unroll
     for (int k = 0; k < CR; ++k) {
         const int l = l0 + k;
         if (k < n && l >= p.q_begin) {
-            const float* cf = sh.coef + k * kStride;
             float o[8];
-            const float cp = l != G * S ? cf[NSRC] : 0.f;
+            const float cp = l != G * S ? coef_at(16 * k + G + 1) : 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = cp * pk[k][e];
 #pragma unroll
             for (int c = 0; c <= G; ++c) {
-                const float a = cf[c];
+                const float a = coef_at(16 * k + c);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] = fmaf(a, st.src[c][e], o[e]);
             }
@@ -309,9 +314,6 @@ void block_fwd_twophase_kernel(BlockFwdParams p) {
     BlockShared<NSRC, CR> sh;
     sh.row_slots = kRowSlots;
     sh.part = lds;
-    sh.fin = sh.part + kVals * kRowSlots;
-    sh.coef = sh.fin + kVals;
-    sh.rs = sh.coef + CR * kStride;
 
     const int ln = threadIdx.x;                   // chunk index of d owned by this lane
     const int64_t t = blockIdx.x;                 // token
@@ -324,6 +326,8 @@ void block_fwd_twophase_kernel(BlockFwdParams p) {
     const int64_t row_elems = p.T * (int64_t)p.d;
 
     BlockState<TI, NSRC, CR> st;
+    st.rsv = 0.f;
+    st.buf = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.part_sum[e] = 0.f;
 #pragma unroll
@@ -376,7 +380,7 @@ template <typename TI, int NSRC, int CR>
 hipError_t launch_twophase(const BlockFwdParams& p, int nw, hipStream_t stream) {
     constexpr int kStride = BlockLds<NSRC, CR>::kStride;
     constexpr int kVals = BlockLds<NSRC, CR>::kVals;
-    const size_t lds = sizeof(float) * (kVals * 4 * nw + kVals + CR * kStride + NSRC);
+    const size_t lds = sizeof(float) * 2 * kVals * 4 * nw;
     hipLaunchKernelGGL((block_fwd_twophase_kernel<TI, NSRC, CR>), dim3((unsigned)p.T),
                        dim3(64 * nw), lds, stream, p);
     return hipGetLastError();
