@@ -280,6 +280,9 @@ def extra_measurements(dev):
             "fwd_ms": ms_f, "bwd_ms": ms_b,
             "fwd_bwd_tokens_per_s": T / ((ms_f + ms_b) * 1e-3),
             "fwd_algorithmic_GBps": (2 * n * T * d * 2) / (ms_f * 1e-3) / 1e9,
+            # compulsory traffic of the backward: history and dout read, dhist written
+            "bwd_algorithmic_GBps": (3 * n * T * d * 2) / (ms_b * 1e-3) / 1e9,
+            "bwd_frac_of_hbm_peak": (3 * n * T * d * 2) / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
         }
         del ws
     return res
