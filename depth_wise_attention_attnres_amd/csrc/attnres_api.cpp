@@ -253,6 +253,7 @@ int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dt
     p.ws_a1 = reinterpret_cast<float*>(ws + L.off_a1);
     p.ws_a2 = reinterpret_cast<float*>(ws + L.off_a2);
     p.ws_a2t = reinterpret_cast<float*>(ws + L.off_a2t);
+    p.ws_wsplit = reinterpret_cast<uint16_t*>(ws + L.off_wsplit);
     p.ws_c3 = reinterpret_cast<float*>(ws + L.off_c3);
     p.ws_kappa = reinterpret_cast<float*>(ws + L.off_kappa);
     p.ws_dwpart = reinterpret_cast<float*>(ws + L.off_dwpart);

@@ -51,7 +51,7 @@ struct BwdLayout {
     int64_t n_blk;     // v_0 + every block, complete or not
     int64_t nx;        // most sources a read can see
     int64_t n_chunks;  // token chunks of the dw partial sums
-    int64_t off_a1, off_a2, off_a2t, off_c3, off_kappa, off_dwpart;
+    int64_t off_a1, off_a2, off_a2t, off_c3, off_kappa, off_dwpart, off_wsplit;
     int64_t bytes;
 };
 BwdLayout bwd_layout(int64_t S, int64_t n_hist, int64_t T, int64_t d, int64_t n_q);
@@ -73,6 +73,7 @@ struct BwdParams {
     float* ws_c3;       // [T][n_blk]      sum over reads of ds r^2 s / d per v_0 / block
     float* ws_kappa;    // [T][n_q]        ds r^2 s / d of each read's partial sum
     float* ws_dwpart;   // [n_chunks][n_q][d]
+    uint16_t* ws_wsplit;  // [3][n_q][d] bf16: w = hi + mid + lo (matrix-core scores)
 };
 hipError_t launch_bwd(const BwdParams& p, int n_chunks, hipStream_t stream);
 // zero `bytes` (a multiple of 4) of device memory with a kernel
