@@ -233,6 +233,23 @@ def _time(fn, stream, reps, warm):
     return a.elapsed_time(b) / reps
 
 
+def model_order_bytes_per_token(n, d, S, vb=2, ob=2):
+    """HBM bytes per token of one model-order Block sweep (phase 1 per group:
+    frozen fp32 sources read, new row and partial sum read, new block written,
+    the group's fp32 phase-1 sums and log-sum-exps written, the first read's
+    output; phase 2 per row: row, partial sum and phase-1 sum read, partial sum
+    and output written).  Queries come from L2 and are not counted."""
+    total = 0
+    n_blk = 1 + (n - 1) // S
+    for m in range(n_blk):
+        n_reads = min(S, n - m * S)
+        total += 4 * d * m + vb * d + (4 * d if (m > 0 and S > 1) else 0) + 4 * d
+        total += n_reads * (4 * d + 4) + ob * d + 4 + 4 * (m + 1)
+        for k in range(1, n_reads):
+            total += vb * d + (4 * d if k > 1 else 0) + 4 * d + 4 + 4 * d + ob * d + 4
+    return total
+
+
 def extra_measurements(dev):
     """The other rows of the hot path at their workload sizes: the Block
     two-phase forward over a 128K-token S=8 history (one call), and the Full
@@ -255,7 +272,25 @@ def extra_measurements(dev):
                     "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
                     "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "algorithmic_bytes": nbytes}
-    del h, w, out, lse
+    # the same prefill in model order: one phase-1 call per block group, one
+    # phase-2 call per row inside a block (state: fp32 block sums, partial sum,
+    # RMS-scale cache, the group's phase-1 results)
+    S = wl.S
+    n_blk = 1 + (n - 1) // S
+    st = {"blocks": torch.empty((n_blk, T, d), dtype=torch.float32, device=dev),
+          "partial": torch.empty((T, d), dtype=torch.float32, device=dev),
+          "rs": torch.empty((n_blk, T), dtype=torch.float32, device=dev),
+          "o": torch.empty((S, T, d), dtype=torch.float32, device=dev),
+          "lse1": torch.empty((S, T), dtype=torch.float32, device=dev)}
+    ms = _time(lambda: ar.block_model_order(h, w, S, out=out, lse=lse, state=st), stream, 3, 1)
+    nbytes = model_order_bytes_per_token(n, d, S) * T
+    res[wl.name + "_model_order"] = {
+        "what": "Block AttnRes S=8 in model order: attnres_block_phase1 per group + attnres_block_phase2 per row",
+        "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+        "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
+        "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes": nbytes}
+    del h, w, out, lse, st
     torch.cuda.empty_cache()
 
     wl = WORKLOADS["fwdbwd_L24_d1024"]

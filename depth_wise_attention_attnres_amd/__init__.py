@@ -27,8 +27,9 @@ STATUS = {0: "ATTNRES_OK", 1: "ATTNRES_ERR_INVALID_ARG", 2: "ATTNRES_ERR_UNSUPPO
           3: "ATTNRES_ERR_ALIGN", 4: "ATTNRES_ERR_WORKSPACE", 5: "ATTNRES_ERR_HIP"}
 
 # every symbol include/attnres.h declares
-EXPORTS = ["attnres_full_fwd", "attnres_block_fwd", "attnres_bwd", "attnres_bwd_workspace_bytes",
-           "attnres_block_index_table", "attnres_status_string", "attnres_last_error"]
+EXPORTS = ["attnres_full_fwd", "attnres_block_fwd", "attnres_block_phase1", "attnres_block_phase2",
+           "attnres_bwd", "attnres_bwd_workspace_bytes", "attnres_block_index_table",
+           "attnres_status_string", "attnres_last_error"]
 
 if not os.path.exists(LIBRARY):
     raise ImportError(f"libattnres.so is not built ({LIBRARY}); run __graft_entry__.build()")
@@ -43,6 +44,12 @@ _lib.attnres_full_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, 
 _lib.attnres_block_fwd.restype = _int
 _lib.attnres_block_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp,
                                    _int, _vp, _vp]
+_lib.attnres_block_phase1.restype = _int
+_lib.attnres_block_phase1.argtypes = [_vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _i64, _f32, _vp,
+                                      _vp, _vp, _vp, _int, _vp, _vp]
+_lib.attnres_block_phase2.restype = _int
+_lib.attnres_block_phase2.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp, _vp, _vp, _f32, _vp,
+                                      _int, _vp, _vp]
 _lib.attnres_bwd.restype = _int
 _lib.attnres_bwd.argtypes = [_int, _i64, _vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32,
                              _vp, _int, _vp, _int, _vp, _vp, _sz, _vp]
@@ -159,6 +166,110 @@ def block_fwd(hist, w, S: int, *, q_begin: int = 0, n_q: int | None = None, eps:
         _require(lse, "lse", dtype=torch.float32, shape=(n_q, T))
     _check(_lib.attnres_block_fwd(_ptr(hist), _dtype_code(hist), n_hist, T, d, S, _ptr(w),
                                   q_begin, n_q, eps, _ptr(out), odt, _ptr(lse), _stream(hist)))
+    return out, lse
+
+
+def block_phase1(blocks, n_src: int, v, w, *, partial=None, eps: float = 1e-6, rs=None, o=None,
+                 lse1=None, out0=None, lse0=None):
+    """Model-order Block AttnRes, phase 1: close block n_src-1 into blocks[n_src-1]
+    (= partial + v, fp32) and score the group's reads (queries w [n_reads, d])
+    against blocks[0 .. n_src-1].  Returns (o, lse1); out0 / lse0 receive the
+    group's first read if given."""
+    import torch
+    _require(blocks, "blocks", dtype=torch.float32)
+    _, T, d = blocks.shape
+    _require(v, "v", shape=(T, d))
+    n_reads = w.shape[0]
+    _require(w, "w", dtype=torch.float32, shape=(n_reads, d))
+    if partial is not None:
+        _require(partial, "partial", dtype=torch.float32, shape=(T, d))
+    if rs is not None:
+        _require(rs, "rs", dtype=torch.float32)
+    if o is None:
+        o = torch.empty((n_reads, T, d), dtype=torch.float32, device=v.device)
+    _require(o, "o", dtype=torch.float32, shape=(n_reads, T, d))
+    if lse1 is None:
+        lse1 = torch.empty((n_reads, T), dtype=torch.float32, device=v.device)
+    _require(lse1, "lse1", dtype=torch.float32, shape=(n_reads, T))
+    odt = F32
+    if out0 is not None:
+        _require(out0, "out0", shape=(T, d))
+        odt = _dtype_code(out0)
+    if lse0 is not None:
+        _require(lse0, "lse0", dtype=torch.float32, shape=(T,))
+    _check(_lib.attnres_block_phase1(_ptr(blocks), n_src, T, d, _ptr(v), _dtype_code(v),
+                                     _ptr(partial), _ptr(w), n_reads, eps, _ptr(rs), _ptr(o),
+                                     _ptr(lse1), _ptr(out0), odt, _ptr(lse0), _stream(v)))
+    return o, lse1
+
+
+def block_phase2(v, partial, first_in_block: bool, w, o, lse1, *, eps: float = 1e-6, out=None,
+                 out_dtype=None, lse=None):
+    """Model-order Block AttnRes, phase 2: partial += v (in place; = v when
+    first_in_block), then merge the partial sum into the read's phase-1 result.
+    Returns (out, lse)."""
+    import torch
+    _require(v, "v")
+    T, d = v.shape
+    _require(partial, "partial", dtype=torch.float32, shape=(T, d))
+    _require(w, "w", dtype=torch.float32, shape=(d,))
+    _require(o, "o", dtype=torch.float32, shape=(T, d))
+    _require(lse1, "lse1", dtype=torch.float32, shape=(T,))
+    odt = _dtype_code(v) if out_dtype is None else (F32 if out_dtype == torch.float32 else BF16)
+    if out is None:
+        out = torch.empty((T, d), dtype=_torch_dtype(odt), device=v.device)
+    else:
+        _require(out, "out", shape=(T, d))
+        odt = _dtype_code(out)
+    if lse is not None:
+        _require(lse, "lse", dtype=torch.float32, shape=(T,))
+    _check(_lib.attnres_block_phase2(_ptr(v), _dtype_code(v), T, d, _ptr(partial),
+                                     1 if first_in_block else 0, _ptr(w), _ptr(o), _ptr(lse1), eps,
+                                     _ptr(out), odt, _ptr(lse), _stream(v)))
+    return out, lse
+
+
+def block_model_order(hist, w, S: int, *, eps: float = 1e-6, out=None, lse=None, state=None):
+    """All reads of a Block AttnRes history in model order through the two
+    phase entry points (one phase-1 call per block group, one phase-2 call per
+    row inside a block), as a model's forward runs them.  `state` may carry
+    preallocated buffers (dict with blocks, partial, rs, o, lse1).  Returns
+    (out [n_hist, T, d], lse [n_hist, T])."""
+    import torch
+    _require(hist, "hist")
+    n_hist, T, d = hist.shape
+    _require(w, "w", dtype=torch.float32, shape=(n_hist, d))
+    dev = hist.device
+    n_blk = 1 + (n_hist - 1) // S
+    st = state if state is not None else {}
+    blocks = st.get("blocks")
+    if blocks is None:
+        blocks = torch.empty((n_blk, T, d), dtype=torch.float32, device=dev)
+    partial = st.get("partial")
+    if partial is None:
+        partial = torch.empty((T, d), dtype=torch.float32, device=dev)
+    rs = st.get("rs")
+    if rs is None:
+        rs = torch.empty((n_blk, T), dtype=torch.float32, device=dev)
+    o = st.get("o")
+    if o is None:
+        o = torch.empty((S, T, d), dtype=torch.float32, device=dev)
+    lse1 = st.get("lse1")
+    if lse1 is None:
+        lse1 = torch.empty((S, T), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty_like(hist)
+    if lse is None:
+        lse = torch.empty((n_hist, T), dtype=torch.float32, device=dev)
+    for m in range(n_blk):
+        l0 = m * S
+        n_reads = min(S, n_hist - l0)
+        block_phase1(blocks[: m + 1], m + 1, hist[l0], w[l0: l0 + n_reads],
+                     partial=partial if (m > 0 and S > 1) else None, eps=eps, rs=rs[: m + 1],
+                     o=o[:n_reads], lse1=lse1[:n_reads], out0=out[l0], lse0=lse[l0])
+        for k in range(1, n_reads):
+            block_phase2(hist[l0 + k], partial, k == 1, w[l0 + k], o[k], lse1[k], eps=eps,
+                         out=out[l0 + k], lse=lse[l0 + k])
     return out, lse
 
 

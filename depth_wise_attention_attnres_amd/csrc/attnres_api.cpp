@@ -184,6 +184,97 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
     return hip_status(fn, attnres::launch_block_fwd(p, hist_dtype, out_dtype, stream));
 }
 
+int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d, const void* v,
+                         attnres_dtype v_dtype, const float* partial, const float* w,
+                         int64_t n_reads, float eps, float* rs, float* o, float* lse1, void* out0,
+                         attnres_dtype out_dtype, float* lse0, hipStream_t stream) {
+    const char* fn = "attnres_block_phase1";
+    if (n_src < 1 || n_src > attnres::kBlockMaxRegSources)
+        return fail(n_src < 1 ? ATTNRES_ERR_INVALID_ARG : ATTNRES_ERR_UNSUPPORTED,
+                    "%s: n_src = %" PRId64 " outside 1 .. %d", fn, n_src, attnres::kBlockMaxRegSources);
+    if (n_reads < 1 || n_reads > 64)
+        return fail(n_reads < 1 ? ATTNRES_ERR_INVALID_ARG : ATTNRES_ERR_UNSUPPORTED,
+                    "%s: n_reads = %" PRId64 " outside 1 .. 64", fn, n_reads);
+    // v is the new history row; one query row is checked like a read
+    int st = check_common(fn, v, v_dtype, n_src, T, d, w, 0, 1, eps);
+    if (st != ATTNRES_OK) return st;
+    if (!valid_dtype(out_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad out dtype %d", fn, (int)out_dtype);
+    if (T == 0) return ok();
+    if (blocks == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: blocks is NULL", fn);
+    if (o == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: o is NULL", fn);
+    if (lse1 == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: lse1 is NULL", fn);
+    if (!aligned(blocks, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: blocks is not 16-byte aligned", fn);
+    if (partial != nullptr && !aligned(partial, 16))
+        return fail(ATTNRES_ERR_ALIGN, "%s: partial is not 16-byte aligned", fn);
+    if (!aligned(o, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: o is not 16-byte aligned", fn);
+    if (!aligned(lse1, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse1 is not 4-byte aligned", fn);
+    if (rs != nullptr && !aligned(rs, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: rs is not 4-byte aligned", fn);
+    if (out0 != nullptr && !aligned(out0, 16))
+        return fail(ATTNRES_ERR_ALIGN, "%s: out0 is not 16-byte aligned", fn);
+    if (lse0 != nullptr && !aligned(lse0, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse0 is not 4-byte aligned", fn);
+
+    attnres::Phase1Params p;
+    p.blocks = blocks;
+    p.v = v;
+    p.partial = partial;
+    p.w = w;
+    p.rs = rs;
+    p.o = o;
+    p.lse1 = lse1;
+    p.out0 = out0;
+    p.lse0 = lse0;
+    p.T = T;
+    p.d = (int)d;
+    p.nc = (int)(d / 8);
+    p.n_src = (int)n_src;
+    p.n_reads = (int)n_reads;
+    p.v_dt = v_dtype;
+    p.out_dt = out_dtype;
+    p.eps = eps;
+    p.inv_d = 1.0f / (float)d;
+    return hip_status(fn, attnres::launch_block_phase1(p, stream));
+}
+
+int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_t d, float* partial,
+                         int first_in_block, const float* w, const float* o, const float* lse1,
+                         float eps, void* out, attnres_dtype out_dtype, float* lse,
+                         hipStream_t stream) {
+    const char* fn = "attnres_block_phase2";
+    int st = check_common(fn, v, v_dtype, 1, T, d, w, 0, 1, eps);
+    if (st != ATTNRES_OK) return st;
+    if (!valid_dtype(out_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad out dtype %d", fn, (int)out_dtype);
+    if (first_in_block != 0 && first_in_block != 1)
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: first_in_block must be 0 or 1", fn);
+    if (T == 0) return ok();
+    if (partial == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: partial is NULL", fn);
+    if (o == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: o is NULL", fn);
+    if (lse1 == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: lse1 is NULL", fn);
+    if (out == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (!aligned(partial, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: partial is not 16-byte aligned", fn);
+    if (!aligned(o, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: o is not 16-byte aligned", fn);
+    if (!aligned(lse1, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse1 is not 4-byte aligned", fn);
+    if (!aligned(out, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: out is not 16-byte aligned", fn);
+    if (lse != nullptr && !aligned(lse, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse is not 4-byte aligned", fn);
+
+    attnres::Phase2Params p;
+    p.v = v;
+    p.partial = partial;
+    p.w = w;
+    p.o = o;
+    p.lse1 = lse1;
+    p.out = out;
+    p.lse = lse;
+    p.T = T;
+    p.d = (int)d;
+    p.nc = (int)(d / 8);
+    p.first = first_in_block;
+    p.v_dt = v_dtype;
+    p.out_dt = out_dtype;
+    p.eps = eps;
+    p.inv_d = 1.0f / (float)d;
+    return hip_status(fn, attnres::launch_block_phase2(p, stream));
+}
+
 size_t attnres_bwd_workspace_bytes(attnres_variant variant, int64_t S, int64_t n_hist, int64_t T,
                                    int64_t d, int64_t q_begin, int64_t n_q) {
     if (variant != ATTNRES_FULL && variant != ATTNRES_BLOCK) return 0;

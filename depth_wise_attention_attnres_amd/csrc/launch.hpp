@@ -76,6 +76,38 @@ struct BwdParams {
     uint16_t* ws_wsplit;  // [3][n_q][d] bf16: w = hi + mid + lo (matrix-core scores)
 };
 hipError_t launch_bwd(const BwdParams& p, int n_chunks, hipStream_t stream);
+
+// Block AttnRes in model order (block_model.hip)
+struct Phase1Params {
+    float* blocks;          // [n_src][T][d] fp32; row n_src-1 written
+    const void* v;          // [T][d] history row closing the block
+    const float* partial;   // [T][d] fp32 or null
+    const float* w;         // [n_reads][d]
+    float* rs;              // [n_src][T] or null
+    float* o;               // [n_reads][T][d] fp32
+    float* lse1;            // [n_reads][T]
+    void* out0;             // [T][d] or null
+    float* lse0;            // [T] or null
+    int64_t T;
+    int d, nc, n_src, n_reads;
+    attnres_dtype v_dt, out_dt;
+    float eps, inv_d;
+};
+struct Phase2Params {
+    const void* v;          // [T][d]
+    float* partial;         // [T][d] fp32, in place
+    const float* w;         // [d]
+    const float* o;         // [T][d] fp32
+    const float* lse1;      // [T]
+    void* out;              // [T][d]
+    float* lse;             // [T] or null
+    int64_t T;
+    int d, nc, first;
+    attnres_dtype v_dt, out_dt;
+    float eps, inv_d;
+};
+hipError_t launch_block_phase1(const Phase1Params& p, hipStream_t stream);
+hipError_t launch_block_phase2(const Phase2Params& p, hipStream_t stream);
 // zero `bytes` (a multiple of 4) of device memory with a kernel
 hipError_t launch_fill_zero(void* dst, int64_t bytes, hipStream_t stream);
 

@@ -124,6 +124,56 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
                       attnres_dtype out_dtype, float* lse, hipStream_t stream);
 
 /*
+ * Block AttnRes in model order, phase 1 (DataCamp, "two-phase computation":
+ * the reads of one block group share the frozen sources and are batched;
+ * block reading of "DepthBench reading notes" sec. 2.5).  Called when history
+ * row m*S arrives (m = n_src - 1), i.e. when block m is complete (m = 0: the
+ * embedding v_0), before sublayer m*S + 1 runs:
+ *   1. forms the new source  blocks[m] = partial + v  in fp32 (partial may be
+ *      NULL: the new source is v alone -- v_0, or any block when S = 1);
+ *   2. for the n_reads reads l = m*S .. m*S + n_reads - 1 of the group
+ *      (n_reads <= S; fewer at the end of the history), scores the frozen
+ *      sources blocks[0 .. m] with the read's query w[k] and writes
+ *      o[k] = sum_c alpha_c blocks[c] (alpha the softmax over the frozen
+ *      sources only, fp32) and lse1[k] = log sum_c exp(s_c);
+ *   3. read m*S sees no partial sum, so its output h = o[0] is also written to
+ *      out0 (out_dtype, rounded once; may be NULL) and its lse to lse0 (may
+ *      be NULL).
+ *   blocks  [n_src][T][d] fp32, caller-owned state across calls: rows
+ *           0 .. n_src-2 must hold the earlier sources; row n_src-1 is written.
+ *   v       [T][d] history row m*S (v_dtype); partial [T][d] fp32 or NULL.
+ *   w       [n_reads][d] fp32; o [n_reads][T][d] fp32; lse1 [n_reads][T] fp32.
+ *   rs      [n_src][T] fp32 RMS scales r(b_c), or NULL (then all are computed
+ *           here): rows 0 .. n_src-2 must hold the values of earlier calls;
+ *           row n_src-1 is written.
+ * Requirements as attnres_block_fwd; 1 <= n_src <= 13, 1 <= n_reads <= 64.
+ */
+int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d,
+                         const void* v, attnres_dtype v_dtype, const float* partial,
+                         const float* w, int64_t n_reads, float eps, float* rs,
+                         float* o, float* lse1, void* out0, attnres_dtype out_dtype,
+                         float* lse0, hipStream_t stream);
+
+/*
+ * Block AttnRes in model order, phase 2 (DataCamp, "two-phase computation":
+ * the partial sum of the current block is merged online): for read l with
+ * l mod S != 0, after sublayer l has produced history row v:
+ *   partial = (first_in_block ? 0 : partial) + v        (fp32, in place)
+ *   s_p = r(partial) (w . partial),  M = max(lse1, s_p)
+ *   h = (e^(lse1 - M) o + e^(s_p - M) partial) / (e^(lse1 - M) + e^(s_p - M))
+ *   lse = M + log(e^(lse1 - M) + e^(s_p - M))
+ * with o, lse1 the read's phase-1 results.  first_in_block is 1 for the first
+ * row after a block boundary (l mod S == 1).
+ *   v [T][d] (v_dtype); partial [T][d] fp32 in/out; w [d] fp32;
+ *   o [T][d] fp32; lse1 [T] fp32; out [T][d] out_dtype; lse [T] fp32 or NULL.
+ * Requirements as attnres_block_fwd.
+ */
+int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_t d,
+                         float* partial, int first_in_block, const float* w,
+                         const float* o, const float* lse1, float eps, void* out,
+                         attnres_dtype out_dtype, float* lse, hipStream_t stream);
+
+/*
  * Backward of attnres_full_fwd (variant ATTNRES_FULL) or attnres_block_fwd
  * (ATTNRES_BLOCK, block size S) for the reads q_begin .. q_begin + n_q - 1.
  * The pages state no gradient; this is the derivative of the forward

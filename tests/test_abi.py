@@ -181,3 +181,41 @@ def test_bwd_workspace_size(ar):
     assert lib.attnres_bwd_workspace_bytes(1, 1, 49, 16384, 1024, 0, 49) == full
     assert lib.attnres_bwd_workspace_bytes(0, 1, 49, 16384, 1024, 10, 49) == 0  # reads past the history
     assert lib.attnres_bwd_workspace_bytes(2, 1, 49, 16384, 1024, 0, 49) == 0
+
+
+def test_block_phase_validation(ar):
+    lib = ar.raw()
+    # blocks, n_src, T, d, v, v_dt, partial, w, n_reads, eps, rs, o, lse1, out0, out_dt, lse0, stream
+    def ph1(blocks=P, n_src=3, T=16, d=64, v=P2, vdt=BF16, partial=None, w=P3, n_reads=4, eps=1e-6,
+            rs=None, o=P, lse1=P2, out0=None, odt=BF16, lse0=None):
+        return lib.attnres_block_phase1(blocks, n_src, T, d, v, vdt, partial, w, n_reads, eps, rs, o,
+                                        lse1, out0, odt, lse0, None)
+    assert ph1(n_src=0) == INVALID
+    assert ph1(n_src=14) == UNSUPPORTED
+    assert ph1(n_reads=0) == INVALID
+    assert ph1(n_reads=65) == UNSUPPORTED
+    assert ph1(d=12) == ALIGN
+    assert ph1(blocks=None) == INVALID
+    assert ph1(o=None) == INVALID
+    assert ph1(lse1=None) == INVALID
+    assert ph1(v=None) == INVALID
+    assert ph1(w=None) == INVALID
+    assert ph1(partial=P + 8) == ALIGN
+    assert ph1(out0=P + 4) == ALIGN
+    assert ph1(rs=P + 2) == ALIGN
+    assert ph1(odt=9) == INVALID
+    assert ph1(T=0) == OK
+
+    def ph2(v=P, vdt=BF16, T=16, d=64, partial=P2, first=1, w=P3, o=P, lse1=P2, eps=1e-6, out=P3,
+            odt=BF16, lse=None):
+        return lib.attnres_block_phase2(v, vdt, T, d, partial, first, w, o, lse1, eps, out, odt, lse,
+                                        None)
+    assert ph2(first=2) == INVALID
+    assert ph2(partial=None) == INVALID
+    assert ph2(o=None) == INVALID
+    assert ph2(lse1=None) == INVALID
+    assert ph2(out=None) == INVALID
+    assert ph2(out=P3 + 2) == ALIGN
+    assert ph2(d=4) == ALIGN
+    assert ph2(eps=float("nan")) == INVALID
+    assert ph2(T=0) == OK
