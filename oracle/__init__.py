@@ -67,6 +67,8 @@ def _load():
     lib.attnres_oracle_block_fwd_twophase.restype = ip
     lib.attnres_oracle_block_fwd_twophase.argtypes = [i64, vp, i64, i64, i64, vp, i64,
                                                       i64, dbl, vp, vp]
+    lib.attnres_oracle_prenorm.restype = ip
+    lib.attnres_oracle_prenorm.argtypes = [vp, i64, i64, i64, vp, dbl, vp]
     lib.attnres_oracle_bwd.restype = ip
     lib.attnres_oracle_bwd.argtypes = [ip, i64, vp, i64, i64, i64, vp, i64, i64, dbl,
                                        vp, vp, vp]
@@ -132,6 +134,20 @@ def full_fwd(hist, w, **kw):
 
 def block_fwd(hist, w, S: int, **kw):
     return fwd(BLOCK, hist, w, S=S, **kw)
+
+
+def prenorm(z, gain=None, eps: float = 1e-6) -> np.ndarray:
+    """Pre-norm of read mixtures z [n_q, T, d]: gain[l] * z * r(z) with the
+    keys' RMSNorm (gain [n_q, d] or None for unit gain), fp64."""
+    z = _f64(z)
+    n_q, T, d = z.shape
+    g = None if gain is None else _f64(gain)
+    if g is not None and g.shape != (n_q, d):
+        raise ValueError("gain must be [n_q, d]")
+    y = np.zeros_like(z)
+    if _load().attnres_oracle_prenorm(_ptr(z), n_q, T, d, _ptr(g), float(eps), _ptr(y)) != 0:
+        raise ValueError("oracle prenorm rejected its arguments")
+    return y
 
 
 def block_fwd_twophase(hist, w, S: int, *, q_begin: int = 0, n_q: int | None = None,

@@ -147,6 +147,25 @@ static double dot(const double* a, const double* b, int64_t d) {
     return s;
 }
 
+/* Pre-norm of each read's mixture: the sublayer's branch input
+ * RMSNorm_pre,l(z_l) ([DB] sec. 2.3, the f_l equation), with the same RMSNorm
+ * as the keys (r = 1/sqrt(mean z^2 + eps)) and a per-read gain vector:
+ *   y[l][t] = gain[l] * z[l][t] * r(z[l][t])      (gain NULL: unit gain)
+ *   z, y [n_q][T][d];  gain [n_q][d] or NULL.  Returns 0, or -1 on bad sizes. */
+int attnres_oracle_prenorm(const double* z, int64_t n_q, int64_t T, int64_t d,
+                           const double* gain, double eps, double* y) {
+    if (n_q < 0 || T < 0 || d < 1 || !(eps >= 0.0)) return -1;
+    for (int64_t j = 0; j < n_q; ++j) {
+        for (int64_t t = 0; t < T; ++t) {
+            const double* zr = z + (j * T + t) * d;
+            double* yr = y + (j * T + t) * d;
+            const double r = rms_inv(zr, d, eps);
+            for (int64_t k = 0; k < d; ++k) yr[k] = (gain ? gain[j * d + k] : 1.0) * zr[k] * r;
+        }
+    }
+    return 0;
+}
+
 /* Single-pass forward for Full (variant 0) or Block (variant 1).
  *   hist  [n_hist][T][d]   w [n_q][d] (row j is read q_begin + j)
  *   out   [n_q][T][d]      lse [n_q][T] or NULL

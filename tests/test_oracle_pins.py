@@ -382,3 +382,42 @@ def test_round_to_bf16_matches_torch(oracle):
     assert np.array_equal(mine, ref)
     assert (oracle.ulp_bf16(np.array([1.0, 1.5, 8.0, 15.9]))
             == np.array([2 ** -7, 2 ** -7, 2 ** -4, 2 ** -4])).all()
+
+
+# ---------------------------------------------------------------------------
+# pre-norm of the mixture (the branch input RMSNorm_pre,l(z_l))
+
+def test_prenorm_worked_example(oracle):
+    spec = json.load(open(os.path.join(GOLDEN, "worked_examples.json")))
+    for ex in spec["prenorm_examples"]:
+        y = oracle.prenorm(np.array(ex["z"]), np.array(ex["gain"]), eps=ex["eps"])
+        np.testing.assert_allclose(y, np.array(ex["y"]), rtol=1e-15, atol=0, err_msg=ex["name"])
+
+
+def test_prenorm_unit_rms_and_scale_free(oracle):
+    rng = np.random.default_rng(21)
+    z = rng.standard_normal((3, 5, 48)) * rng.uniform(0.1, 9.0, (3, 5, 1))
+    y = oracle.prenorm(z, eps=0.0)
+    np.testing.assert_allclose((y * y).mean(-1), 1.0, rtol=1e-13)  # unit gain: RMS 1
+    np.testing.assert_allclose(oracle.prenorm(7.5 * z, eps=0.0), y, rtol=1e-13)  # scale-free
+    np.testing.assert_allclose(oracle.prenorm(-z, eps=0.0), -y, rtol=0, atol=0)  # odd
+    # the direction is kept: y is a positive multiple of z
+    cos = (y * z).sum(-1) / np.sqrt((y * y).sum(-1) * (z * z).sum(-1))
+    np.testing.assert_allclose(cos, 1.0, rtol=1e-13)
+
+
+def test_prenorm_gain_is_elementwise(oracle):
+    rng = np.random.default_rng(22)
+    z = rng.standard_normal((2, 4, 16))
+    g = rng.standard_normal((2, 16))
+    y1 = oracle.prenorm(z, eps=1e-6)
+    yg = oracle.prenorm(z, g, eps=1e-6)
+    np.testing.assert_allclose(yg, g[:, None, :] * y1, rtol=1e-14, atol=1e-15)
+
+
+def test_prenorm_eps_inside_the_root(oracle):
+    # a constant vector c: y = c / sqrt(c^2 + eps); the zero vector stays zero
+    c, eps = 0.01, 1e-4
+    y = oracle.prenorm(np.full((1, 1, 8), c), eps=eps)
+    np.testing.assert_allclose(y, c / np.sqrt(c * c + eps), rtol=1e-14)
+    assert np.array_equal(oracle.prenorm(np.zeros((1, 2, 8)), eps=eps), np.zeros((1, 2, 8)))
