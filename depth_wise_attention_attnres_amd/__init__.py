@@ -40,16 +40,16 @@ _i64, _f32, _int, _vp, _sz = (ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctyp
                               ctypes.c_size_t)
 _lib.attnres_full_fwd.restype = _int
 _lib.attnres_full_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp, _i64,
-                                  _vp, _int, _vp, _vp]
+                                  _vp, _int, _vp, _vp, _vp, _vp]
 _lib.attnres_block_fwd.restype = _int
 _lib.attnres_block_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp,
                                    _int, _vp, _vp]
 _lib.attnres_block_phase1.restype = _int
 _lib.attnres_block_phase1.argtypes = [_vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _i64, _f32, _vp,
-                                      _vp, _vp, _vp, _int, _vp, _vp]
+                                      _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp]
 _lib.attnres_block_phase2.restype = _int
 _lib.attnres_block_phase2.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp, _vp, _vp, _f32, _vp,
-                                      _int, _vp, _vp]
+                                      _int, _vp, _vp, _vp, _vp]
 _lib.attnres_bwd.restype = _int
 _lib.attnres_bwd.argtypes = [_int, _i64, _vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32,
                              _vp, _int, _vp, _int, _vp, _vp, _sz, _vp]
@@ -121,8 +121,10 @@ def _require(t, name, *, dtype=None, shape=None):
 
 def full_fwd(hist, w, *, q_begin: int = 0, n_q: int | None = None, eps: float = 1e-6,
              rinv=None, rinv_valid_rows: int = 0, out=None, out_dtype=None, lse=None,
-             want_lse: bool = True):
-    """Full AttnRes reads q_begin .. q_begin+n_q-1.  Returns (out, lse)."""
+             want_lse: bool = True, normed=None, norm_gain=None):
+    """Full AttnRes reads q_begin .. q_begin+n_q-1.  Returns (out, lse).
+    normed (same shape and dtype as out) receives the fused pre-norm
+    norm_gain * h * r(h) when given (norm_gain [n_q, d] fp32 or None)."""
     import torch
     _require(hist, "hist")
     n_hist, T, d = hist.shape
@@ -140,9 +142,13 @@ def full_fwd(hist, w, *, q_begin: int = 0, n_q: int | None = None, eps: float = 
         _require(lse, "lse", dtype=torch.float32, shape=(n_q, T))
     if rinv is not None:
         _require(rinv, "rinv", dtype=torch.float32, shape=(n_hist, T))
+    if normed is not None:
+        _require(normed, "normed", dtype=out.dtype, shape=(n_q, T, d))
+        if norm_gain is not None:
+            _require(norm_gain, "norm_gain", dtype=torch.float32, shape=(n_q, d))
     _check(_lib.attnres_full_fwd(_ptr(hist), _dtype_code(hist), n_hist, T, d, _ptr(w), q_begin,
                                  n_q, eps, _ptr(rinv), rinv_valid_rows, _ptr(out), odt, _ptr(lse),
-                                 _stream(hist)))
+                                 _ptr(norm_gain), _ptr(normed), _stream(hist)))
     return out, lse
 
 
@@ -170,7 +176,7 @@ def block_fwd(hist, w, S: int, *, q_begin: int = 0, n_q: int | None = None, eps:
 
 
 def block_phase1(blocks, n_src: int, v, w, *, partial=None, eps: float = 1e-6, rs=None, o=None,
-                 lse1=None, out0=None, lse0=None):
+                 lse1=None, out0=None, lse0=None, normed0=None, norm_gain0=None):
     """Model-order Block AttnRes, phase 1: close block n_src-1 into blocks[n_src-1]
     (= partial + v, fp32) and score the group's reads (queries w [n_reads, d])
     against blocks[0 .. n_src-1].  Returns (o, lse1); out0 / lse0 receive the
@@ -197,14 +203,22 @@ def block_phase1(blocks, n_src: int, v, w, *, partial=None, eps: float = 1e-6, r
         odt = _dtype_code(out0)
     if lse0 is not None:
         _require(lse0, "lse0", dtype=torch.float32, shape=(T,))
+    if normed0 is not None:
+        _require(normed0, "normed0", shape=(T, d))
+        if out0 is not None and normed0.dtype != out0.dtype:
+            raise TypeError("normed0 must have the dtype of out0")
+        odt = _dtype_code(normed0)
+        if norm_gain0 is not None:
+            _require(norm_gain0, "norm_gain0", dtype=torch.float32, shape=(d,))
     _check(_lib.attnres_block_phase1(_ptr(blocks), n_src, T, d, _ptr(v), _dtype_code(v),
                                      _ptr(partial), _ptr(w), n_reads, eps, _ptr(rs), _ptr(o),
-                                     _ptr(lse1), _ptr(out0), odt, _ptr(lse0), _stream(v)))
+                                     _ptr(lse1), _ptr(out0), odt, _ptr(lse0), _ptr(norm_gain0),
+                                     _ptr(normed0), _stream(v)))
     return o, lse1
 
 
 def block_phase2(v, partial, first_in_block: bool, w, o, lse1, *, eps: float = 1e-6, out=None,
-                 out_dtype=None, lse=None):
+                 out_dtype=None, lse=None, normed=None, norm_gain=None):
     """Model-order Block AttnRes, phase 2: partial += v (in place; = v when
     first_in_block), then merge the partial sum into the read's phase-1 result.
     Returns (out, lse)."""
@@ -223,18 +237,25 @@ def block_phase2(v, partial, first_in_block: bool, w, o, lse1, *, eps: float = 1
         odt = _dtype_code(out)
     if lse is not None:
         _require(lse, "lse", dtype=torch.float32, shape=(T,))
+    if normed is not None:
+        _require(normed, "normed", dtype=out.dtype, shape=(T, d))
+        if norm_gain is not None:
+            _require(norm_gain, "norm_gain", dtype=torch.float32, shape=(d,))
     _check(_lib.attnres_block_phase2(_ptr(v), _dtype_code(v), T, d, _ptr(partial),
                                      1 if first_in_block else 0, _ptr(w), _ptr(o), _ptr(lse1), eps,
-                                     _ptr(out), odt, _ptr(lse), _stream(v)))
+                                     _ptr(out), odt, _ptr(lse), _ptr(norm_gain), _ptr(normed),
+                                     _stream(v)))
     return out, lse
 
 
-def block_model_order(hist, w, S: int, *, eps: float = 1e-6, out=None, lse=None, state=None):
+def block_model_order(hist, w, S: int, *, eps: float = 1e-6, out=None, lse=None, state=None,
+                      normed=None, norm_gain=None):
     """All reads of a Block AttnRes history in model order through the two
     phase entry points (one phase-1 call per block group, one phase-2 call per
     row inside a block), as a model's forward runs them.  `state` may carry
     preallocated buffers (dict with blocks, partial, rs, o, lse1).  Returns
-    (out [n_hist, T, d], lse [n_hist, T])."""
+    (out [n_hist, T, d], lse [n_hist, T]).  normed (like out) receives the
+    fused pre-norm of every read when given (norm_gain [n_hist, d] or None)."""
     import torch
     _require(hist, "hist")
     n_hist, T, d = hist.shape
@@ -264,12 +285,16 @@ def block_model_order(hist, w, S: int, *, eps: float = 1e-6, out=None, lse=None,
     for m in range(n_blk):
         l0 = m * S
         n_reads = min(S, n_hist - l0)
+        ng = (lambda l: None) if norm_gain is None else (lambda l: norm_gain[l])
+        nd = (lambda l: None) if normed is None else (lambda l: normed[l])
         block_phase1(blocks[: m + 1], m + 1, hist[l0], w[l0: l0 + n_reads],
                      partial=partial if (m > 0 and S > 1) else None, eps=eps, rs=rs[: m + 1],
-                     o=o[:n_reads], lse1=lse1[:n_reads], out0=out[l0], lse0=lse[l0])
+                     o=o[:n_reads], lse1=lse1[:n_reads], out0=out[l0], lse0=lse[l0],
+                     normed0=nd(l0), norm_gain0=ng(l0))
         for k in range(1, n_reads):
             block_phase2(hist[l0 + k], partial, k == 1, w[l0 + k], o[k], lse1[k], eps=eps,
-                         out=out[l0 + k], lse=lse[l0 + k])
+                         out=out[l0 + k], lse=lse[l0 + k], normed=nd(l0 + k),
+                         norm_gain=ng(l0 + k))
     return out, lse
 
 

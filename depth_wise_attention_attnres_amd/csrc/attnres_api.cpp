@@ -112,7 +112,7 @@ int attnres_block_index_table(int64_t n_hist, int64_t S, int64_t q_begin, int64_
 int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
                      int64_t d, const float* w, int64_t q_begin, int64_t n_q, float eps,
                      float* rinv, int64_t rinv_valid_rows, void* out, attnres_dtype out_dtype,
-                     float* lse, hipStream_t stream) {
+                     float* lse, const float* norm_gain, void* normed, hipStream_t stream) {
     const char* fn = "attnres_full_fwd";
     int st = check_common(fn, hist, hist_dtype, n_hist, T, d, w, q_begin, n_q, eps);
     if (st != ATTNRES_OK) return st;
@@ -127,6 +127,10 @@ int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
     if (!aligned(out, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: out is not 16-byte aligned", fn);
     if (lse != nullptr && !aligned(lse, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse is not 4-byte aligned", fn);
     if (rinv != nullptr && !aligned(rinv, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: rinv is not 4-byte aligned", fn);
+    if (normed != nullptr && !aligned(normed, 16))
+        return fail(ATTNRES_ERR_ALIGN, "%s: normed is not 16-byte aligned", fn);
+    if (normed != nullptr && norm_gain != nullptr && !aligned(norm_gain, 16))
+        return fail(ATTNRES_ERR_ALIGN, "%s: norm_gain is not 16-byte aligned", fn);
 
     attnres::FullFwdParams p;
     p.hist = hist;
@@ -134,6 +138,8 @@ int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
     p.rinv = rinv;
     p.out = out;
     p.lse = lse;
+    p.norm_gain = normed != nullptr ? norm_gain : nullptr;
+    p.normed = normed;
     p.T = T;
     p.d = (int)d;
     p.nc = (int)(d / 8);
@@ -169,6 +175,8 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
     p.rinv = nullptr;
     p.out = out;
     p.lse = lse;
+    p.norm_gain = nullptr;
+    p.normed = nullptr;
     p.T = T;
     p.d = (int)d;
     p.nc = (int)(d / 8);
@@ -187,7 +195,8 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
 int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d, const void* v,
                          attnres_dtype v_dtype, const float* partial, const float* w,
                          int64_t n_reads, float eps, float* rs, float* o, float* lse1, void* out0,
-                         attnres_dtype out_dtype, float* lse0, hipStream_t stream) {
+                         attnres_dtype out_dtype, float* lse0, const float* norm_gain0,
+                         void* normed0, hipStream_t stream) {
     const char* fn = "attnres_block_phase1";
     if (n_src < 1 || n_src > attnres::kBlockMaxRegSources)
         return fail(n_src < 1 ? ATTNRES_ERR_INVALID_ARG : ATTNRES_ERR_UNSUPPORTED,
@@ -212,8 +221,14 @@ int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d, con
     if (out0 != nullptr && !aligned(out0, 16))
         return fail(ATTNRES_ERR_ALIGN, "%s: out0 is not 16-byte aligned", fn);
     if (lse0 != nullptr && !aligned(lse0, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse0 is not 4-byte aligned", fn);
+    if (normed0 != nullptr && !aligned(normed0, 16))
+        return fail(ATTNRES_ERR_ALIGN, "%s: normed0 is not 16-byte aligned", fn);
+    if (normed0 != nullptr && norm_gain0 != nullptr && !aligned(norm_gain0, 16))
+        return fail(ATTNRES_ERR_ALIGN, "%s: norm_gain0 is not 16-byte aligned", fn);
 
     attnres::Phase1Params p;
+    p.norm_gain0 = normed0 != nullptr ? norm_gain0 : nullptr;
+    p.normed0 = normed0;
     p.blocks = blocks;
     p.v = v;
     p.partial = partial;
@@ -238,7 +253,7 @@ int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d, con
 int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_t d, float* partial,
                          int first_in_block, const float* w, const float* o, const float* lse1,
                          float eps, void* out, attnres_dtype out_dtype, float* lse,
-                         hipStream_t stream) {
+                         const float* norm_gain, void* normed, hipStream_t stream) {
     const char* fn = "attnres_block_phase2";
     int st = check_common(fn, v, v_dtype, 1, T, d, w, 0, 1, eps);
     if (st != ATTNRES_OK) return st;
@@ -255,8 +270,14 @@ int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_
     if (!aligned(lse1, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse1 is not 4-byte aligned", fn);
     if (!aligned(out, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: out is not 16-byte aligned", fn);
     if (lse != nullptr && !aligned(lse, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse is not 4-byte aligned", fn);
+    if (normed != nullptr && !aligned(normed, 16))
+        return fail(ATTNRES_ERR_ALIGN, "%s: normed is not 16-byte aligned", fn);
+    if (normed != nullptr && norm_gain != nullptr && !aligned(norm_gain, 16))
+        return fail(ATTNRES_ERR_ALIGN, "%s: norm_gain is not 16-byte aligned", fn);
 
     attnres::Phase2Params p;
+    p.norm_gain = normed != nullptr ? norm_gain : nullptr;
+    p.normed = normed;
     p.v = v;
     p.partial = partial;
     p.w = w;

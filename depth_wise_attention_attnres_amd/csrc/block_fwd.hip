@@ -306,8 +306,6 @@ __device__ __forceinline__ void block_chunk_dispatch(int g, const BlockFwdParams
 template <typename TI, int NSRC, int CR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void block_fwd_twophase_kernel(BlockFwdParams p) {
-    constexpr int kStride = BlockLds<NSRC, CR>::kStride;
-    constexpr int kVals = BlockLds<NSRC, CR>::kVals;
     const int kRowSlots = blockDim.x / 16;
 
     extern __shared__ float lds[];
@@ -378,7 +376,6 @@ namespace {
 
 template <typename TI, int NSRC, int CR>
 hipError_t launch_twophase(const BlockFwdParams& p, int nw, hipStream_t stream) {
-    constexpr int kStride = BlockLds<NSRC, CR>::kStride;
     constexpr int kVals = BlockLds<NSRC, CR>::kVals;
     const size_t lds = sizeof(float) * 2 * kVals * 4 * nw;
     hipLaunchKernelGGL((block_fwd_twophase_kernel<TI, NSRC, CR>), dim3((unsigned)p.T),

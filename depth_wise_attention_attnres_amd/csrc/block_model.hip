@@ -67,7 +67,7 @@ void block_phase1_kernel(Phase1Params p) {
     const bool ok = tid < p.nc;
     const uint32_t chunk = (uint32_t)tid;
     const int m = p.n_src - 1;  // index of the new source
-    extern __shared__ float lds[];  // [2][kVals][row_slots]
+    extern __shared__ float lds[];  // [2][kVals][row_slots], then [row_slots] for the pre-norm
 
     // ---- sources: the frozen ones, then the new one formed here -----------
     float src[NSRC][8];
@@ -194,6 +194,30 @@ void block_phase1_kernel(Phase1Params p) {
                 if (k0 + k == 0 && p.out0 != nullptr)
                     store8(static_cast<char*>(p.out0) + t * p.d * (p.out_dt == ATTNRES_BF16 ? 2 : 4),
                            p.out_dt, p.d, chunk, ok, o);
+                if (k0 + k == 0 && p.normed0 != nullptr) {  // uniform: every thread takes it
+                    float* red = lds + 2 * kVals * row_slots;
+                    float ss = 0.f;
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) ss = fmaf(o[e2], o[e2], ss);
+                    ss = tg_sum<16>(ss);
+                    red[row_slot] = ss;
+                    __syncthreads();
+                    float tot = 0.f;
+                    for (int r = 0; r < row_slots; ++r) tot += red[r];
+                    const float rn = fast_rsqrt(fmaf(tot, p.inv_d, p.eps));
+                    float g[8];
+                    if (p.norm_gain0 != nullptr) {
+                        load8(p.norm_gain0, ATTNRES_F32, p.d, chunk, ok, g);
+                    } else {
+#pragma unroll
+                        for (int e2 = 0; e2 < 8; ++e2) g[e2] = 1.f;
+                    }
+                    float y[8];
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) y[e2] = g[e2] * (o[e2] * rn);
+                    store8(static_cast<char*>(p.normed0) + t * p.d * (p.out_dt == ATTNRES_BF16 ? 2 : 4),
+                           p.out_dt, p.d, chunk, ok, y);
+                }
             }
         }
     }
@@ -243,20 +267,43 @@ __global__ __launch_bounds__(256) void block_phase2_kernel(Phase2Params p) {
     const float A = fast_exp2(l1 - M), B = fast_exp2(sp - M);
     const float inv = 1.0f / (A + B);
     const float a = A * inv, b = B * inv;
+    float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const uint32_t ch = (uint32_t)(c * 64 + ln);
-        float h[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = fmaf(a, o[c][e], b * x[c][e]);
-        store8(out_row, p.out_dt, p.d, ch, (int)ch < p.nc, h);
+        for (int e = 0; e < 8; ++e) {
+            o[c][e] = fmaf(a, o[c][e], b * x[c][e]);  // o now holds h
+            ss = fmaf(o[c][e], o[c][e], ss);
+        }
+        store8(out_row, p.out_dt, p.d, ch, (int)ch < p.nc, o[c]);
     }
     if (p.lse != nullptr && ln == 0) p.lse[t] = (M + fast_log2(A + B)) * kLn2;
+    if (p.normed != nullptr) {  // fused pre-norm of the output (uniform branch)
+        ss = tg_sum<64>(ss);
+        const float rn = fast_rsqrt(fmaf(ss, p.inv_d, p.eps));
+        void* n_row = static_cast<char*>(p.normed) + t * p.d * ob;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const uint32_t ch = (uint32_t)(c * 64 + ln);
+            float g[8];
+            if (p.norm_gain != nullptr) {
+                load8(p.norm_gain, ATTNRES_F32, p.d, ch, (int)ch < p.nc, g);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) g[e] = 1.f;
+            }
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = g[e] * (o[c][e] * rn);
+            store8(n_row, p.out_dt, p.d, ch, (int)ch < p.nc, y);
+        }
+    }
 }
 
 hipError_t launch_block_phase1(const Phase1Params& p, hipStream_t stream) {
     const int nw = p.nc <= 64 ? 1 : p.nc <= 128 ? 2 : p.nc <= 256 ? 4 : 8;
-    auto lds = [&](int nsrc) { return sizeof(float) * 2 * (size_t)(4 * nsrc + nsrc) * 4 * nw; };
+    auto lds = [&](int nsrc) { return sizeof(float) * (2 * (size_t)(4 * nsrc + nsrc) + 1) * 4 * nw; };
     if (p.n_src <= 5)
         hipLaunchKernelGGL(block_phase1_kernel<5>, dim3((unsigned)p.T), dim3(64 * nw), lds(5), stream, p);
     else if (p.n_src <= 9)

@@ -195,10 +195,37 @@ __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdPara
         const rsrc_t orr = make_rsrc(out_blk + (int64_t)j * row_elems, blk_elems * sizeof(TO));
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            float o[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = acc[c][e] * inv_z;
-            store_chunk((TO*)nullptr, orr, out_off[c], o);
+            for (int e = 0; e < 8; ++e) acc[c][e] *= inv_z;
+            store_chunk((TO*)nullptr, orr, out_off[c], acc[c]);
+        }
+        if (p.normed != nullptr) {  // fused pre-norm of the output (uniform branch)
+            float ss = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(acc[c][e], acc[c][e], ss);
+            ss = tg_sum<LPT>(ss);
+            const float rn = fast_rsqrt(fmaf(ss, p.inv_d, p.eps));
+            const rsrc_t nrr = make_rsrc(static_cast<TO*>(p.normed) + tok0 * p.d + (int64_t)j * row_elems,
+                                         blk_elems * sizeof(TO));
+            const rsrc_t grr = make_rsrc(p.norm_gain + (int64_t)j * p.d, (uint64_t)p.d * 4);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                float g[8];
+                if (p.norm_gain != nullptr) {
+                    Chunk<float> gc;
+                    gc.load(grr, in_off[c] == kOOB ? kOOB : (uint32_t)((c * LPT + ln) * 32));
+                    gc.to_float(g);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) g[e] = 1.f;
+                }
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = g[e] * (acc[c][e] * rn);
+                store_chunk((TO*)nullptr, nrr, out_off[c], y);
+            }
         }
         if (p.lse != nullptr && ln == 0) p.lse[(int64_t)j * p.T + t] = (m2 + fast_log2(Z)) * kLn2;
     }

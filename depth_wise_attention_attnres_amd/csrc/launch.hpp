@@ -21,6 +21,8 @@ struct FwdParams {
     float* rinv;       // [n_hist][T] or null
     void* out;         // [n_q][T][d]
     float* lse;        // [n_q][T] or null
+    const float* norm_gain;  // [n_q][d] or null (unit gain)
+    void* normed;      // [n_q][T][d] pre-norm of the outputs, or null
     int64_t T;
     int d;             // width, multiple of 8
     int nc;            // d / 8 chunks
@@ -88,6 +90,8 @@ struct Phase1Params {
     float* lse1;            // [n_reads][T]
     void* out0;             // [T][d] or null
     float* lse0;            // [T] or null
+    const float* norm_gain0;  // [d] or null
+    void* normed0;          // [T][d] or null
     int64_t T;
     int d, nc, n_src, n_reads;
     attnres_dtype v_dt, out_dt;
@@ -101,6 +105,8 @@ struct Phase2Params {
     const float* lse1;      // [T]
     void* out;              // [T][d]
     float* lse;             // [T] or null
+    const float* norm_gain; // [d] or null
+    void* normed;           // [T][d] or null
     int64_t T;
     int d, nc, first;
     attnres_dtype v_dt, out_dt;

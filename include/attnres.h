@@ -103,12 +103,19 @@ typedef enum attnres_variant {
  *                      scales are computed on the fly (rinv_valid_rows must be 0).
  *   out, out_dtype     [n_q][T][d], F32 or BF16 (rounded once, to nearest even)
  *   lse                optional [n_q][T] fp32
+ *   norm_gain, normed  optional fused pre-norm of each output, the sublayer's
+ *                      branch input RMSNorm_pre,l(h_l) ("DepthBench reading
+ *                      notes" sec. 2.3, the f_l equation): normed [n_q][T][d]
+ *                      (out_dtype) = norm_gain[j] * h * r(h), with r as for
+ *                      the keys, taken from the fp32 h before its rounding;
+ *                      norm_gain [n_q][d] fp32, or NULL for unit gain.
+ *                      normed NULL: no pre-norm (norm_gain ignored).
  */
 int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
                      int64_t T, int64_t d, const float* w, int64_t q_begin,
                      int64_t n_q, float eps, float* rinv, int64_t rinv_valid_rows,
                      void* out, attnres_dtype out_dtype, float* lse,
-                     hipStream_t stream);
+                     const float* norm_gain, void* normed, hipStream_t stream);
 
 /*
  * Block AttnRes forward, two-phase ("DepthBench reading notes" sec. 2.5;
@@ -138,7 +145,8 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
  *      sources only, fp32) and lse1[k] = log sum_c exp(s_c);
  *   3. read m*S sees no partial sum, so its output h = o[0] is also written to
  *      out0 (out_dtype, rounded once; may be NULL) and its lse to lse0 (may
- *      be NULL).
+ *      be NULL); normed0 (out_dtype, may be NULL) receives its pre-norm
+ *      norm_gain0 * h * r(h) as in attnres_full_fwd (norm_gain0 [d] or NULL).
  *   blocks  [n_src][T][d] fp32, caller-owned state across calls: rows
  *           0 .. n_src-2 must hold the earlier sources; row n_src-1 is written.
  *   v       [T][d] history row m*S (v_dtype); partial [T][d] fp32 or NULL.
@@ -152,7 +160,8 @@ int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d,
                          const void* v, attnres_dtype v_dtype, const float* partial,
                          const float* w, int64_t n_reads, float eps, float* rs,
                          float* o, float* lse1, void* out0, attnres_dtype out_dtype,
-                         float* lse0, hipStream_t stream);
+                         float* lse0, const float* norm_gain0, void* normed0,
+                         hipStream_t stream);
 
 /*
  * Block AttnRes in model order, phase 2 (DataCamp, "two-phase computation":
@@ -165,13 +174,16 @@ int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d,
  * with o, lse1 the read's phase-1 results.  first_in_block is 1 for the first
  * row after a block boundary (l mod S == 1).
  *   v [T][d] (v_dtype); partial [T][d] fp32 in/out; w [d] fp32;
- *   o [T][d] fp32; lse1 [T] fp32; out [T][d] out_dtype; lse [T] fp32 or NULL.
+ *   o [T][d] fp32; lse1 [T] fp32; out [T][d] out_dtype; lse [T] fp32 or NULL;
+ *   normed [T][d] out_dtype or NULL: the pre-norm norm_gain * h * r(h) of
+ *   the output as in attnres_full_fwd (norm_gain [d] fp32 or NULL).
  * Requirements as attnres_block_fwd.
  */
 int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_t d,
                          float* partial, int first_in_block, const float* w,
                          const float* o, const float* lse1, float eps, void* out,
-                         attnres_dtype out_dtype, float* lse, hipStream_t stream);
+                         attnres_dtype out_dtype, float* lse, const float* norm_gain,
+                         void* normed, hipStream_t stream);
 
 /*
  * Backward of attnres_full_fwd (variant ATTNRES_FULL) or attnres_block_fwd

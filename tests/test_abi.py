@@ -45,9 +45,9 @@ def test_library_exports_every_declared_symbol(ar):
 
 
 def _full(ar, hist=P, hdt=BF16, n_hist=4, T=16, d=64, w=P2, q_begin=0, n_q=4, eps=1e-6,
-          rinv=None, rvalid=0, out=P3, odt=BF16, lse=None):
+          rinv=None, rvalid=0, out=P3, odt=BF16, lse=None, gain=None, normed=None):
     return ar.raw().attnres_full_fwd(hist, hdt, n_hist, T, d, w, q_begin, n_q, eps, rinv, rvalid,
-                                     out, odt, lse, None)
+                                     out, odt, lse, gain, normed, None)
 
 
 def test_full_fwd_validation(ar):
@@ -77,6 +77,8 @@ def test_full_fwd_validation(ar):
     assert _full(ar, eps=float("inf")) == INVALID
     assert _full(ar, eps=float("nan")) == INVALID
     assert _full(ar, T=1 << 40) == UNSUPPORTED
+    assert _full(ar, normed=P + 8) == ALIGN
+    assert _full(ar, normed=P, gain=P2 + 4) == ALIGN
     assert _full(ar, T=(1 << 27) + 1, d=8, n_hist=1, n_q=1) == UNSUPPORTED
     assert "2^27" in ar.last_error()
     assert _full(ar, T=1 << 27, d=8, n_hist=1, n_q=1, hist=None) == INVALID  # size accepted
@@ -187,9 +189,9 @@ def test_block_phase_validation(ar):
     lib = ar.raw()
     # blocks, n_src, T, d, v, v_dt, partial, w, n_reads, eps, rs, o, lse1, out0, out_dt, lse0, stream
     def ph1(blocks=P, n_src=3, T=16, d=64, v=P2, vdt=BF16, partial=None, w=P3, n_reads=4, eps=1e-6,
-            rs=None, o=P, lse1=P2, out0=None, odt=BF16, lse0=None):
+            rs=None, o=P, lse1=P2, out0=None, odt=BF16, lse0=None, g0=None, n0=None):
         return lib.attnres_block_phase1(blocks, n_src, T, d, v, vdt, partial, w, n_reads, eps, rs, o,
-                                        lse1, out0, odt, lse0, None)
+                                        lse1, out0, odt, lse0, g0, n0, None)
     assert ph1(n_src=0) == INVALID
     assert ph1(n_src=14) == UNSUPPORTED
     assert ph1(n_reads=0) == INVALID
@@ -205,11 +207,12 @@ def test_block_phase_validation(ar):
     assert ph1(rs=P + 2) == ALIGN
     assert ph1(odt=9) == INVALID
     assert ph1(T=0) == OK
+    assert ph1(n0=P + 4) == ALIGN
 
     def ph2(v=P, vdt=BF16, T=16, d=64, partial=P2, first=1, w=P3, o=P, lse1=P2, eps=1e-6, out=P3,
-            odt=BF16, lse=None):
+            odt=BF16, lse=None, g=None, nrm=None):
         return lib.attnres_block_phase2(v, vdt, T, d, partial, first, w, o, lse1, eps, out, odt, lse,
-                                        None)
+                                        g, nrm, None)
     assert ph2(first=2) == INVALID
     assert ph2(partial=None) == INVALID
     assert ph2(o=None) == INVALID
@@ -219,3 +222,5 @@ def test_block_phase_validation(ar):
     assert ph2(d=4) == ALIGN
     assert ph2(eps=float("nan")) == INVALID
     assert ph2(T=0) == OK
+    assert ph2(nrm=P + 4) == ALIGN
+    assert ph2(nrm=P, g=P2 + 8) == ALIGN

@@ -121,3 +121,17 @@ def test_model_order_workload_sampled(ar, oracle):
     print(f"model order {wl.name}: {stats}", flush=True)
     del h, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_hist,T,d,S", [(17, 40, 256, 4), (13, 21, 136, 3), (12, 9, 2048, 5)])
+def test_model_order_prenorm_matches_oracle(ar, oracle, dtype, n_hist, T, d, S):
+    h, w = _inputs(n_hist, T, d, seed=n_hist + S, dtype=dtype)
+    gain = torch.from_numpy(np.random.default_rng(d + S).uniform(0.5, 1.5, (n_hist, d))
+                            .astype(np.float32)).to(DEV)
+    normed = torch.empty_like(h)
+    out, _ = ar.block_model_order(h, w, S, normed=normed, norm_gain=gain)
+    torch.cuda.synchronize()
+    ref, _ = oracle.block_fwd(to_f64(h), to_f64(w), S)
+    check_out(to_f64(out), ref, dtype)
+    check_out(to_f64(normed), oracle.prenorm(ref, to_f64(gain)), dtype, what="normed")

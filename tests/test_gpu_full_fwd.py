@@ -149,3 +149,38 @@ def test_full_workload_model_order_sampled(ar, oracle, name):
     stats = check_out(to_f64(out.index_select(1, ti)), ref, wl.dtype)
     check_lse(to_f64(lse.index_select(1, ti)), ref_lse)
     print(f"{name}: {stats}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# fused pre-norm of the output (the sublayer's branch input RMSNorm_pre,l(h_l))
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_gain", [False, True])
+@pytest.mark.parametrize("n_hist,T,d", [(9, 37, 64), (7, 129, 520), (6, 33, 2048)])
+def test_full_prenorm_matches_oracle(ar, oracle, dtype, with_gain, n_hist, T, d):
+    h, w, hd, wd = _inputs(n_hist, T, d, seed=n_hist + d, dtype=dtype)
+    gain = torch.from_numpy(np.random.default_rng(d).uniform(0.5, 1.5, (n_hist, d)).astype(np.float32)).to(DEV) \
+        if with_gain else None
+    out = torch.empty(h.shape, dtype=h.dtype, device=DEV)
+    normed = torch.empty_like(out)
+    ar.full_fwd(h, w, out=out, normed=normed, norm_gain=gain)
+    torch.cuda.synchronize()
+    ref, _ = oracle.full_fwd(hd, wd)
+    ref_n = oracle.prenorm(ref, None if gain is None else to_f64(gain))
+    check_out(to_f64(out), ref, dtype)
+    check_out(to_f64(normed), ref_n, dtype, what="normed")
+
+
+def test_full_prenorm_in_model_order(ar, oracle):
+    # read by read with the RMS cache, as a model runs it; gain per read
+    n_hist, T, d = 17, 48, 896
+    h, w, hd, wd = _inputs(n_hist, T, d, seed=4, dtype="bf16")
+    gain = torch.from_numpy(np.random.default_rng(5).uniform(0.5, 1.5, (n_hist, d)).astype(np.float32)).to(DEV)
+    rinv = torch.empty((n_hist, T), device=DEV)
+    normed = torch.empty_like(h)
+    for l in range(n_hist):
+        ar.full_fwd(h, w[l:l + 1], q_begin=l, n_q=1, rinv=rinv, rinv_valid_rows=l,
+                    normed=normed[l:l + 1], norm_gain=gain[l:l + 1])
+    torch.cuda.synchronize()
+    ref, _ = oracle.full_fwd(hd, wd)
+    check_out(to_f64(normed), oracle.prenorm(ref, to_f64(gain)), "bf16", what="normed")
