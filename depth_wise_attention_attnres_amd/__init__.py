@@ -40,10 +40,10 @@ _i64, _f32, _int, _vp, _sz = (ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctyp
                               ctypes.c_size_t)
 _lib.attnres_full_fwd.restype = _int
 _lib.attnres_full_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp, _i64,
-                                  _vp, _int, _vp, _vp, _vp, _vp]
+                                  _vp, _int, _vp, _vp, _vp, _vp, _vp]
 _lib.attnres_block_fwd.restype = _int
 _lib.attnres_block_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp,
-                                   _int, _vp, _vp]
+                                   _int, _vp, _vp, _vp]
 _lib.attnres_block_phase1.restype = _int
 _lib.attnres_block_phase1.argtypes = [_vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _i64, _f32, _vp,
                                       _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp]
@@ -121,10 +121,11 @@ def _require(t, name, *, dtype=None, shape=None):
 
 def full_fwd(hist, w, *, q_begin: int = 0, n_q: int | None = None, eps: float = 1e-6,
              rinv=None, rinv_valid_rows: int = 0, out=None, out_dtype=None, lse=None,
-             want_lse: bool = True, normed=None, norm_gain=None):
+             want_lse: bool = True, normed=None, norm_gain=None, alpha=None):
     """Full AttnRes reads q_begin .. q_begin+n_q-1.  Returns (out, lse).
     normed (same shape and dtype as out) receives the fused pre-norm
-    norm_gain * h * r(h) when given (norm_gain [n_q, d] fp32 or None)."""
+    norm_gain * h * r(h) when given (norm_gain [n_q, d] fp32 or None); alpha
+    [n_q, n_hist, T] fp32 receives the softmax weights when given."""
     import torch
     _require(hist, "hist")
     n_hist, T, d = hist.shape
@@ -146,14 +147,16 @@ def full_fwd(hist, w, *, q_begin: int = 0, n_q: int | None = None, eps: float = 
         _require(normed, "normed", dtype=out.dtype, shape=(n_q, T, d))
         if norm_gain is not None:
             _require(norm_gain, "norm_gain", dtype=torch.float32, shape=(n_q, d))
+    if alpha is not None:
+        _require(alpha, "alpha", dtype=torch.float32, shape=(n_q, n_hist, T))
     _check(_lib.attnres_full_fwd(_ptr(hist), _dtype_code(hist), n_hist, T, d, _ptr(w), q_begin,
                                  n_q, eps, _ptr(rinv), rinv_valid_rows, _ptr(out), odt, _ptr(lse),
-                                 _ptr(norm_gain), _ptr(normed), _stream(hist)))
+                                 _ptr(norm_gain), _ptr(normed), _ptr(alpha), _stream(hist)))
     return out, lse
 
 
 def block_fwd(hist, w, S: int, *, q_begin: int = 0, n_q: int | None = None, eps: float = 1e-6,
-              out=None, out_dtype=None, lse=None, want_lse: bool = True):
+              out=None, out_dtype=None, lse=None, want_lse: bool = True, alpha=None):
     """Block AttnRes reads (block size S), two-phase.  Returns (out, lse)."""
     import torch
     _require(hist, "hist")
@@ -170,8 +173,11 @@ def block_fwd(hist, w, S: int, *, q_begin: int = 0, n_q: int | None = None, eps:
         lse = torch.empty((n_q, T), dtype=torch.float32, device=hist.device)
     if lse is not None:
         _require(lse, "lse", dtype=torch.float32, shape=(n_q, T))
+    if alpha is not None:
+        _require(alpha, "alpha", dtype=torch.float32, shape=(n_q, n_hist, T))
     _check(_lib.attnres_block_fwd(_ptr(hist), _dtype_code(hist), n_hist, T, d, S, _ptr(w),
-                                  q_begin, n_q, eps, _ptr(out), odt, _ptr(lse), _stream(hist)))
+                                  q_begin, n_q, eps, _ptr(out), odt, _ptr(lse), _ptr(alpha),
+                                  _stream(hist)))
     return out, lse
 
 

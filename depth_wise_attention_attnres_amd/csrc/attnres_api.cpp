@@ -112,7 +112,8 @@ int attnres_block_index_table(int64_t n_hist, int64_t S, int64_t q_begin, int64_
 int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
                      int64_t d, const float* w, int64_t q_begin, int64_t n_q, float eps,
                      float* rinv, int64_t rinv_valid_rows, void* out, attnres_dtype out_dtype,
-                     float* lse, const float* norm_gain, void* normed, hipStream_t stream) {
+                     float* lse, const float* norm_gain, void* normed, float* alpha,
+                     hipStream_t stream) {
     const char* fn = "attnres_full_fwd";
     int st = check_common(fn, hist, hist_dtype, n_hist, T, d, w, q_begin, n_q, eps);
     if (st != ATTNRES_OK) return st;
@@ -131,8 +132,10 @@ int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
         return fail(ATTNRES_ERR_ALIGN, "%s: normed is not 16-byte aligned", fn);
     if (normed != nullptr && norm_gain != nullptr && !aligned(norm_gain, 16))
         return fail(ATTNRES_ERR_ALIGN, "%s: norm_gain is not 16-byte aligned", fn);
+    if (alpha != nullptr && !aligned(alpha, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: alpha is not 4-byte aligned", fn);
 
     attnres::FullFwdParams p;
+    p.alpha = alpha;
     p.hist = hist;
     p.w = w;
     p.rinv = rinv;
@@ -157,7 +160,7 @@ int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
 
 int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
                       int64_t d, int64_t S, const float* w, int64_t q_begin, int64_t n_q,
-                      float eps, void* out, attnres_dtype out_dtype, float* lse,
+                      float eps, void* out, attnres_dtype out_dtype, float* lse, float* alpha,
                       hipStream_t stream) {
     const char* fn = "attnres_block_fwd";
     int st = check_common(fn, hist, hist_dtype, n_hist, T, d, w, q_begin, n_q, eps);
@@ -168,8 +171,10 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
     if (out == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if (!aligned(out, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: out is not 16-byte aligned", fn);
     if (lse != nullptr && !aligned(lse, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: lse is not 4-byte aligned", fn);
+    if (alpha != nullptr && !aligned(alpha, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: alpha is not 4-byte aligned", fn);
 
     attnres::BlockFwdParams p;
+    p.alpha = alpha;
     p.hist = hist;
     p.w = w;
     p.rinv = nullptr;

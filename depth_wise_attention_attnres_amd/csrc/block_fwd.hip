@@ -247,6 +247,12 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
         const float inv = 1.0f / (A + B);
         if (c <= G) cv = e * fast_exp2(M1 - M) * inv;
         if (c == G + 1) cv = B * inv;
+        if (p.alpha != nullptr && read_ok && tid == lane) {  // weight probe, stored by wave 0
+            float* al = p.alpha + (int64_t)(l - p.q_begin) * p.n_hist * p.T + t;
+            const int ns = G + 1 + (has_p ? 1 : 0);
+            if (c < ns) al[(int64_t)c * p.T] = cv;
+            for (int x = ns + c; x < p.n_hist; x += 16) al[(int64_t)x * p.T] = 0.f;
+        }
         if (read_ok && tid == lane && c == 0 && p.lse != nullptr)  // wave 0 stores lse
             p.lse[(int64_t)(l - p.q_begin) * p.T + t] = (M + fast_log2(A + B)) * kLn2;
     }

@@ -80,6 +80,10 @@ __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdPara
             for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
         float m2 = -INFINITY;  // running max of scores, log2 domain
         float Z = 0.f;         // running sum of exp2(s2 - m2)
+        int ns = 0;            // sources scored so far
+        // weight probe: lane 0 keeps each source's score in alpha and turns
+        // the scores into weights once the read's log-sum-exp is known
+        float* const al = p.alpha != nullptr ? p.alpha + (int64_t)j * p.n_hist * p.T + t : nullptr;
         float run[BLOCK ? NCH : 1][8];  // Block: the fp32 sum being formed
 #pragma unroll
         for (int c = 0; c < (BLOCK ? NCH : 1); ++c)
@@ -173,6 +177,8 @@ __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdPara
                         p.rinv[(int64_t)i * p.T + t] = r;
                 }
                 const float s2 = r * dp * kLog2e;
+                if (al != nullptr && ln == 0) al[(int64_t)ns * p.T] = s2;
+                ++ns;
                 if (s2 > m2) {  // new running max: rescale what is accumulated
                     const float cs = fast_exp2(m2 - s2);
                     Z *= cs;
@@ -228,6 +234,11 @@ __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdPara
             }
         }
         if (p.lse != nullptr && ln == 0) p.lse[(int64_t)j * p.T + t] = (m2 + fast_log2(Z)) * kLn2;
+        if (al != nullptr && ln == 0) {  // the same lane reads back what it wrote
+            const float lse2 = m2 + fast_log2(Z);
+            for (int x = 0; x < ns; ++x) al[(int64_t)x * p.T] = fast_exp2(al[(int64_t)x * p.T] - lse2);
+            for (int x = ns; x < p.n_hist; ++x) al[(int64_t)x * p.T] = 0.f;
+        }
     }
 }
 

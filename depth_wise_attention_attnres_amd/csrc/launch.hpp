@@ -23,6 +23,7 @@ struct FwdParams {
     float* lse;        // [n_q][T] or null
     const float* norm_gain;  // [n_q][d] or null (unit gain)
     void* normed;      // [n_q][T][d] pre-norm of the outputs, or null
+    float* alpha;      // [n_q][n_hist][T] softmax weights in source order, or null
     int64_t T;
     int d;             // width, multiple of 8
     int nc;            // d / 8 chunks

@@ -110,12 +110,20 @@ typedef enum attnres_variant {
  *                      the keys, taken from the fp32 h before its rounding;
  *                      norm_gain [n_q][d] fp32, or NULL for unit gain.
  *                      normed NULL: no pre-norm (norm_gain ignored).
+ *   alpha              optional weight probe [n_q][n_hist][T] fp32 (tokens
+ *                      fastest): alpha[j][x][t] is the softmax weight of the
+ *                      read's source x in source order (Full: rows 0..l);
+ *                      entries past the read's source count are 0.  The data
+ *                      behind the pages' weight maps ("DepthBench reading
+ *                      notes", the AttnRes weight figures); a probe, not a
+ *                      fast path (one lane per token writes it).
  */
 int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
                      int64_t T, int64_t d, const float* w, int64_t q_begin,
                      int64_t n_q, float eps, float* rinv, int64_t rinv_valid_rows,
                      void* out, attnres_dtype out_dtype, float* lse,
-                     const float* norm_gain, void* normed, hipStream_t stream);
+                     const float* norm_gain, void* normed, float* alpha,
+                     hipStream_t stream);
 
 /*
  * Block AttnRes forward, two-phase ("DepthBench reading notes" sec. 2.5;
@@ -123,12 +131,15 @@ int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
  * computation"): reads l = q_begin .. q_begin + n_q - 1 with block size S
  * (S >= 1; S = 1 is Full AttnRes).  The raw history is read once; block sums
  * and the partial sum are built on chip in fp32.  Arguments as in
- * attnres_full_fwd, without the rinv cache.
+ * attnres_full_fwd, without the rinv cache and the pre-norm; alpha (optional,
+ * [n_q][n_hist][T]) holds the weights of v_0, b_1 .. b_m and, when the read
+ * has one, the partial sum, in that order.
  */
 int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
                       int64_t T, int64_t d, int64_t S, const float* w,
                       int64_t q_begin, int64_t n_q, float eps, void* out,
-                      attnres_dtype out_dtype, float* lse, hipStream_t stream);
+                      attnres_dtype out_dtype, float* lse, float* alpha,
+                      hipStream_t stream);
 
 /*
  * Block AttnRes in model order, phase 1 (DataCamp, "two-phase computation":

@@ -45,9 +45,9 @@ def test_library_exports_every_declared_symbol(ar):
 
 
 def _full(ar, hist=P, hdt=BF16, n_hist=4, T=16, d=64, w=P2, q_begin=0, n_q=4, eps=1e-6,
-          rinv=None, rvalid=0, out=P3, odt=BF16, lse=None, gain=None, normed=None):
+          rinv=None, rvalid=0, out=P3, odt=BF16, lse=None, gain=None, normed=None, alpha=None):
     return ar.raw().attnres_full_fwd(hist, hdt, n_hist, T, d, w, q_begin, n_q, eps, rinv, rvalid,
-                                     out, odt, lse, gain, normed, None)
+                                     out, odt, lse, gain, normed, alpha, None)
 
 
 def test_full_fwd_validation(ar):
@@ -79,6 +79,7 @@ def test_full_fwd_validation(ar):
     assert _full(ar, T=1 << 40) == UNSUPPORTED
     assert _full(ar, normed=P + 8) == ALIGN
     assert _full(ar, normed=P, gain=P2 + 4) == ALIGN
+    assert _full(ar, alpha=P + 2) == ALIGN
     assert _full(ar, T=(1 << 27) + 1, d=8, n_hist=1, n_q=1) == UNSUPPORTED
     assert "2^27" in ar.last_error()
     assert _full(ar, T=1 << 27, d=8, n_hist=1, n_q=1, hist=None) == INVALID  # size accepted
@@ -91,17 +92,17 @@ def test_empty_calls_launch_nothing(ar):
     assert _full(ar, T=0, hist=None, w=None, out=None) == OK
     assert ar.last_error() == ""
     assert ar.raw().attnres_block_fwd(P, BF16, 4, 0, 64, 2, P2, 0, 4, 1e-6, P3, BF16, None,
-                                      None) == OK
+                                      None, None) == OK
 
 
 def test_block_fwd_validation(ar):
     lib = ar.raw()
-    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 0, P2, 0, 9, 1e-6, P3, BF16, None, None) == INVALID
+    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 0, P2, 0, 9, 1e-6, P3, BF16, None, None, None) == INVALID
     assert "S must be" in ar.last_error()
-    assert lib.attnres_block_fwd(P, BF16, 9, 16, 60, 2, P2, 0, 9, 1e-6, P3, BF16, None, None) == ALIGN
-    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 2, P2, 5, 9, 1e-6, P3, BF16, None, None) == INVALID
-    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 2, P2, 0, 9, 1e-6, None, BF16, None, None) == INVALID
-    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 2, P2, 0, 9, 1e-6, P3 + 4, BF16, None, None) == ALIGN
+    assert lib.attnres_block_fwd(P, BF16, 9, 16, 60, 2, P2, 0, 9, 1e-6, P3, BF16, None, None, None) == ALIGN
+    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 2, P2, 5, 9, 1e-6, P3, BF16, None, None, None) == INVALID
+    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 2, P2, 0, 9, 1e-6, None, BF16, None, None, None) == INVALID
+    assert lib.attnres_block_fwd(P, BF16, 9, 16, 64, 2, P2, 0, 9, 1e-6, P3 + 4, BF16, None, None, None) == ALIGN
 
 
 def test_status_strings(ar):

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity import check_lse, check_out, to_f64
+from parity import check_lse, check_out, check_rel, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -99,3 +99,23 @@ def test_block_workload_sampled(ar, oracle, name, S):
     print(f"{name}: {stats}", flush=True)
     del h, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_hist,T,d,S", [(17, 40, 256, 4), (13, 21, 136, 3), (65, 6, 2048, 8),
+                                          (70, 5, 64, 1)])
+def test_block_alpha_probe(ar, oracle, dtype, n_hist, T, d, S):
+    # two-phase kernel (<= 13 sources) and the streaming fallback (S = 1, 70 rows)
+    h, w, hd, wd = _inputs(n_hist, T, d, seed=n_hist * 3 + S, dtype=dtype, w_sigma=0.05)
+    alpha = torch.full((n_hist, n_hist, T), float("nan"), device=DEV)
+    ar.block_fwd(h, w, S, alpha=alpha)
+    torch.cuda.synchronize()
+    _, _, ref = oracle.fwd(oracle.BLOCK, hd, wd, S=S, want_alpha=True)
+    ref = ref.transpose(0, 2, 1)
+    a = to_f64(alpha)
+    check_rel(a, ref, 1e-5, "alpha")
+    assert (a >= 0).all()
+    np.testing.assert_allclose(a.sum(1), 1.0, atol=1e-5)
+    for l in range(n_hist):
+        ns = oracle.num_sources(oracle.BLOCK, l, S)
+        assert (a[l, ns:] == 0).all()

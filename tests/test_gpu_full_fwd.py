@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity import check_lse, check_out, to_f64
+from parity import check_lse, check_out, check_rel, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -184,3 +184,25 @@ def test_full_prenorm_in_model_order(ar, oracle):
     torch.cuda.synchronize()
     ref, _ = oracle.full_fwd(hd, wd)
     check_out(to_f64(normed), oracle.prenorm(ref, to_f64(gain)), "bf16", what="normed")
+
+
+# ---------------------------------------------------------------------------
+# weight probe (softmax weights in source order, tokens fastest)
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_hist,T,d,q_begin", [(9, 37, 64, 0), (17, 40, 520, 3), (6, 33, 2048, 0)])
+def test_full_alpha_probe(ar, oracle, dtype, n_hist, T, d, q_begin):
+    h, w, hd, wd = _inputs(n_hist, T, d, seed=n_hist * 5 + d, dtype=dtype, w_sigma=0.05)
+    n_q = n_hist - q_begin
+    w = w[q_begin:].contiguous()
+    alpha = torch.full((n_q, n_hist, T), float("nan"), device=DEV)
+    ar.full_fwd(h, w, q_begin=q_begin, alpha=alpha)
+    torch.cuda.synchronize()
+    _, _, ref = oracle.fwd(oracle.FULL, hd, wd[q_begin:], q_begin=q_begin, want_alpha=True)
+    ref = ref.transpose(0, 2, 1)  # [n_q][n_hist][T]
+    a = to_f64(alpha)
+    check_rel(a, ref, 1e-5, "alpha")
+    assert (a >= 0).all()
+    np.testing.assert_allclose(a.sum(1), 1.0, atol=1e-5)
+    for j in range(n_q):  # exactly zero past the read's source count
+        assert (a[j, q_begin + j + 1:] == 0).all()
