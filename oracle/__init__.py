@@ -67,6 +67,10 @@ def _load():
     lib.attnres_oracle_block_fwd_twophase.restype = ip
     lib.attnres_oracle_block_fwd_twophase.argtypes = [i64, vp, i64, i64, i64, vp, i64,
                                                       i64, dbl, vp, vp]
+    lib.attnres_oracle_fwd_tokq.restype = ip
+    lib.attnres_oracle_fwd_tokq.argtypes = [ip, i64, vp, i64, i64, i64, vp, i64, i64, dbl, vp, vp]
+    lib.attnres_oracle_query_proj.restype = ip
+    lib.attnres_oracle_query_proj.argtypes = [vp, vp, i64, i64, i64, vp]
     lib.attnres_oracle_prenorm.restype = ip
     lib.attnres_oracle_prenorm.argtypes = [vp, i64, i64, i64, vp, dbl, vp]
     lib.attnres_oracle_bwd.restype = ip
@@ -134,6 +138,34 @@ def full_fwd(hist, w, **kw):
 
 def block_fwd(hist, w, S: int, **kw):
     return fwd(BLOCK, hist, w, S=S, **kw)
+
+
+def fwd_tokq(variant: int, hist, q, *, S: int = 1, q_begin: int = 0, eps: float = 1e-6):
+    """Forward with a query per (read, token): q [n_q, T, d].  Returns (out, lse)."""
+    hist, q = _f64(hist), _f64(q)
+    n_hist, T, d = hist.shape
+    n_q = q.shape[0]
+    if q.shape != (n_q, T, d) or q_begin < 0 or q_begin + n_q > n_hist:
+        raise ValueError("q must be [n_q, T, d] with q_begin + n_q <= n_hist")
+    out = np.zeros((n_q, T, d), np.float64)
+    lse = np.zeros((n_q, T), np.float64)
+    rc = _load().attnres_oracle_fwd_tokq(variant, S, _ptr(hist), n_hist, T, d, _ptr(q), q_begin,
+                                         n_q, float(eps), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle fwd_tokq rejected its arguments")
+    return out, lse
+
+
+def query_proj(x, W) -> np.ndarray:
+    """q[j, t] = W[j] @ x[j, t] in fp64: x [n_q, T, d], W [n_q, d, d]."""
+    x, W = _f64(x), _f64(W)
+    n_q, T, d = x.shape
+    if W.shape != (n_q, d, d):
+        raise ValueError("W must be [n_q, d, d]")
+    q = np.zeros_like(x)
+    if _load().attnres_oracle_query_proj(_ptr(x), _ptr(W), n_q, T, d, _ptr(q)) != 0:
+        raise ValueError("oracle query_proj rejected its arguments")
+    return q
 
 
 def prenorm(z, gain=None, eps: float = 1e-6) -> np.ndarray:

@@ -172,10 +172,49 @@ int attnres_oracle_prenorm(const double* z, int64_t n_q, int64_t T, int64_t d,
  *   alpha [n_q][T][n_hist] or NULL: softmax weights, in source order,
  *         zero-padded past the read's source count.
  * Returns 0, or -1 on bad arguments / allocation failure. */
+static int fwd_impl(int variant, int64_t S, const double* hist, int64_t n_hist,
+                    int64_t T, int64_t d, const double* w, int per_token, int64_t q_begin,
+                    int64_t n_q, double eps, double* out, double* lse, double* alpha);
+
 int attnres_oracle_fwd(int variant, int64_t S, const double* hist, int64_t n_hist,
                        int64_t T, int64_t d, const double* w, int64_t q_begin,
                        int64_t n_q, double eps, double* out, double* lse,
                        double* alpha) {
+    return fwd_impl(variant, S, hist, n_hist, T, d, w, 0, q_begin, n_q, eps, out, lse, alpha);
+}
+
+/* The same forward with an input-dependent query per (read, token)
+ * ("Kimi K3 notes 2" sec. 6, the ablation): q [n_q][T][d], row (j, t) is the
+ * query of read q_begin + j for token t. */
+int attnres_oracle_fwd_tokq(int variant, int64_t S, const double* hist, int64_t n_hist,
+                            int64_t T, int64_t d, const double* q, int64_t q_begin,
+                            int64_t n_q, double eps, double* out, double* lse) {
+    return fwd_impl(variant, S, hist, n_hist, T, d, q, 1, q_begin, n_q, eps, out, lse, NULL);
+}
+
+/* Input-dependent query projection: q[j][t] = W[j] x[j][t], with
+ * W [n_q][d][d] row-major (q_k = sum_i W[j][k][i] x_i) and x [n_q][T][d] the
+ * hidden state each read projects from. */
+int attnres_oracle_query_proj(const double* x, const double* W, int64_t n_q, int64_t T,
+                              int64_t d, double* q) {
+    if (n_q < 0 || T < 0 || d < 1) return -1;
+    for (int64_t j = 0; j < n_q; ++j)
+        for (int64_t t = 0; t < T; ++t) {
+            const double* xr = x + (j * T + t) * d;
+            double* qr = q + (j * T + t) * d;
+            for (int64_t k = 0; k < d; ++k) {
+                const double* wr = W + (j * d + k) * d;
+                double s = 0.0;
+                for (int64_t i = 0; i < d; ++i) s += wr[i] * xr[i];
+                qr[k] = s;
+            }
+        }
+    return 0;
+}
+
+static int fwd_impl(int variant, int64_t S, const double* hist, int64_t n_hist,
+                    int64_t T, int64_t d, const double* w, int per_token, int64_t q_begin,
+                    int64_t n_q, double eps, double* out, double* lse, double* alpha) {
     if (variant != 0 && variant != 1) return -1;
     if (variant == 1 && S < 1) return -1;
     if (n_hist < 1 || T < 0 || d < 1 || q_begin < 0 || n_q < 0 ||
@@ -199,7 +238,7 @@ int attnres_oracle_fwd(int variant, int64_t S, const double* hist, int64_t n_his
             if (!ok) continue;
             for (int64_t j = 0; j < n_q; ++j) {
                 int64_t l = q_begin + j;
-                const double* wl = w + j * d;
+                const double* wl = per_token ? w + (j * T + t) * d : w + j * d;
                 int64_t n = build_sources(variant, S, hist, T, d, l, t, src, lo, hi);
                 /* scores s(x) = r(x) * (w_l . x) */
                 double smax = -INFINITY;

@@ -421,3 +421,58 @@ def test_prenorm_eps_inside_the_root(oracle):
     y = oracle.prenorm(np.full((1, 1, 8), c), eps=eps)
     np.testing.assert_allclose(y, c / np.sqrt(c * c + eps), rtol=1e-14)
     assert np.array_equal(oracle.prenorm(np.zeros((1, 2, 8)), eps=eps), np.zeros((1, 2, 8)))
+
+
+# ---------------------------------------------------------------------------
+# input-dependent query (projection of the current hidden state)
+
+def test_query_proj_worked_example(oracle):
+    spec = json.load(open(os.path.join(GOLDEN, "worked_examples.json")))
+    for ex in spec["query_proj_examples"]:
+        q = oracle.query_proj(np.array(ex["x"]), np.array(ex["W"]))
+        np.testing.assert_array_equal(q, np.array(ex["q"]), err_msg=ex["name"])
+
+
+@pytest.mark.parametrize("variant,S", [(0, 1), (1, 3)])
+def test_tokq_zero_projection_is_the_zero_query(oracle, variant, S):
+    rng = np.random.default_rng(31)
+    hist = rng.standard_normal((8, 5, 16))
+    q = np.zeros((8, 5, 16))
+    out, lse = oracle.fwd_tokq(variant, hist, q, S=S)
+    ref, ref_lse = oracle.fwd(variant, hist, np.zeros((8, 16)), S=S)
+    np.testing.assert_allclose(out, ref, rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-15)
+
+
+@pytest.mark.parametrize("variant,S", [(0, 1), (1, 2)])
+def test_tokq_shared_state_equals_fixed_query(oracle, variant, S):
+    # every token has the same current state x_l, so q_l = W_l x_l is one query
+    # per read: the per-token path must equal the pinned fixed-query forward
+    rng = np.random.default_rng(32)
+    n, T, d = 7, 6, 12
+    hist = rng.standard_normal((n, T, d))
+    W = rng.standard_normal((n, d, d)) * 0.1
+    xs = rng.standard_normal((n, 1, d))
+    q = oracle.query_proj(np.repeat(xs, T, axis=1), W)
+    out, lse = oracle.fwd_tokq(variant, hist, q, S=S)
+    ref, ref_lse = oracle.fwd(variant, hist, q[:, 0, :], S=S)
+    np.testing.assert_allclose(out, ref, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-14)
+
+
+def test_tokq_follows_its_token(oracle):
+    # permuting the tokens of the history and of the queries permutes the outputs
+    rng = np.random.default_rng(33)
+    n, T, d = 6, 9, 8
+    hist = rng.standard_normal((n, T, d))
+    q = rng.standard_normal((n, T, d)) * 0.4
+    perm = rng.permutation(T)
+    out, _ = oracle.fwd_tokq(0, hist, q)
+    out_p, _ = oracle.fwd_tokq(0, hist[:, perm], q[:, perm])
+    np.testing.assert_allclose(out_p, out[:, perm], rtol=0, atol=0)
+    # and a per-token query is really used: two tokens with equal histories but
+    # different queries read differently
+    hist2 = np.repeat(hist[:, :1], 2, axis=1)
+    q2 = np.stack([q[:, 0], -q[:, 0]], axis=1)
+    out2, _ = oracle.fwd_tokq(0, hist2, q2)
+    assert np.abs(out2[-1, 0] - out2[-1, 1]).max() > 1e-3
