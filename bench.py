@@ -293,6 +293,36 @@ def extra_measurements(dev):
     del h, w, out, lse, st
     torch.cuda.empty_cache()
 
+    # input-dependent query on the L=32 / d=896 history: the projection of every
+    # read's newest row (one call, all reads) and the model-order sweep with a
+    # projection per read (synthetic W ~ N(0, 0.05^2 / d), bf16)
+    wl = WORKLOADS["full_L32_d896"]
+    h, _, _ = device_inputs(wl, dev)
+    n, T, d = h.shape
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed + 101)
+    W = (torch.randn((n, d, d), generator=gen, device=dev) * (0.05 / d ** 0.5)).to(torch.bfloat16)
+    q_all = torch.empty((n, T, d), dtype=torch.float32, device=dev)
+    ms_p = _time(lambda: ar.query_proj(h, W, q=q_all), stream, 3, 1)
+    flops = 2.0 * n * T * d * d
+    q1 = torch.empty((1, T, d), dtype=torch.float32, device=dev)
+    rinv = torch.empty((n, T), dtype=torch.float32, device=dev)
+    out = torch.empty_like(h)
+
+    def sweep():
+        for l in range(n):
+            ar.query_proj(h[l:l + 1], W[l:l + 1], q=q1)
+            ar.full_fwd_q(h, q1, q_begin=l, rinv=rinv, rinv_valid_rows=l, out=out[l:l + 1],
+                          want_lse=False)
+    ms_s = _time(sweep, stream, 3, 1)
+    res[wl.name + "_input_dependent_query"] = {
+        "what": "q_l = W_l v_l (d x d, bf16 matrix cores) + Full AttnRes with per-token queries",
+        "proj_all_reads_ms": ms_p, "proj_TFLOPs": flops / (ms_p * 1e-3) / 1e12,
+        "proj_frac_of_bf16_dense_peak": flops / (ms_p * 1e-3) / 1e12 / 2500.0,
+        "model_order_ms": ms_s, "model_order_tokens_per_s": T / (ms_s * 1e-3)}
+    del h, W, q_all, q1, rinv, out
+    torch.cuda.empty_cache()
+
     wl = WORKLOADS["fwdbwd_L24_d1024"]
     h, w, g = device_inputs(wl, dev)
     n, T, d = h.shape

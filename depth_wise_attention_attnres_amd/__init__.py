@@ -27,7 +27,8 @@ STATUS = {0: "ATTNRES_OK", 1: "ATTNRES_ERR_INVALID_ARG", 2: "ATTNRES_ERR_UNSUPPO
           3: "ATTNRES_ERR_ALIGN", 4: "ATTNRES_ERR_WORKSPACE", 5: "ATTNRES_ERR_HIP"}
 
 # every symbol include/attnres.h declares
-EXPORTS = ["attnres_full_fwd", "attnres_block_fwd", "attnres_block_phase1", "attnres_block_phase2",
+EXPORTS = ["attnres_full_fwd", "attnres_full_fwd_q", "attnres_query_proj", "attnres_block_fwd",
+           "attnres_block_phase1", "attnres_block_phase2",
            "attnres_bwd", "attnres_bwd_workspace_bytes", "attnres_block_index_table",
            "attnres_status_string", "attnres_last_error"]
 
@@ -44,6 +45,11 @@ _lib.attnres_full_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, 
 _lib.attnres_block_fwd.restype = _int
 _lib.attnres_block_fwd.argtypes = [_vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp,
                                    _int, _vp, _vp, _vp]
+_lib.attnres_full_fwd_q.restype = _int
+_lib.attnres_full_fwd_q.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _vp, _i64,
+                                    _vp, _int, _vp, _vp]
+_lib.attnres_query_proj.restype = _int
+_lib.attnres_query_proj.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _int, _vp, _vp]
 _lib.attnres_block_phase1.restype = _int
 _lib.attnres_block_phase1.argtypes = [_vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _i64, _f32, _vp,
                                       _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp]
@@ -152,6 +158,47 @@ def full_fwd(hist, w, *, q_begin: int = 0, n_q: int | None = None, eps: float = 
     _check(_lib.attnres_full_fwd(_ptr(hist), _dtype_code(hist), n_hist, T, d, _ptr(w), q_begin,
                                  n_q, eps, _ptr(rinv), rinv_valid_rows, _ptr(out), odt, _ptr(lse),
                                  _ptr(norm_gain), _ptr(normed), _ptr(alpha), _stream(hist)))
+    return out, lse
+
+
+def query_proj(x, W, *, q=None):
+    """Input-dependent queries q[j, t] = W[j] @ x[j, t] (bf16 x [n_q, T, d] and
+    W [n_q, d, d]; fp32 q).  Returns q."""
+    import torch
+    _require(x, "x", dtype=torch.bfloat16)
+    n_q, T, d = x.shape
+    _require(W, "W", dtype=torch.bfloat16, shape=(n_q, d, d))
+    if q is None:
+        q = torch.empty((n_q, T, d), dtype=torch.float32, device=x.device)
+    _require(q, "q", dtype=torch.float32, shape=(n_q, T, d))
+    _check(_lib.attnres_query_proj(_ptr(x), BF16, n_q, T, d, _ptr(W), BF16, _ptr(q), _stream(x)))
+    return q
+
+
+def full_fwd_q(hist, q, *, q_begin: int = 0, eps: float = 1e-6, rinv=None,
+               rinv_valid_rows: int = 0, out=None, out_dtype=None, lse=None, want_lse: bool = True):
+    """Full AttnRes with a query per (read, token): q [n_q, T, d] fp32 for reads
+    q_begin .. q_begin + n_q - 1.  Returns (out, lse)."""
+    import torch
+    _require(hist, "hist")
+    n_hist, T, d = hist.shape
+    n_q = q.shape[0]
+    _require(q, "q", dtype=torch.float32, shape=(n_q, T, d))
+    odt = _dtype_code(hist) if out_dtype is None else (F32 if out_dtype == torch.float32 else BF16)
+    if out is None:
+        out = torch.empty((n_q, T, d), dtype=_torch_dtype(odt), device=hist.device)
+    else:
+        _require(out, "out", shape=(n_q, T, d))
+        odt = _dtype_code(out)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, T), dtype=torch.float32, device=hist.device)
+    if lse is not None:
+        _require(lse, "lse", dtype=torch.float32, shape=(n_q, T))
+    if rinv is not None:
+        _require(rinv, "rinv", dtype=torch.float32, shape=(n_hist, T))
+    _check(_lib.attnres_full_fwd_q(_ptr(hist), _dtype_code(hist), n_hist, T, d, _ptr(q), q_begin,
+                                   n_q, eps, _ptr(rinv), rinv_valid_rows, _ptr(out), odt,
+                                   _ptr(lse), _stream(hist)))
     return out, lse
 
 

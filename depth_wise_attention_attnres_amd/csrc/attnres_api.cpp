@@ -109,13 +109,16 @@ int attnres_block_index_table(int64_t n_hist, int64_t S, int64_t q_begin, int64_
     return ok();
 }
 
-int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
-                     int64_t d, const float* w, int64_t q_begin, int64_t n_q, float eps,
-                     float* rinv, int64_t rinv_valid_rows, void* out, attnres_dtype out_dtype,
-                     float* lse, const float* norm_gain, void* normed, float* alpha,
-                     hipStream_t stream) {
-    const char* fn = "attnres_full_fwd";
-    int st = check_common(fn, hist, hist_dtype, n_hist, T, d, w, q_begin, n_q, eps);
+namespace {
+
+// w (one query per read) or qtok (one per read and token; w must be NULL)
+int full_fwd_impl(const char* fn, const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
+                  int64_t T, int64_t d, const float* w, const float* qtok, int64_t q_begin,
+                  int64_t n_q, float eps, float* rinv, int64_t rinv_valid_rows, void* out,
+                  attnres_dtype out_dtype, float* lse, const float* norm_gain, void* normed,
+                  float* alpha, hipStream_t stream) {
+    int st = check_common(fn, hist, hist_dtype, n_hist, T, d, qtok != nullptr ? qtok : w, q_begin,
+                          n_q, eps);
     if (st != ATTNRES_OK) return st;
     if (!valid_dtype(out_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad out dtype %d", fn, (int)out_dtype);
     if (rinv_valid_rows < 0 || rinv_valid_rows > n_hist)
@@ -136,6 +139,7 @@ int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
 
     attnres::FullFwdParams p;
     p.alpha = alpha;
+    p.qtok = qtok;
     p.hist = hist;
     p.w = w;
     p.rinv = rinv;
@@ -158,6 +162,47 @@ int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
     return hip_status(fn, attnres::launch_full_fwd(p, hist_dtype, out_dtype, stream));
 }
 
+}  // namespace
+
+int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
+                     int64_t d, const float* w, int64_t q_begin, int64_t n_q, float eps,
+                     float* rinv, int64_t rinv_valid_rows, void* out, attnres_dtype out_dtype,
+                     float* lse, const float* norm_gain, void* normed, float* alpha,
+                     hipStream_t stream) {
+    return full_fwd_impl("attnres_full_fwd", hist, hist_dtype, n_hist, T, d, w, nullptr, q_begin,
+                         n_q, eps, rinv, rinv_valid_rows, out, out_dtype, lse, norm_gain, normed,
+                         alpha, stream);
+}
+
+int attnres_full_fwd_q(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
+                       int64_t d, const float* q, int64_t q_begin, int64_t n_q, float eps,
+                       float* rinv, int64_t rinv_valid_rows, void* out, attnres_dtype out_dtype,
+                       float* lse, hipStream_t stream) {
+    return full_fwd_impl("attnres_full_fwd_q", hist, hist_dtype, n_hist, T, d, nullptr, q, q_begin,
+                         n_q, eps, rinv, rinv_valid_rows, out, out_dtype, lse, nullptr, nullptr,
+                         nullptr, stream);
+}
+
+int attnres_query_proj(const void* x, attnres_dtype x_dtype, int64_t n_q, int64_t T, int64_t d,
+                       const void* W, attnres_dtype w_dtype, float* q, hipStream_t stream) {
+    const char* fn = "attnres_query_proj";
+    if (!valid_dtype(x_dtype) || !valid_dtype(w_dtype))
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad dtype", fn);
+    if (n_q < 0 || T < 0 || d < 1) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad sizes", fn);
+    if (d % 8 != 0) return fail(ATTNRES_ERR_ALIGN, "%s: d = %" PRId64 " is not a multiple of 8", fn, d);
+    if (d > attnres::kMaxD) return fail(ATTNRES_ERR_UNSUPPORTED, "%s: d = %" PRId64 " exceeds %d", fn, d, attnres::kMaxD);
+    if (x_dtype != ATTNRES_BF16 || w_dtype != ATTNRES_BF16)
+        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: only bf16 x and W (the matrix-core path)", fn);
+    if (T > ((int64_t)1 << 27)) return fail(ATTNRES_ERR_UNSUPPORTED, "%s: T exceeds 2^27 tokens", fn);
+    if (n_q * ((T + 63) / 64) * ((d + 63) / 64) >= ((int64_t)1 << 31))
+        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: too many tiles for one launch", fn);
+    if (n_q == 0 || T == 0) return ok();
+    if (x == nullptr || W == nullptr || q == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(q, 16))
+        return fail(ATTNRES_ERR_ALIGN, "%s: x, W and q must be 16-byte aligned", fn);
+    return hip_status(fn, attnres::launch_query_proj(x, W, q, n_q, T, (int)d, stream));
+}
+
 int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
                       int64_t d, int64_t S, const float* w, int64_t q_begin, int64_t n_q,
                       float eps, void* out, attnres_dtype out_dtype, float* lse, float* alpha,
@@ -175,6 +220,7 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
 
     attnres::BlockFwdParams p;
     p.alpha = alpha;
+    p.qtok = nullptr;
     p.hist = hist;
     p.w = w;
     p.rinv = nullptr;

@@ -63,7 +63,10 @@ __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdPara
         const int l = p.q_begin + j;
         float wv[NCH][8];
         {
-            const rsrc_t wr = make_rsrc(p.w + (int64_t)j * p.d, (uint64_t)p.d * 4);
+            // the read's query: one per read, or one per (read, token)
+            const float* wrow = p.qtok != nullptr ? p.qtok + ((int64_t)j * p.T + t) * p.d
+                                                  : p.w + (int64_t)j * p.d;
+            const rsrc_t wr = make_rsrc(wrow, (uint64_t)p.d * 4);
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const uint32_t off = in_off[c] == kOOB ? kOOB : (uint32_t)((c * LPT + ln) * 32);

@@ -24,6 +24,7 @@ struct FwdParams {
     const float* norm_gain;  // [n_q][d] or null (unit gain)
     void* normed;      // [n_q][T][d] pre-norm of the outputs, or null
     float* alpha;      // [n_q][n_hist][T] softmax weights in source order, or null
+    const float* qtok; // [n_q][T][d] per-token queries (then w is unused), or null
     int64_t T;
     int d;             // width, multiple of 8
     int nc;            // d / 8 chunks
@@ -114,6 +115,9 @@ struct Phase2Params {
     float eps, inv_d;
 };
 hipError_t launch_block_phase1(const Phase1Params& p, hipStream_t stream);
+// q[j][t] = W[j] x[j][t] on the matrix cores (bf16 x and W, fp32 q)
+hipError_t launch_query_proj(const void* x, const void* W, float* q, int64_t n_q, int64_t T, int d,
+                             hipStream_t stream);
 hipError_t launch_block_phase2(const Phase2Params& p, hipStream_t stream);
 // zero `bytes` (a multiple of 4) of device memory with a kernel
 hipError_t launch_fill_zero(void* dst, int64_t bytes, hipStream_t stream);

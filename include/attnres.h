@@ -126,6 +126,32 @@ int attnres_full_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
                      hipStream_t stream);
 
 /*
+ * Input-dependent query (the ablation in "Kimi K3 notes 2", sec. 6: a d x d
+ * projection of the current hidden state replaces the learned per-read
+ * query).  q[j][t] = W[j] x[j][t], i.e. q_k = sum_i W[j][k][i] x[j][t][i].
+ *   x  [n_q][T][d] bf16: the hidden state each read projects from (for read
+ *      l of a history, the newest row v_l: pass hist + l*T*d)
+ *   W  [n_q][d][d] bf16, row-major (output index first)
+ *   q  [n_q][T][d] fp32 (overwritten)
+ * Other dtypes return ATTNRES_ERR_UNSUPPORTED.  d % 8 == 0, d <= 4096,
+ * 16-byte aligned pointers.
+ */
+int attnres_query_proj(const void* x, attnres_dtype x_dtype, int64_t n_q, int64_t T, int64_t d,
+                       const void* W, attnres_dtype w_dtype, float* q, hipStream_t stream);
+
+/*
+ * Full AttnRes forward with a query per (read, token) -- the same aggregation
+ * as attnres_full_fwd, scored with q[j][t] (from attnres_query_proj or any
+ * caller) instead of one w[j] per read.  Arguments as in attnres_full_fwd with
+ * q [n_q][T][d] fp32 in place of w (16-byte aligned); no pre-norm or weight
+ * probe.
+ */
+int attnres_full_fwd_q(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
+                       int64_t d, const float* q, int64_t q_begin, int64_t n_q, float eps,
+                       float* rinv, int64_t rinv_valid_rows, void* out, attnres_dtype out_dtype,
+                       float* lse, hipStream_t stream);
+
+/*
  * Block AttnRes forward, two-phase ("DepthBench reading notes" sec. 2.5;
  * "LLMRes", Block paragraph; DataCamp, block section and "two-phase
  * computation"): reads l = q_begin .. q_begin + n_q - 1 with block size S

@@ -225,3 +225,25 @@ def test_block_phase_validation(ar):
     assert ph2(T=0) == OK
     assert ph2(nrm=P + 4) == ALIGN
     assert ph2(nrm=P, g=P2 + 8) == ALIGN
+
+
+def test_query_proj_and_full_fwd_q_validation(ar):
+    lib = ar.raw()
+    # x, x_dt, n_q, T, d, W, w_dt, q, stream
+    assert lib.attnres_query_proj(P, F32, 2, 16, 64, P2, BF16, P3, None) == UNSUPPORTED
+    assert lib.attnres_query_proj(P, BF16, 2, 16, 64, P2, F32, P3, None) == UNSUPPORTED
+    assert lib.attnres_query_proj(P, BF16, 2, 16, 60, P2, BF16, P3, None) == ALIGN
+    assert lib.attnres_query_proj(P, BF16, 2, 16, 8192, P2, BF16, P3, None) == UNSUPPORTED
+    assert lib.attnres_query_proj(P, BF16, 2, 16, 64, None, BF16, P3, None) == INVALID
+    assert lib.attnres_query_proj(P, BF16, 2, 16, 64, P2, BF16, P3 + 4, None) == ALIGN
+    assert lib.attnres_query_proj(P, BF16, 0, 16, 64, None, BF16, None, None) == OK
+    assert lib.attnres_query_proj(P, 7, 2, 16, 64, P2, BF16, P3, None) == INVALID
+    # hist, dt, n_hist, T, d, q, q_begin, n_q, eps, rinv, rvalid, out, out_dt, lse, stream
+    assert lib.attnres_full_fwd_q(P, BF16, 4, 16, 64, None, 0, 4, 1e-6, None, 0, P3, BF16, None,
+                                  None) == INVALID
+    assert lib.attnres_full_fwd_q(P, BF16, 4, 16, 64, P2 + 4, 0, 4, 1e-6, None, 0, P3, BF16, None,
+                                  None) == ALIGN
+    assert lib.attnres_full_fwd_q(P, BF16, 4, 16, 64, P2, 1, 4, 1e-6, None, 0, P3, BF16, None,
+                                  None) == INVALID
+    assert lib.attnres_full_fwd_q(P, BF16, 4, 0, 64, P2, 0, 4, 1e-6, None, 0, P3, BF16, None,
+                                  None) == OK
