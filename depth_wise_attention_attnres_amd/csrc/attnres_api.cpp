@@ -194,7 +194,7 @@ int attnres_query_proj(const void* x, attnres_dtype x_dtype, int64_t n_q, int64_
     if (x_dtype != ATTNRES_BF16 || w_dtype != ATTNRES_BF16)
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: only bf16 x and W (the matrix-core path)", fn);
     if (T > ((int64_t)1 << 27)) return fail(ATTNRES_ERR_UNSUPPORTED, "%s: T exceeds 2^27 tokens", fn);
-    if (n_q * ((T + 63) / 64) * ((d + 63) / 64) >= ((int64_t)1 << 31))
+    if (n_q * ((T + 127) / 128) * ((d + 127) / 128) >= ((int64_t)1 << 31))
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: too many tiles for one launch", fn);
     if (n_q == 0 || T == 0) return ok();
     if (x == nullptr || W == nullptr || q == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: NULL pointer", fn);

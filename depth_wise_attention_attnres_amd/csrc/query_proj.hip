@@ -5,10 +5,8 @@
 // v_mfma_f32_32x32x16_bf16, D[32 tokens x 32 outputs] += A B with
 //   A[i][k] = x[token t0 + i][k]   (lane j: token j % 32, k = 8 (j / 32) .. + 7)
 //   B[k][n] = W[output o0 + n][k]  (lane j: output j % 32, same k)
-// so both operands are 16-byte loads contiguous in k.  bf16 x bf16 products
-// are exact in fp32; the accumulators are folded into fp32 totals every 16
-// steps.  One wave per 32 x 32 tile, four waves (a 64 x 64 tile) per
-// workgroup; operands are fetched two steps ahead.
+// so both operands are 8 consecutive k of one row.  bf16 x bf16 products are
+// exact in fp32; the accumulators are folded into fp32 totals every 16 steps.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -17,81 +15,139 @@ namespace attnres {
 namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ bf16x8_t ld8(const bf16_t* ptr, bool ok) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (ok) v = *reinterpret_cast<const u32x4*>(ptr);
-    return __builtin_bit_cast(bf16x8_t, v);
-}
 }  // namespace
+
+// Workgroup tile: 128 tokens x 128 outputs; wave (wr, wc) of the 2 x 2 waves
+// computes 64 x 64 as 2 x 2 fragments of 32 x 32, so each operand fragment
+// read from LDS feeds two matrix instructions.  K goes in stages of 32
+// elements through double-buffered LDS: the workgroup loads a stage's 128
+// token rows and 128 W rows (contiguous in k, 16 bytes per lane)
+// while it multiplies the previous stage; one barrier per stage.
+constexpr int kTileM = 128, kTileN = 128, kStageK = 32;
+constexpr int kLdsRow = kStageK + 8;  // bf16 elements per LDS row (padded: staggers the banks)
 
 __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q,
                                                          int64_t T, int d, int tiles_t, int tiles_o) {
-    const int wave = threadIdx.x >> 6, ln = threadIdx.x & 63;
+    __shared__ __attribute__((aligned(16))) bf16_t lds_a[2][kTileM * kLdsRow];
+    __shared__ __attribute__((aligned(16))) bf16_t lds_b[2][kTileN * kLdsRow];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, ln = tid & 63;
     const int h = ln >> 5, m = ln & 31;
+    const int wr = wave >> 1, wc = wave & 1;
     // blockIdx.x = (read j, token tile, output tile), output tiles fastest so
     // that the workgroups sharing a token tile run together and reuse it in L2
-    const int64_t b = blockIdx.x;
-    const int to = (int)(b % tiles_o);
-    const int64_t rest = b / tiles_o;
+    const int64_t blk = blockIdx.x;
+    const int to = (int)(blk % tiles_o);
+    const int64_t rest = blk / tiles_o;
     const int tt = (int)(rest % tiles_t);
     const int64_t j = rest / tiles_t;
-    const int64_t t0 = (int64_t)tt * 64 + 32 * (wave >> 1);
-    const int o0 = to * 64 + 32 * (wave & 1);
+    const int64_t t0 = (int64_t)tt * kTileM;
+    const int o0 = to * kTileN;
+    const bf16_t* xj = x + j * T * d;
+    const bf16_t* wj = W + j * (int64_t)d * d;
 
-    const int64_t tok = t0 + m;
-    const bool tok_ok = tok < T;
-    const int out = o0 + m;
-    const bool out_ok = out < d;
-    const bf16_t* xp = x + (j * T + (tok_ok ? tok : 0)) * d + 8 * h;
-    const bf16_t* wp = W + (j * d + (out_ok ? out : 0)) * (int64_t)d + 8 * h;
-
-    constexpr int kFold = 16, kPD = 2;
-    f32x16 acc, tot;
+    // global -> LDS: thread tid moves the 16-byte chunks (row, kc) =
+    // (idx / kCh, idx % kCh), idx = tid + 256 c, of each operand tile
+    constexpr int kCh = kStageK / 8;                 // 16-byte chunks per row
+    constexpr int kPer = kTileM * kCh / 256;         // chunks per thread and operand
+    u32x4 sa[kPer], sb[kPer];
+    auto gload = [&](int k0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = tot[r] = 0.f;
-    bf16x8_t ra[kPD], rb[kPD];
-    const int n_steps = (d + 15) / 16;
-    auto fetch = [&](int u, int st) {
-        const bool kok = 16 * st + 8 * h < d;  // d % 8 == 0: all eight or none
-        ra[u] = ld8(xp + 16 * st, tok_ok && kok);
-        rb[u] = ld8(wp + 16 * st, out_ok && kok);
+        for (int c = 0; c < kPer; ++c) {
+            const int idx = tid + 256 * c;
+            const int row = idx / kCh, kc = idx % kCh;
+            const int k = k0 + 8 * kc;
+            const int64_t tok = t0 + row;
+            const int out = o0 + row;
+            u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
+            if (tok < T && k < d) va = *reinterpret_cast<const u32x4*>(xj + tok * d + k);
+            if (out < d && k < d) vb = *reinterpret_cast<const u32x4*>(wj + (int64_t)out * d + k);
+            sa[c] = va;
+            sb[c] = vb;
+        }
     };
+    auto lstore = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < kPD; ++u)
-        if (u < n_steps) fetch(u, u);
-    for (int s0 = 0; s0 < n_steps; s0 += kPD) {
+        for (int c = 0; c < kPer; ++c) {
+            const int idx = tid + 256 * c;
+            const int row = idx / kCh, kc = idx % kCh;
+            *reinterpret_cast<u32x4*>(&lds_a[buf][row * kLdsRow + 8 * kc]) = sa[c];
+            *reinterpret_cast<u32x4*>(&lds_b[buf][row * kLdsRow + 8 * kc]) = sb[c];
+        }
+    };
+
+    constexpr int kFold = 16;  // K-steps of 16 between folds into the fp32 totals
+    f32x16 acc[2][2], tot[2][2];
 #pragma unroll
-        for (int u = 0; u < kPD; ++u) {
-            const int st = s0 + u;
-            if (st >= n_steps) break;
-            const bf16x8_t a = ra[u], bb = rb[u];
-            if (st + kPD < n_steps) fetch(u, st + kPD);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
-            if ((st + 1) % kFold == 0 || st + 1 == n_steps) {
+    for (int fa = 0; fa < 2; ++fa)
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[fa][fb][r] = tot[fa][fb][r] = 0.f;
+
+    const int n_stages = (d + kStageK - 1) / kStageK;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    int step = 0;  // K-steps of 16 done
+    for (int st = 0; st < n_stages; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < n_stages) gload((st + 1) * kStageK);
+#pragma unroll
+        for (int sub = 0; sub < kStageK / 16; ++sub) {
+            bf16x8_t fa_op[2], fb_op[2];
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const int ra = 64 * wr + 32 * f + m, rb = 64 * wc + 32 * f + m;
+                fa_op[f] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_a[buf][ra * kLdsRow + 16 * sub + 8 * h]));
+                fb_op[f] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_b[buf][rb * kLdsRow + 16 * sub + 8 * h]));
+            }
+#pragma unroll
+            for (int fa = 0; fa < 2; ++fa)
+#pragma unroll
+                for (int fb = 0; fb < 2; ++fb)
+                    acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_op[fa], fb_op[fb], acc[fa][fb], 0, 0, 0);
+            ++step;
+            if (step % kFold == 0) {
+#pragma unroll
+                for (int fa = 0; fa < 2; ++fa)
+#pragma unroll
+                    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            tot[fa][fb][r] += acc[fa][fb][r];
+                            acc[fa][fb][r] = 0.f;
+                        }
+            }
+        }
+        if (st + 1 < n_stages) {
+            lstore(buf ^ 1);  // the other buffer: last read before the previous barrier
+            __syncthreads();
+        }
+    }
+    // lane j, register r of fragment (fa, fb) holds token t0 + 64 wr + 32 fa + i,
+    // output o0 + 64 wc + 32 fb + m, with i = 8 (r / 4) + 4 h + r % 4
+#pragma unroll
+    for (int fa = 0; fa < 2; ++fa)
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) {
+            const int out = o0 + 64 * wc + 32 * fb + m;
+            if (out < d) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    tot[r] += acc[r];
-                    acc[r] = 0.f;
+                    const int64_t ti = t0 + 64 * wr + 32 * fa + 8 * (r / 4) + 4 * h + r % 4;
+                    if (ti < T) q[(j * T + ti) * d + out] = tot[fa][fb][r] + acc[fa][fb][r];
                 }
             }
         }
-    }
-    // lane j, register r holds D[i][n = m]: token t0 + i, output o0 + m,
-    // i = 8 (r / 4) + 4 h + r % 4
-    if (out_ok) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t ti = t0 + 8 * (r / 4) + 4 * h + r % 4;
-            if (ti < T) q[(j * T + ti) * d + out] = tot[r];
-        }
-    }
 }
 
 hipError_t launch_query_proj(const void* x, const void* W, float* q, int64_t n_q, int64_t T, int d,
                              hipStream_t stream) {
-    const int tiles_t = (int)((T + 63) / 64);
-    const int tiles_o = (d + 63) / 64;
+    const int tiles_t = (int)((T + kTileM - 1) / kTileM);
+    const int tiles_o = (d + kTileN - 1) / kTileN;
     const int64_t blocks = n_q * tiles_t * (int64_t)tiles_o;
     hipLaunchKernelGGL(query_proj_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), q, T, d,
