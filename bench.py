@@ -233,6 +233,23 @@ def _time(fn, stream, reps, warm):
     return a.elapsed_time(b) / reps
 
 
+FP32_VECTOR_PEAK_TFLOPS = 78.6  # 256 CUs x 64 lanes x 2 FLOP x 2.4 GHz, no packed fp32
+
+
+def bwd_fmas_per_token(n_hist, n_q, S):
+    """Multiply-adds per token and per column of d for one backward: for each
+    read, the score and gradient dots of its sources (two per source), the
+    value and query paths into every history row it sees (two per row) and
+    the dw product (one per row); once per row, the squared norm of the
+    source it closes and the coupling term."""
+    total = 2 * n_hist
+    for l in range(n_q):
+        m = l // S
+        n_src = m + 1 + (1 if l % S else 0)
+        total += 2 * n_src + 3 * (l + 1)
+    return total
+
+
 def model_order_bytes_per_token(n, d, S, vb=2, ob=2):
     """HBM bytes per token of one model-order Block sweep (phase 1 per group:
     frozen fp32 sources read, new row and partial sum read, new block written,
@@ -348,6 +365,11 @@ def extra_measurements(dev):
             # compulsory traffic of the backward: history and dout read, dhist written
             "bwd_algorithmic_GBps": (3 * n * T * d * 2) / (ms_b * 1e-3) / 1e9,
             "bwd_frac_of_hbm_peak": (3 * n * T * d * 2) / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            # the backward is bound by its arithmetic: algorithmic FMAs over the
+            # non-packed fp32 vector peak (packed fp32 is not used, so 78.6 TFLOP/s)
+            "bwd_algorithmic_TFLOPs": 2 * bwd_fmas_per_token(n, n, S) * d * T / (ms_b * 1e-3) / 1e12,
+            "bwd_frac_of_fp32_vector_peak":
+                2 * bwd_fmas_per_token(n, n, S) * d * T / (ms_b * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
         }
         del ws
     return res

@@ -247,3 +247,18 @@ def test_query_proj_and_full_fwd_q_validation(ar):
                                   None) == INVALID
     assert lib.attnres_full_fwd_q(P, BF16, 4, 0, 64, P2, 0, 4, 1e-6, None, 0, P3, BF16, None,
                                   None) == OK
+
+
+def test_package_fails_loudly_without_the_library(tmp_path):
+    # a copy of the package without libattnres.so must refuse to import (there
+    # is no CPU fallback)
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(ROOT, "depth_wise_attention_attnres_amd")
+    dst = tmp_path / "depth_wise_attention_attnres_amd"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.so", "csrc", "__pycache__"))
+    r = subprocess.run([sys.executable, "-c", "import depth_wise_attention_attnres_amd"],
+                       cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "not built" in r.stderr
