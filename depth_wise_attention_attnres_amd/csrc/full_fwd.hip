@@ -37,7 +37,9 @@ __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdPara
     constexpr int TPB = kStreamThreads / LPT;  // tokens per block
     const int ln = threadIdx.x % LPT;
     const int64_t tok0 = (int64_t)blockIdx.x * TPB;
-    const int tl = threadIdx.x / LPT;  // token within the block
+    // token within the block; with one token per wave it is wave-uniform, and
+    // saying so keeps every per-token address (query row, probe) scalar
+    const int tl = LPT == 64 ? __builtin_amdgcn_readfirstlane(threadIdx.x / LPT) : threadIdx.x / LPT;
     const int64_t t = tok0 + tl;
     if (t >= p.T) return;  // whole token groups leave together
 
