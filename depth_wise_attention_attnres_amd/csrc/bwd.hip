@@ -1053,11 +1053,9 @@ hipError_t launch_rest(const BwdParams& p, int n_chunks, hipStream_t stream) {
     if (p.n_hist <= 8)
         hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 8, 4>), dim3((unsigned)(p.T * slices)), dim3(64),
                            0, stream, p);
-    else if (p.n_hist <= 16)
+    else  // 16-row tiles: 125 VGPRs, four waves per SIMD (32-row tiles: 192, two
+          // waves, 1 ms slower at 49 rows / d = 1024 although they stream fewer reads)
         hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 16, 4>), dim3((unsigned)(p.T * slices)),
-                           dim3(64), 0, stream, p);
-    else
-        hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 32, 4>), dim3((unsigned)(p.T * slices)),
                            dim3(64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
