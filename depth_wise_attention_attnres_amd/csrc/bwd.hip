@@ -428,7 +428,7 @@ __global__ __launch_bounds__(512) void bwd_scores_mfma_kernel(BwdParams p, int r
 #pragma unroll
         for (int r = 0; r < 16; ++r) accG[r] = accP[r] = accQ[r] = totP[r] = totQ[r] = 0.f;
         // operands of the next kPD K-steps, in a ring (one slot per step)
-        constexpr int kPD = 3;
+        constexpr int kPD = 2;
         bf16x8_t rx[kPD], rw0[kPD], rw1[kPD], rw2[kPD], rg[kPD];
         auto fetch = [&](int u, int k0) {
             const bool kok = k0 + 8 * h < p.d;  // d % 8 == 0: all eight or none
