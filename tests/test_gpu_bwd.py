@@ -98,3 +98,15 @@ def test_bwd_workload_sampled(ar, oracle, variant, S):
     _, dw_sub = _run(ar, variant, S, hs, w, gs)
     check_rel(to_f64(dw_sub), ref_dw, 1e-5, "dw (token subset)")
     print(f"bwd {variant} S={S}: {stats}", flush=True)
+
+
+@pytest.mark.parametrize("variant,S,n_hist,q_begin,n_q,d", [(FULL, 1, 12, 4, 5, 128), (FULL, 1, 49, 17, 32, 256),
+                                                            (FULL, 1, 70, 40, 30, 64),
+                                                            (FULL, 1, 40, 0, 40, 136),
+                                                            (BLOCK, 4, 30, 9, 21, 128)])
+def test_bwd_read_subsets_bf16(ar, oracle, variant, S, n_hist, q_begin, n_q, d):
+    # bf16 history and dout: the matrix-core scores path (Full, <= 64 reads),
+    # with reads that start past row 0 and row tiles the first read tile skips
+    h, w, g = _case(n_hist, 11, d, seed=q_begin * 5 + n_q + d, dtype="bf16", n_q=n_q,
+                    q_begin=q_begin)
+    _check(ar, oracle, variant, S, h, w, g, "bf16", q_begin=q_begin)
