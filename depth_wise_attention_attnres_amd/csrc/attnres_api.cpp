@@ -420,12 +420,13 @@ int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dt
     p.ws_c3 = reinterpret_cast<float*>(ws + L.off_c3);
     p.ws_kappa = reinterpret_cast<float*>(ws + L.off_kappa);
     p.ws_dwpart = reinterpret_cast<float*>(ws + L.off_dwpart);
+    p.ws_dwstage = reinterpret_cast<float*>(ws + L.off_dwstage);
     if (n_q == 0) {
         // no read: every history row gets a zero gradient
         return hip_status(fn, attnres::launch_fill_zero(
                                   dhist, n_hist * T * d * (dhist_dtype == ATTNRES_BF16 ? 2 : 4), stream));
     }
-    return hip_status(fn, attnres::launch_bwd(p, (int)L.n_chunks, stream));
+    return hip_status(fn, attnres::launch_bwd(p, (int)L.n_chunks, (int)L.n_dw_groups, stream));
 }
 
 }  // extern "C"

@@ -34,7 +34,8 @@
 //               per-chunk partial dw for tiles of 32 reads on the matrix cores
 //               (fp32 MFMA), the chunk's (token, row) pairs streamed through a
 //               prefetch ring.
-//   bwd_dw_sum  fixed-order sum of the partials (bitwise reproducible).
+//   bwd_dw_sum  fixed-order sum of the partials in two stages, groups of
+//               chunks then the groups (bitwise reproducible).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -927,12 +928,26 @@ __global__ __launch_bounds__(64) void bwd_dw_part_kernel(BwdParams p) {
     }
 }
 
-__global__ __launch_bounds__(256) void bwd_dw_sum_kernel(BwdParams p, int n_chunks) {
+// dw = sum of the per-chunk partials, in two fixed-order stages (bitwise
+// reproducible): groups of consecutive chunks in parallel, then the groups.
+__global__ __launch_bounds__(256) void bwd_dw_sum_kernel(BwdParams p, int n_chunks, int groups) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)p.n_q * p.d;
+    if (idx >= total) return;
+    const int per = (n_chunks + groups - 1) / groups;
+    const int c0 = blockIdx.y * per;
+    const int c1 = c0 + per < n_chunks ? c0 + per : n_chunks;
+    float s = 0.f;
+    for (int c = c0; c < c1; ++c) s += p.ws_dwpart[(int64_t)c * total + idx];
+    p.ws_dwstage[(int64_t)blockIdx.y * total + idx] = s;
+}
+
+__global__ __launch_bounds__(256) void bwd_dw_final_kernel(BwdParams p, int groups) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = (int64_t)p.n_q * p.d;
     if (idx >= total) return;
     float s = 0.f;
-    for (int c = 0; c < n_chunks; ++c) s += p.ws_dwpart[(int64_t)c * total + idx];
+    for (int g = 0; g < groups; ++g) s += p.ws_dwstage[(int64_t)g * total + idx];
     p.dw[idx] = s;
 }
 
@@ -975,6 +990,8 @@ BwdLayout bwd_layout(int64_t S, int64_t n_hist, int64_t T, int64_t d, int64_t n_
     L.off_kappa = take(T * n_q);
     L.off_dwpart = take(L.n_chunks * n_q * d);
     L.off_wsplit = take((3 * n_q * d + 1) / 2);  // bf16
+    L.n_dw_groups = L.n_chunks < 16 ? L.n_chunks : 16;
+    L.off_dwstage = take(L.n_dw_groups * n_q * d);
     L.bytes = off;
     return L;
 }
@@ -1048,7 +1065,7 @@ hipError_t launch_scores(const BwdParams& p, hipStream_t stream) {
 }
 
 template <typename TI, typename TG, typename TO>
-hipError_t launch_rest(const BwdParams& p, int n_chunks, hipStream_t stream) {
+hipError_t launch_rest(const BwdParams& p, int n_chunks, int groups, hipStream_t stream) {
     const unsigned slices = (unsigned)((p.d + kSlice - 1) / kSlice);
     if (p.n_hist <= 8)
         hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 8, 4>), dim3((unsigned)(p.T * slices)), dim3(64),
@@ -1065,32 +1082,36 @@ hipError_t launch_rest(const BwdParams& p, int n_chunks, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = (int64_t)p.n_q * p.d;
-    hipLaunchKernelGGL(bwd_dw_sum_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       stream, p, n_chunks);
+    hipLaunchKernelGGL(bwd_dw_sum_kernel, dim3((unsigned)((total + 255) / 256), (unsigned)groups),
+                       dim3(256), 0, stream, p, n_chunks, groups);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dw_final_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, p, groups);
     return hipGetLastError();
 }
 
 template <typename TI, typename TG>
-hipError_t dispatch_out(const BwdParams& p, int n_chunks, hipStream_t stream) {
-    return p.dhist_dt == ATTNRES_BF16 ? launch_rest<TI, TG, bf16_t>(p, n_chunks, stream)
-                                      : launch_rest<TI, TG, float>(p, n_chunks, stream);
+hipError_t dispatch_out(const BwdParams& p, int n_chunks, int groups, hipStream_t stream) {
+    return p.dhist_dt == ATTNRES_BF16 ? launch_rest<TI, TG, bf16_t>(p, n_chunks, groups, stream)
+                                      : launch_rest<TI, TG, float>(p, n_chunks, groups, stream);
 }
 
 template <typename TI, typename TG>
-hipError_t run_bwd(const BwdParams& p, int n_chunks, hipStream_t stream) {
+hipError_t run_bwd(const BwdParams& p, int n_chunks, int groups, hipStream_t stream) {
     hipError_t e = launch_scores<TI, TG>(p, stream);
     if (e != hipSuccess) return e;
-    return dispatch_out<TI, TG>(p, n_chunks, stream);
+    return dispatch_out<TI, TG>(p, n_chunks, groups, stream);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdParams& p, int n_chunks, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p, int n_chunks, int groups, hipStream_t stream) {
     if (p.hist_dt == ATTNRES_BF16)
-        return p.dout_dt == ATTNRES_BF16 ? run_bwd<bf16_t, bf16_t>(p, n_chunks, stream)
-                                         : run_bwd<bf16_t, float>(p, n_chunks, stream);
-    return p.dout_dt == ATTNRES_BF16 ? run_bwd<float, bf16_t>(p, n_chunks, stream)
-                                     : run_bwd<float, float>(p, n_chunks, stream);
+        return p.dout_dt == ATTNRES_BF16 ? run_bwd<bf16_t, bf16_t>(p, n_chunks, groups, stream)
+                                         : run_bwd<bf16_t, float>(p, n_chunks, groups, stream);
+    return p.dout_dt == ATTNRES_BF16 ? run_bwd<float, bf16_t>(p, n_chunks, groups, stream)
+                                     : run_bwd<float, float>(p, n_chunks, groups, stream);
 }
 
 }  // namespace attnres

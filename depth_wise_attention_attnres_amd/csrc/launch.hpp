@@ -55,7 +55,8 @@ struct BwdLayout {
     int64_t n_blk;     // v_0 + every block, complete or not
     int64_t nx;        // most sources a read can see
     int64_t n_chunks;  // token chunks of the dw partial sums
-    int64_t off_a1, off_a2, off_a2t, off_c3, off_kappa, off_dwpart, off_wsplit;
+    int64_t n_dw_groups;  // chunk groups of the first dw reduction stage
+    int64_t off_a1, off_a2, off_a2t, off_c3, off_kappa, off_dwpart, off_wsplit, off_dwstage;
     int64_t bytes;
 };
 BwdLayout bwd_layout(int64_t S, int64_t n_hist, int64_t T, int64_t d, int64_t n_q);
@@ -77,9 +78,10 @@ struct BwdParams {
     float* ws_c3;       // [T][n_blk]      sum over reads of ds r^2 s / d per v_0 / block
     float* ws_kappa;    // [T][n_q]        ds r^2 s / d of each read's partial sum
     float* ws_dwpart;   // [n_chunks][n_q][d]
+    float* ws_dwstage;  // [n_dw_groups][n_q][d]
     uint16_t* ws_wsplit;  // [3][n_q][d] bf16: w = hi + mid + lo (matrix-core scores)
 };
-hipError_t launch_bwd(const BwdParams& p, int n_chunks, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int n_chunks, int n_dw_groups, hipStream_t stream);
 
 // Block AttnRes in model order (block_model.hip)
 struct Phase1Params {
