@@ -90,6 +90,44 @@ def cpu_baseline(wl, hist, w, target_s: float = 15.0):
     }
 
 
+PROFILE_WORKLOADS = {
+    "block_S8_d2048_128k": "Block AttnRes two-phase forward, all 65 reads in one call, S=8",
+    "block_S8_d2048_128k_model_order": "Block AttnRes S=8 in model order (phase 1 per group, phase 2 per row)",
+}
+
+
+def profile_run(name):
+    """One history copy (calibration), then the workload twice, for counters."""
+    import torch
+    import depth_wise_attention_attnres_amd as ar
+    from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS["block_S8_d2048_128k"]
+    h, w, _ = device_inputs(wl, dev)
+    n, T, d = h.shape
+    dst = torch.empty_like(h)
+    dst.copy_(h)
+    del dst
+    out = torch.empty_like(h)
+    lse = torch.empty((n, T), dtype=torch.float32, device=dev)
+    if name == "block_S8_d2048_128k":
+        fn = lambda: ar.block_fwd(h, w, wl.S, out=out, lse=lse)
+    else:
+        S = wl.S
+        n_blk = 1 + (n - 1) // S
+        st = {"blocks": torch.empty((n_blk, T, d), dtype=torch.float32, device=dev),
+              "partial": torch.empty((T, d), dtype=torch.float32, device=dev),
+              "rs": torch.empty((n_blk, T), dtype=torch.float32, device=dev),
+              "o": torch.empty((S, T, d), dtype=torch.float32, device=dev),
+              "lse1": torch.empty((S, T), dtype=torch.float32, device=dev)}
+        fn = lambda: ar.block_model_order(h, w, S, out=out, lse=lse, state=st)
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    print(f"profile run done: {name} ({PROFILE_WORKLOADS[name]}), history copy "
+          f"{h.numel() * h.element_size()} bytes", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,15 +136,22 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the Block 128K and forward+backward measurements")
+    ap.add_argument("--profile", choices=sorted(PROFILE_WORKLOADS),
+                    help="for rocprofv3: copy the workload's history once (a transfer of known "
+                         "size that calibrates the HBM counters), run the workload twice, exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the AttnRes aggregation "
-              "is per-token independent and this build has no multi-GPU path.", file=sys.stderr)
+              "is per-token independent and the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
     import depth_wise_attention_attnres_amd as ar
     from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs
+
+    if args.profile:
+        profile_run(args.profile)
+        return
 
     wl = WORKLOADS[WORKLOAD]
     dev = torch.device("cuda:0")

@@ -41,12 +41,20 @@ def main():
     ap.add_argument("--write")
     ap.add_argument("--stats-only", metavar="TITLE",
                     help="write profiles/<name>.md with the kernel-trace table only")
+    ap.add_argument("--kernel-summary", metavar="TITLE",
+                    help="write profiles/<name>.md for the kernels matching --kernel of a "
+                         "bench.py --profile run: trace, HBM counters per dispatch, SQ counters")
+    ap.add_argument("--copy-bytes", type=float, help="bytes read (= written) by the calibration copy")
+    ap.add_argument("--alg-bytes", type=float, help="algorithmic bytes of one run of the workload")
+    ap.add_argument("--sq", nargs="*", default=[], help="counter CSVs of SQ passes")
     ap.add_argument("--name", default="full_fwd_stream_L32_d896")
     ap.add_argument("--kernel", default="full_fwd_stream_kernel")
     ap.add_argument("--commands", default="", help="text of the commands that made the CSVs")
     args = ap.parse_args()
     if args.stats_only:
         return stats_only(args)
+    if args.kernel_summary:
+        return kernel_summary(args)
     if not (args.fetch and args.write):
         raise SystemExit("--fetch and --write are required (or use --stats-only)")
 
@@ -141,6 +149,63 @@ def main():
     with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(rec, indent=1))
+
+
+def kernel_summary(args):
+    """Trace, HBM traffic and SQ counters of the kernels (matching --kernel) of
+    one run of a workload; counters are scaled by the calibration copy."""
+    def sel(path):
+        return [r for r in rows(path) if any(k in r["Kernel_Name"] for k in args.kernel.split(","))]
+
+    def per_dispatch(path):
+        rs = rows(path)
+        cp = [float(r["Counter_Value"]) * 1024 for r in rs if "copyBuffer" in r["Kernel_Name"]
+              or "copy" in r["Kernel_Name"].lower() and "attnres" not in r["Kernel_Name"]]
+        if not cp:
+            raise SystemExit(f"{path}: no calibration copy dispatch")
+        factor = args.copy_bytes / max(cp)
+        by = {}
+        for r in sel(path):
+            by.setdefault(int(r["Dispatch_Id"]), 0.0)
+            by[int(r["Dispatch_Id"])] += float(r["Counter_Value"]) * 1024 * factor
+        ids = sorted(by)
+        half = ids[len(ids) // 2:]  # the second of the two runs
+        return factor, sum(by[i] for i in half)
+
+    f_fac, fetched = per_dispatch(args.fetch)
+    w_fac, written = per_dispatch(args.write)
+    st = [r for r in rows(args.trace_stats) if any(k in r["Name"] for k in args.kernel.split(","))]
+    total_ns = sum(float(r["TotalDurationNs"]) for r in st) / 2  # per run (two runs)
+    lines = [f"# {args.name}: {args.kernel_summary}", "",
+             "Commands (run from /tmp with TMPDIR=/tmp on the GPU box; $R = the repo root):", "",
+             "```", args.commands.strip(), "```", "",
+             "## rocprofv3 --kernel-trace --stats", "",
+             "| kernel | calls | average ns | total ns |", "|---|---|---|---|"]
+    for r in st:
+        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['TotalDurationNs']):.0f} |")
+    gbs = args.alg_bytes / (total_ns * 1e-9) / 1e9
+    lines += ["", f"One run: {total_ns / 1e6:.2f} ms of kernel time; algorithmic bytes "
+              f"{args.alg_bytes / 1e9:.2f} GB -> {gbs:.0f} GB/s = {gbs / 80:.1f}% of 8 TB/s.", "",
+              "## HBM traffic of one run (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+              f"Calibration on the history copy ({args.copy_bytes / 1e9:.2f} GB read and written): "
+              f"FETCH_SIZE x {f_fac:.3f}, WRITE_SIZE x {w_fac:.3f}.", "",
+              f"Fetched {fetched / 1e9:.2f} GB, written {written / 1e9:.2f} GB, together "
+              f"{(fetched + written) / args.alg_bytes:.3f} x the algorithmic bytes."]
+    if args.sq:
+        agg = {}
+        waves = 0.0
+        for path in args.sq:
+            for r in sel(path):
+                agg[r["Counter_Name"]] = agg.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        waves = agg.get("SQ_WAVES", 0.0)
+        lines += ["", "## SQ counters (both runs; per wave where it applies)", "",
+                  "| counter | total | per wave |", "|---|---|---|"]
+        for k in sorted(agg):
+            lines.append(f"| {k} | {agg[k]:.4g} | {agg[k] / waves if waves else 0:.1f} |")
+    with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def stats_only(args):
