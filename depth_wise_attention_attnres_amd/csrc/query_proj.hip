@@ -6,7 +6,8 @@
 //   A[i][k] = x[token t0 + i][k]   (lane j: token j % 32, k = 8 (j / 32) .. + 7)
 //   B[k][n] = W[output o0 + n][k]  (lane j: output j % 32, same k)
 // so both operands are 8 consecutive k of one row.  bf16 x bf16 products are
-// exact in fp32; the accumulators are folded into fp32 totals every 16 steps.
+// exact in fp32 and each accumulator is one fp32 chain over d / 16 <= 256
+// steps, so its rounding is that of a plain fp32 sum of d terms.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -19,11 +20,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Workgroup tile: 128 tokens x 128 outputs; wave (wr, wc) of the 2 x 2 waves
 // computes 64 x 64 as 2 x 2 fragments of 32 x 32, so each operand fragment
-// read from LDS feeds two matrix instructions.  K goes in stages of 32
+// read from LDS feeds two matrix instructions.  K goes in stages of 64
 // elements through double-buffered LDS: the workgroup loads a stage's 128
 // token rows and 128 W rows (contiguous in k, 16 bytes per lane)
 // while it multiplies the previous stage; one barrier per stage.
-constexpr int kTileM = 128, kTileN = 128, kStageK = 32;
+constexpr int kTileM = 128, kTileN = 128, kStageK = 64;
 constexpr int kLdsRow = kStageK + 8;  // bf16 elements per LDS row (padded: staggers the banks)
 
 __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q,
@@ -76,20 +77,18 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
         }
     };
 
-    constexpr int kFold = 16;  // K-steps of 16 between folds into the fp32 totals
-    f32x16 acc[2][2], tot[2][2];
+    f32x16 acc[2][2];
 #pragma unroll
     for (int fa = 0; fa < 2; ++fa)
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[fa][fb][r] = tot[fa][fb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) acc[fa][fb][r] = 0.f;
 
     const int n_stages = (d + kStageK - 1) / kStageK;
     gload(0);
     lstore(0);
     __syncthreads();
-    int step = 0;  // K-steps of 16 done
     for (int st = 0; st < n_stages; ++st) {
         const int buf = st & 1;
         if (st + 1 < n_stages) gload((st + 1) * kStageK);
@@ -109,18 +108,6 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
 #pragma unroll
                 for (int fb = 0; fb < 2; ++fb)
                     acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_op[fa], fb_op[fb], acc[fa][fb], 0, 0, 0);
-            ++step;
-            if (step % kFold == 0) {
-#pragma unroll
-                for (int fa = 0; fa < 2; ++fa)
-#pragma unroll
-                    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            tot[fa][fb][r] += acc[fa][fb][r];
-                            acc[fa][fb][r] = 0.f;
-                        }
-            }
         }
         if (st + 1 < n_stages) {
             lstore(buf ^ 1);  // the other buffer: last read before the previous barrier
@@ -138,7 +125,7 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int64_t ti = t0 + 64 * wr + 32 * fa + 8 * (r / 4) + 4 * h + r % 4;
-                    if (ti < T) q[(j * T + ti) * d + out] = tot[fa][fb][r] + acc[fa][fb][r];
+                    if (ti < T) q[(j * T + ti) * d + out] = acc[fa][fb][r];
                 }
             }
         }
