@@ -1,0 +1,163 @@
+"""GPU parity of the Full forward for calls with many reads (run on an MI355X).
+
+A call with at least 16 reads whose rows fit in a workgroup's LDS is served by
+the kernel that stages each token's rows in LDS once (full_batch.hip); the
+shapes below are chosen to qualify (see ``_qualifies``), covering one to four
+16-byte chunks per lane, ragged last groups of reads (n_q not a multiple of 4),
+reads that start past row 0, the RMS cache, the fused pre-norm and the weight
+probe.  Every output is compared with the fp64 oracle; the full-size
+workloads compare a token sample, which is exact per token because tokens are
+independent."""
+import numpy as np
+import pytest
+import torch
+
+from parity import check_lse, check_out, check_rel, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+LDS_BYTES = 160 * 1024  # LDS a workgroup may hold on this part
+
+
+@pytest.fixture(scope="module")
+def ar():
+    import depth_wise_attention_attnres_amd as ar
+    return ar
+
+
+def _qualifies(n_rows, n_q, d, dtype):
+    """The rule the library applies: >= 16 reads, <= 4 (bf16) or 3 (fp32)
+    chunks of 8 per lane, and rows + scales + 8 score tables in LDS."""
+    elem = 2 if dtype == "bf16" else 4
+    n_pad = (n_rows + 3) // 4 * 4
+    lds = n_rows * d * elem + 4 * n_pad + 8 * 16 * n_pad + 16
+    nch = (d // 8 + 63) // 64
+    return n_q >= 16 and nch <= (4 if dtype == "bf16" else 3) and lds <= LDS_BYTES
+
+
+def _inputs(n_hist, T, d, seed, dtype, w_sigma=0.3):
+    rng = np.random.default_rng(seed)
+    hist = rng.standard_normal((n_hist, T, d)).astype(np.float32)
+    w = (rng.standard_normal((n_hist, d)) * w_sigma).astype(np.float32)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    h = torch.from_numpy(hist).to(DEV).to(tdt)
+    return h, torch.from_numpy(w).to(DEV), to_f64(h), w.astype(np.float64)
+
+
+# (n_hist, T, d): chunks per lane 1 (d=64, 200), 2 (520, 896, 1024), 3 (1032), 4 (2048)
+SHAPES = [(16, 37, 64), (19, 50, 200), (33, 70, 520), (21, 33, 1032), (18, 9, 2048),
+          (65, 40, 896), (49, 24, 1024)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_hist,T,d", SHAPES)
+def test_batch_all_reads(ar, oracle, dtype, n_hist, T, d):
+    if not _qualifies(n_hist, n_hist, d, dtype):
+        pytest.skip("rows do not fit in LDS at this dtype (the streaming kernel serves it)")
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=n_hist * 31 + d, dtype=dtype)
+    out, lse = ar.full_fwd(h, w)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.full_fwd(h64, w64)
+    check_out(to_f64(out), ref, dtype)
+    check_lse(to_f64(lse), ref_lse)
+
+
+@pytest.mark.parametrize("hdt,odt", [("bf16", "f32"), ("f32", "bf16")])
+def test_batch_mixed_dtypes(ar, oracle, hdt, odt):
+    h, w, h64, w64 = _inputs(23, 45, 136, seed=8, dtype=hdt)
+    out, _ = ar.full_fwd(h, w, out_dtype=torch.float32 if odt == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, _ = oracle.full_fwd(h64, w64)
+    check_out(to_f64(out), ref, odt)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_batch_q_begin_with_partly_valid_cache(ar, oracle, dtype):
+    # reads 5..24 of a 27-row history; rows 0..4 of the RMS cache come from an
+    # earlier call, rows 5..24 are formed and written by this one
+    n_hist, T, d = 27, 41, 264
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=13, dtype=dtype)
+    rinv = torch.full((n_hist, T), float("nan"), device=DEV)
+    ar.full_fwd(h, w[:5], q_begin=0, n_q=5, rinv=rinv)
+    out, lse = ar.full_fwd(h, w[5:25], q_begin=5, n_q=20, rinv=rinv, rinv_valid_rows=5)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.full_fwd(h64, w64[5:25], q_begin=5, n_q=20)
+    check_out(to_f64(out), ref, dtype)
+    check_lse(to_f64(lse), ref_lse)
+    r = to_f64(rinv)
+    assert np.isfinite(r[:25]).all() and np.isnan(r[25:]).all()  # rows past the last read untouched
+    r_ref = 1.0 / np.sqrt((h64[:25] ** 2).mean(axis=2) + 1e-6)
+    np.testing.assert_allclose(r[:25], r_ref, rtol=2e-6)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_gain", [False, True])
+def test_batch_prenorm(ar, oracle, dtype, with_gain):
+    n_hist, T, d = 22, 29, 520
+    h, w, hd, wd = _inputs(n_hist, T, d, seed=21, dtype=dtype)
+    gain = torch.from_numpy(np.random.default_rng(3).uniform(0.5, 1.5, (n_hist, d)).astype(np.float32)).to(DEV) \
+        if with_gain else None
+    out = torch.empty(h.shape, dtype=h.dtype, device=DEV)
+    normed = torch.empty_like(out)
+    ar.full_fwd(h, w, out=out, normed=normed, norm_gain=gain)
+    torch.cuda.synchronize()
+    ref, _ = oracle.full_fwd(hd, wd)
+    check_out(to_f64(out), ref, dtype)
+    check_out(to_f64(normed), oracle.prenorm(ref, None if gain is None else to_f64(gain)), dtype, what="normed")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("q_begin", [0, 2])
+def test_batch_alpha_probe(ar, oracle, dtype, q_begin):
+    n_hist, T, d = 21, 31, 264
+    h, w, hd, wd = _inputs(n_hist, T, d, seed=17 + q_begin, dtype=dtype, w_sigma=0.05)
+    n_q = n_hist - q_begin
+    w = w[q_begin:].contiguous()
+    alpha = torch.full((n_q, n_hist, T), float("nan"), device=DEV)
+    ar.full_fwd(h, w, q_begin=q_begin, alpha=alpha)
+    torch.cuda.synchronize()
+    _, _, ref = oracle.fwd(oracle.FULL, hd, wd[q_begin:], q_begin=q_begin, want_alpha=True)
+    a = to_f64(alpha)
+    check_rel(a, ref.transpose(0, 2, 1), 1e-5, "alpha")
+    assert (a >= 0).all()
+    np.testing.assert_allclose(a.sum(1), 1.0, atol=1e-5)
+    for j in range(n_q):
+        assert (a[j, q_begin + j + 1:] == 0).all()
+
+
+def test_batch_agrees_with_model_order(ar, oracle):
+    # the batched call and the read-by-read sweep (streaming kernel, RMS cache)
+    # compute the same function: both within the bar of the oracle on one input
+    n_hist, T, d = 40, 64, 896
+    h, w, hd, wd = _inputs(n_hist, T, d, seed=2, dtype="bf16", w_sigma=0.05)
+    ob, lb = ar.full_fwd(h, w)
+    rinv = torch.empty((n_hist, T), device=DEV)
+    om = torch.empty_like(h)
+    lm = torch.empty((n_hist, T), device=DEV)
+    for l in range(n_hist):
+        ar.full_fwd(h, w[l:l + 1], q_begin=l, n_q=1, rinv=rinv, rinv_valid_rows=l,
+                    out=om[l:l + 1], lse=lm[l:l + 1])
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.full_fwd(hd, wd)
+    check_out(to_f64(ob), ref, "bf16")
+    check_out(to_f64(om), ref, "bf16")
+    check_lse(to_f64(lb), ref_lse)
+    check_lse(to_f64(lm), ref_lse)
+
+
+@pytest.mark.parametrize("name", ["full_L32_d896", "fwdbwd_L24_d1024"])
+def test_batch_workload_sampled(ar, oracle, name):
+    # the full-size history in one call with every read, a token sample checked
+    from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs, token_sample
+    wl = WORKLOADS[name]
+    assert _qualifies(wl.n_hist, wl.n_hist, wl.d, wl.dtype)
+    h, w, _ = device_inputs(wl, DEV)
+    out, lse = ar.full_fwd(h, w)
+    torch.cuda.synchronize()
+    idx = token_sample(wl.T, 384, seed=wl.seed)
+    ti = torch.from_numpy(idx).to(DEV)
+    ref, ref_lse = oracle.full_fwd(to_f64(h.index_select(1, ti)), to_f64(w))
+    stats = check_out(to_f64(out.index_select(1, ti)), ref, wl.dtype)
+    check_lse(to_f64(lse.index_select(1, ti)), ref_lse)
+    print(f"{name} batched: {stats}", flush=True)
