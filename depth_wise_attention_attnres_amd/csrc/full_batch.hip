@@ -33,10 +33,50 @@ namespace attnres {
 namespace {
 
 constexpr int kBatchWaves = 8;
-constexpr int kBatchR = 4;  // reads per group: one f32x4 per row in the score table
+// Reads per group.  Groups of 8 halve the row visits but leave too few groups
+// to balance the waves (49 reads: 7 groups for 8 waves, the longest on the
+// critical path) and measured slower; 4 it is, one f32x4 per row of the
+// score table.
+constexpr int kBatchR = 4;
 // Fewer reads than this share too few rows to pay for the staging and would
 // leave most of the workgroup's waves without a group.
 constexpr int kBatchMinReads = 16;
+
+constexpr int kDppRor8 = 0x128;  // row_ror:8 (lanes i and i ^ 8 of a 16-lane row)
+constexpr int kDppShr4 = 0x114;  // row_shr:4 (lane i takes lane i - 4 of its row)
+
+// One transposing step of a multi-value lane reduction over lane bit B, with
+// DPP control CTRL pairing lane i with lane i ^ (1 << B): of each pair of
+// values (v[2j], v[2j+1]) a lane keeps the one its bit selects and sends the
+// other, so N values become N / 2, each summed over both lanes.
+template <int CTRL, int B, int N>
+__device__ __forceinline__ void transpose_step(float (&v)[N], float (&o)[N / 2], int ln) {
+    const bool hi = (ln >> B) & 1;
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+        const float keep = hi ? v[2 * j + 1] : v[2 * j];
+        const float send = hi ? v[2 * j] : v[2 * j + 1];
+        o[j] = keep + dpp<CTRL>(send);
+    }
+}
+
+// Sums over the wave of 4 values: value k ends in lane bits 0, 1 = k, and its
+// total is complete in lanes 4..7 (lane 4 + k holds value k).  The two
+// transposing steps cost 3 operations per pair where plain butterflies take
+// one DPP addition per value and level (15 operations instead of 32).
+__device__ __forceinline__ bool batch_holder(int ln) { return (ln & 0x3C) == 0x04; }
+
+__device__ __forceinline__ float wave_sum_transposed(float (&v)[4], int ln) {
+    float v2[2], v1[1];
+    transpose_step<kDppXor1, 0, 4>(v, v2, ln);
+    transpose_step<kDppXor2, 1, 2>(v2, v1, ln);
+    float x = v1[0];
+    x += dpp<kDppRor8>(x);  // lanes i and i ^ 8
+    x += dpp<kDppShr4>(x);  // lane i takes i - 4: complete where bit 2 is set
+    x = swap16_sum(x);
+    x = swap32_sum(x);
+    return x;
+}
 
 // 64-lane sums of R values, one DPP level at a time over all values so that
 // independent operations sit between the dependent ones
@@ -112,6 +152,7 @@ __host__ __device__ inline BatchLayout batch_layout(int n_rows, int n_pad, int d
 template <typename TI, typename TO, int NCH>
 __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams p, int n_rows, int n_pad) {
     constexpr int R = kBatchR;
+    constexpr int RV = R / 4;  // f32x4 per row of the score table
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     const BatchLayout L = batch_layout(n_rows, n_pad, p.d, (int)sizeof(TI));
     TI* const rows = reinterpret_cast<TI*>(lds_raw);
@@ -185,7 +226,8 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
     __syncthreads();
 
     // ---- groups of R reads ---------------------------------------------------
-    f32x4* const tab = reinterpret_cast<f32x4*>(lds_raw + L.tab_off) + (int64_t)wave * n_pad;
+    f32x4* const tab = reinterpret_cast<f32x4*>(lds_raw + L.tab_off) + (int64_t)wave * n_pad * RV;
+    float* const tabf = reinterpret_cast<float*>(tab);
     const int n_groups = (p.n_q + R - 1) / R;
     for (;;) {
         int idx = 0;
@@ -235,13 +277,10 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
 #pragma unroll
                         for (int e = 0; e < 8; ++e) dot[r] = fmaf(wv[r][c][e], x[e], dot[r]);
                 }
-                wave_sum_multi<R>(dot);
-                if (ln == 0) {
-                    const float ri = rs[i] * kLog2e;
-                    f32x4 s;
-#pragma unroll
-                    for (int r = 0; r < R; ++r) s[r] = (r < nr && i <= l0 + r) ? ri * dot[r] : -INFINITY;
-                    tab[i] = s;
+                const float tot = wave_sum_transposed(dot, ln);
+                if (batch_holder(ln)) {
+                    const int r = ln & 3;
+                    tabf[i * R + r] = (r < nr && i <= l0 + r) ? rs[i] * kLog2e * tot : -INFINITY;
                 }
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) cur[c] = nxt[c];
@@ -255,9 +294,12 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
 #pragma unroll
         for (int r = 0; r < R; ++r) M[r] = -INFINITY;
         for (int i = ln; i <= l_max; i += 64) {
-            const f32x4 s = tab[i];
 #pragma unroll
-            for (int r = 0; r < R; ++r) M[r] = fmaxf(M[r], s[r]);
+            for (int q = 0; q < RV; ++q) {
+                const f32x4 s = tab[i * RV + q];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) M[4 * q + r] = fmaxf(M[4 * q + r], s[r]);
+            }
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -266,24 +308,31 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
             Z[r] = 0.f;
         }
         for (int i = ln; i <= l_max; i += 64) {
-            const f32x4 s = tab[i];
 #pragma unroll
-            for (int r = 0; r < R; ++r) Z[r] += fast_exp2(s[r] - M[r]);
+            for (int q = 0; q < RV; ++q) {
+                const f32x4 s = tab[i * RV + q];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Z[4 * q + r] += fast_exp2(s[r] - M[4 * q + r]);
+            }
         }
         wave_sum_multi<R>(Z);
         float inv[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) inv[r] = r < nr ? 1.0f / Z[r] : 0.f;
         for (int i = ln; i <= l_max; i += 64) {
-            const f32x4 s = tab[i];
-            f32x4 a;
 #pragma unroll
-            for (int r = 0; r < R; ++r) a[r] = fast_exp2(s[r] - M[r]) * inv[r];
-            tab[i] = a;
-            if (p.alpha != nullptr) {
+            for (int q = 0; q < RV; ++q) {
+                const f32x4 s = tab[i * RV + q];
+                f32x4 a;
 #pragma unroll
-                for (int r = 0; r < R; ++r)
-                    if (r < nr) p.alpha[((int64_t)(j0 + r) * p.n_hist + i) * p.T + t] = a[r];
+                for (int r = 0; r < 4; ++r) a[r] = fast_exp2(s[r] - M[4 * q + r]) * inv[4 * q + r];
+                tab[i * RV + q] = a;
+                if (p.alpha != nullptr) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * q + r < nr)
+                            p.alpha[((int64_t)(j0 + 4 * q + r) * p.n_hist + i) * p.T + t] = a[r];
+                }
             }
         }
         if (p.alpha != nullptr) {  // sources a read does not see
@@ -319,7 +368,13 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
                     for (int c = 0; c < NCH; ++c)
                         if (live[c]) nxt[c].load(rows + (int64_t)(i + 1) * d, c * 64 + ln);
                 }
-                const f32x4 a = tab[i];
+                float a[R];
+#pragma unroll
+                for (int q = 0; q < RV; ++q) {
+                    const f32x4 a4 = tab[i * RV + q];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a[4 * q + r] = a4[r];
+                }
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
                     if (!live[c]) continue;

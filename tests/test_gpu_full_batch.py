@@ -28,7 +28,8 @@ def ar():
 
 def _qualifies(n_rows, n_q, d, dtype):
     """The rule the library applies: >= 16 reads, <= 4 (bf16) or 3 (fp32)
-    chunks of 8 per lane, and rows + scales + 8 score tables in LDS."""
+    chunks of 8 per lane, and rows + scales + 8 score tables of 4 floats per
+    row in LDS."""
     elem = 2 if dtype == "bf16" else 4
     n_pad = (n_rows + 3) // 4 * 4
     lds = n_rows * d * elem + 4 * n_pad + 8 * 16 * n_pad + 16
