@@ -295,6 +295,13 @@ def bwd_fmas_per_token(n_hist, n_q, S):
     return total
 
 
+def full_fwd_fmas_per_token(n_hist, n_q):
+    """Multiply-adds per token and per column of d of a Full forward with reads
+    0..n_q-1: a score dot and a weighted-sum term per (read, row), and one
+    squared norm per row."""
+    return n_hist + sum(2 * (l + 1) for l in range(n_q))
+
+
 def model_order_bytes_per_token(n, d, S, vb=2, ob=2):
     """HBM bytes per token of one model-order Block sweep (phase 1 per group:
     frozen fp32 sources read, new row and partial sum read, new block written,
@@ -314,8 +321,11 @@ def model_order_bytes_per_token(n, d, S, vb=2, ob=2):
 
 def extra_measurements(dev):
     """The other rows of the hot path at their workload sizes: the Block
-    two-phase forward over a 128K-token S=8 history (one call), and the Full
-    and Block (S=4) forward + backward of the L=24 / d=1024 workload."""
+    two-phase forward over a 128K-token S=8 history (one call, and in model
+    order), the Full forward with all reads in one call (L=32 / d=896 and
+    L=70 / d=640) and the L=70 model-order sweep, the input-dependent query,
+    and the Full and Block (S=4) forward + backward of the L=24 / d=1024
+    workload."""
     import torch
     import depth_wise_attention_attnres_amd as ar
     from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs
@@ -354,6 +364,45 @@ def extra_measurements(dev):
         "algorithmic_bytes": nbytes}
     del h, w, out, lse, st
     torch.cuda.empty_cache()
+
+    # Full forward with every read in one call (the rows are shared by the
+    # reads, so the call is bound by its arithmetic, not by HBM), and the
+    # deep-narrow L=70 / d=640 history in model order and in one call
+    for name, model_order in [("full_L32_d896", False), ("full_L70_d640", True),
+                              ("full_L70_d640", False)]:
+        wl = WORKLOADS[name]
+        h, w, _ = device_inputs(wl, dev)
+        n, T, d = h.shape
+        out = torch.empty_like(h)
+        lse = torch.empty((n, T), dtype=torch.float32, device=dev)
+        if model_order:
+            rinv = torch.empty((n, T), dtype=torch.float32, device=dev)
+
+            def sweep():
+                for l in range(n):
+                    ar.full_fwd(h, w[l:l + 1], q_begin=l, n_q=1, rinv=rinv, rinv_valid_rows=l,
+                                out=out[l:l + 1], lse=lse[l:l + 1])
+            ms = _time(sweep, stream, 5, 2)
+            nbytes = sum(read_bytes_per_token(l, d) for l in range(n)) * T
+            res[name + "_model_order"] = {
+                "what": f"Full AttnRes forward in model order ({n} calls, one read each, RMS cache)",
+                "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
+                "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "algorithmic_bytes": nbytes}
+            del rinv
+        else:
+            ms = _time(lambda: ar.full_fwd(h, w, out=out, lse=lse), stream, 5, 2)
+            flops = 2.0 * full_fwd_fmas_per_token(n, n) * d * T
+            nbytes = 2 * n * T * d * 2 + n * T * 4
+            res[name + "_batched"] = {
+                "what": f"Full AttnRes forward, all {n} reads in one call",
+                "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
+                "algorithmic_TFLOPs": flops / (ms * 1e-3) / 1e12,
+                "frac_of_fp32_vector_peak": flops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+        del h, w, out, lse
+        torch.cuda.empty_cache()
 
     # input-dependent query on the L=32 / d=896 history: the projection of every
     # read's newest row (one call, all reads) and the model-order sweep with a
@@ -407,6 +456,10 @@ def extra_measurements(dev):
             "fwd_ms": ms_f, "bwd_ms": ms_b,
             "fwd_bwd_tokens_per_s": T / ((ms_f + ms_b) * 1e-3),
             "fwd_algorithmic_GBps": (2 * n * T * d * 2) / (ms_f * 1e-3) / 1e9,
+            **({"fwd_algorithmic_TFLOPs": 2 * full_fwd_fmas_per_token(n, n) * d * T / (ms_f * 1e-3) / 1e12,
+                "fwd_frac_of_fp32_vector_peak":
+                    2 * full_fwd_fmas_per_token(n, n) * d * T / (ms_f * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+               if variant == ar.FULL else {}),
             # compulsory traffic of the backward: history and dout read, dhist written
             "bwd_algorithmic_GBps": (3 * n * T * d * 2) / (ms_b * 1e-3) / 1e9,
             "bwd_frac_of_hbm_peak": (3 * n * T * d * 2) / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
