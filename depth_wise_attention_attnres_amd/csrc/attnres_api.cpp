@@ -51,9 +51,9 @@ int check_common(const char* fn, const void* hist, int hist_dt, int64_t n_hist, 
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: d = %" PRId64 " exceeds %d", fn, d, attnres::kMaxD);
     if (n_hist > (int64_t)1 << 20)
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: n_hist = %" PRId64 " too large", fn, n_hist);
-    // grids hold up to T x (d / 256) workgroups in one dimension
-    if (T > ((int64_t)1 << 27))
-        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: T = %" PRId64 " exceeds 2^27 tokens", fn, T);
+    // grids hold up to 1024 work-items per token, in 32 bits
+    if (T > attnres::kMaxTokens)
+        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: T = %" PRId64 " exceeds 2^22 - 1 tokens per call", fn, T);
     // every element offset must fit int64 comfortably
     if (T > ((int64_t)1 << 40) / (n_hist * d))
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: history of %" PRId64 " x %" PRId64 " x %" PRId64 " too large",
@@ -193,9 +193,11 @@ int attnres_query_proj(const void* x, attnres_dtype x_dtype, int64_t n_q, int64_
     if (d > attnres::kMaxD) return fail(ATTNRES_ERR_UNSUPPORTED, "%s: d = %" PRId64 " exceeds %d", fn, d, attnres::kMaxD);
     if (x_dtype != ATTNRES_BF16 || w_dtype != ATTNRES_BF16)
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: only bf16 x and W (the matrix-core path)", fn);
-    if (T > ((int64_t)1 << 27)) return fail(ATTNRES_ERR_UNSUPPORTED, "%s: T exceeds 2^27 tokens", fn);
-    if (n_q * ((T + 127) / 128) * ((d + 127) / 128) >= ((int64_t)1 << 31))
-        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: too many tiles for one launch", fn);
+    if (T > attnres::kMaxTokens)
+        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: T = %" PRId64 " exceeds 2^22 - 1 tokens per call", fn, T);
+    // one 256-work-item workgroup per 128 x 128 tile, 32-bit work-item count
+    if (n_q * ((T + 127) / 128) * ((d + 127) / 128) >= ((int64_t)1 << 24))
+        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: too many tiles for one launch (n_q x T x d >= 2^38)", fn);
     if (n_q == 0 || T == 0) return ok();
     if (x == nullptr || W == nullptr || q == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     if (!aligned(x, 16) || !aligned(W, 16) || !aligned(q, 16))

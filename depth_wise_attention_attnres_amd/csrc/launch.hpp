@@ -10,6 +10,12 @@
 namespace attnres {
 
 constexpr int kMaxD = 4096;
+// Tokens per call.  A dispatch counts work-items per grid dimension in 32
+// bits, and the widest launches hold 1024 work-items per token (the backward's
+// dhist at d = 4096: 16 slices x 64 lanes; the batched and Block forwards: up
+// to 512), so T stays below 2^22.  Tokens are independent: larger inputs are
+// split by the caller.
+constexpr int64_t kMaxTokens = ((int64_t)1 << 22) - 1;
 // Block reads whose source count (v_0 + completed blocks) is at most this keep
 // their sources in registers (two-phase kernel); more blocks use the
 // streaming kernel, which forms block sums on the fly per read.

@@ -42,8 +42,10 @@
  *     the thread-local error string.  The backward's scratch is caller-supplied.
  *   * d must be a multiple of 8 (8 <= d <= 4096); hist, out, dout, dhist and w
  *     must be 16-byte aligned, lse / rinv / dw 4-byte aligned.
- *   * T <= 2^27 tokens and n_hist * T * d <= 2^40 elements per call
- *     (ATTNRES_ERR_UNSUPPORTED beyond).
+ *   * T < 2^22 tokens and n_hist * T * d <= 2^40 elements per call
+ *     (ATTNRES_ERR_UNSUPPORTED beyond: one launch counts its work-items in
+ *     32 bits).  Tokens are independent, so larger inputs are split by
+ *     tokens across calls (the backward's dw then sums over the calls).
  *   * Calls validate every argument on the host before any launch and return
  *     synchronously on error; on success the work is enqueued on `stream`
  *     (asynchronous).  Outputs must not alias inputs.

@@ -80,9 +80,9 @@ def test_full_fwd_validation(ar):
     assert _full(ar, normed=P + 8) == ALIGN
     assert _full(ar, normed=P, gain=P2 + 4) == ALIGN
     assert _full(ar, alpha=P + 2) == ALIGN
-    assert _full(ar, T=(1 << 27) + 1, d=8, n_hist=1, n_q=1) == UNSUPPORTED
-    assert "2^27" in ar.last_error()
-    assert _full(ar, T=1 << 27, d=8, n_hist=1, n_q=1, hist=None) == INVALID  # size accepted
+    assert _full(ar, T=1 << 22, d=8, n_hist=1, n_q=1) == UNSUPPORTED
+    assert "2^22" in ar.last_error()
+    assert _full(ar, T=(1 << 22) - 1, d=8, n_hist=1, n_q=1, hist=None) == INVALID  # size accepted
 
 
 def test_empty_calls_launch_nothing(ar):
@@ -238,6 +238,11 @@ def test_query_proj_and_full_fwd_q_validation(ar):
     assert lib.attnres_query_proj(P, BF16, 2, 16, 64, P2, BF16, P3 + 4, None) == ALIGN
     assert lib.attnres_query_proj(P, BF16, 0, 16, 64, None, BF16, None, None) == OK
     assert lib.attnres_query_proj(P, 7, 2, 16, 64, P2, BF16, P3, None) == INVALID
+    # one launch: at most 2^24 tiles of 128 x 128 (2^32 work-items), and T < 2^22
+    assert lib.attnres_query_proj(P, BF16, 64, 1 << 21, 4096, P2, BF16, P3, None) == UNSUPPORTED
+    assert "tiles" in ar.last_error()
+    assert lib.attnres_query_proj(P, BF16, 1, 1 << 22, 64, P2, BF16, P3, None) == UNSUPPORTED
+    assert "2^22" in ar.last_error()
     # hist, dt, n_hist, T, d, q, q_begin, n_q, eps, rinv, rvalid, out, out_dt, lse, stream
     assert lib.attnres_full_fwd_q(P, BF16, 4, 16, 64, None, 0, 4, 1e-6, None, 0, P3, BF16, None,
                                   None) == INVALID
