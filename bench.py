@@ -75,18 +75,37 @@ def cpu_baseline(wl, hist, w, target_s: float = 15.0):
         oracle.full_fwd(h64, w64)
         return time.perf_counter() - t0
 
-    probe_n = 128
-    t_probe = run(probe_n)
-    n = int(min(wl.T, max(probe_n, probe_n * target_s / max(t_probe, 1e-3))))
-    n = max(probe_n, (n // 64) * 64)
-    t = run(n)
+    def sized(target):
+        probe_n = 128
+        t_probe = run(probe_n)
+        n = int(min(wl.T, max(probe_n, probe_n * target / max(t_probe, 1e-3))))
+        n = max(probe_n, (n // 64) * 64)
+        return n, run(n)
+
+    cores = oracle.num_threads()
+    n, t = sized(target_s)
+    # the same oracle on one core, on a smaller sample (per-token cost is uniform)
+    oracle.set_num_threads(1)
+    try:
+        n1, t1 = sized(target_s / 3)
+    finally:
+        oracle.set_num_threads(cores)
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {
         "value": n / t,
         "unit": "tokens/s",
-        "cores": oracle.num_threads(),
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{n} of {wl.T} tokens of {wl.name} (all {wl.n_hist} reads per token, fp64, "
                   f"{t:.1f} s)",
+        "single_core": {"value": n1 / t1, "unit": "tokens/s", "cores": 1,
+                        "sample": f"{n1} tokens, {t1:.1f} s"},
+        "cpu_model": cpu_model,
     }
 
 

@@ -56,6 +56,8 @@ def _load():
     vp = ctypes.c_void_p
     lib.attnres_oracle_num_threads.restype = ip
     lib.attnres_oracle_num_threads.argtypes = []
+    lib.attnres_oracle_set_num_threads.restype = None
+    lib.attnres_oracle_set_num_threads.argtypes = [ip]
     lib.attnres_oracle_block_sources.restype = None
     lib.attnres_oracle_block_sources.argtypes = [i64, i64, ctypes.POINTER(i64),
                                                  ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -91,6 +93,11 @@ def _ptr(a: np.ndarray | None):
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS or all cores)."""
     return int(_load().attnres_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the following oracle calls (used to time it on one core)."""
+    _load().attnres_oracle_set_num_threads(int(n))
 
 
 def block_sources(l: int, S: int) -> tuple[int, int, int]:

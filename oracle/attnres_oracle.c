@@ -61,6 +61,15 @@ int attnres_oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the following calls (n >= 1); for timing on one core. */
+void attnres_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Block membership of read l: number of completed blocks m and the half-open
  * row range [part_begin, part_end) of the partial sum (empty when equal). */
 void attnres_oracle_block_sources(int64_t l, int64_t S, int64_t* m_out,
