@@ -151,6 +151,22 @@ def test_full_workload_model_order_sampled(ar, oracle, name):
     print(f"{name}: {stats}", flush=True)
 
 
+def test_full_workload_batched_streaming_sampled(ar, oracle):
+    # the L=70 / d=640 history in one call with all 141 reads: its rows do not
+    # fit in a workgroup's LDS, so the streaming kernel serves every read
+    from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs, token_sample
+    wl = WORKLOADS["full_L70_d640"]
+    h, w, _ = device_inputs(wl, DEV)
+    out, lse = ar.full_fwd(h, w)
+    torch.cuda.synchronize()
+    idx = token_sample(wl.T, 256, seed=wl.seed + 1)
+    ti = torch.from_numpy(idx).to(DEV)
+    ref, ref_lse = oracle.full_fwd(to_f64(h.index_select(1, ti)), to_f64(w))
+    stats = check_out(to_f64(out.index_select(1, ti)), ref, wl.dtype)
+    check_lse(to_f64(lse.index_select(1, ti)), ref_lse)
+    print(f"{wl.name} batched: {stats}", flush=True)
+
+
 # ---------------------------------------------------------------------------
 # fused pre-norm of the output (the sublayer's branch input RMSNorm_pre,l(h_l))
 
