@@ -20,9 +20,10 @@
 //   A1  partial sums of the chunk's reads (fp32), the next chunk's rows are
 //       then requested (the rows of this chunk are dead);
 //   A2  per-lane partial dots (queries double-buffered from L2), summed over
-//       each 16-lane row with DPP butterflies; each row's sums go to LDS;
+//       the wave by transposing reductions (groups of up to 8 values, one
+//       holder lane per value); each wave's sums go to its LDS slot;
 //   A3  every wave, one 16-lane row per read and one lane per source: adds
-//       the row sums (fixed order, so all waves agree bitwise), forms scores,
+//       the wave slots (fixed order, so all waves agree bitwise), forms scores,
 //       the phase-1 max and sum over the frozen sources, merges the partial
 //       sum by the log-sum-exp rule, and keeps each coefficient in the lane
 //       that computed it;
@@ -54,15 +55,49 @@ struct BlockState {
     int buf;              // which half of the row-sum buffer this chunk uses
 };
 
-// Shared-memory layout of one workgroup (nw waves, 4 * nw 16-lane rows): the
-// row sums of a chunk, double-buffered so that one barrier per chunk suffices
-// (a wave can only overwrite a half after every wave has passed the next
-// chunk's barrier, i.e. has finished reading it).
+// Shared-memory layout of one workgroup (nw waves): the wave sums of a chunk,
+// one slot per wave and value (slots padded to a multiple of 4 with zeros, so
+// that A3 adds whole f32x4; one slot per 16-lane row with 13 sources, see
+// block_wave_sums), double-buffered so that one barrier per chunk
+// suffices (a wave can only overwrite a half after every wave has passed the
+// next chunk's barrier, i.e. has finished reading it).
+__host__ __device__ constexpr int block_slots(int nw) { return nw <= 4 ? 4 : 8; }
+// The transposing wave reduction needs its groups of values in registers at
+// once; with 13 sources that pushes the kernel into spills (104 bytes per
+// lane, measured slower), so the 13-source variant keeps plain butterflies
+// over 16-lane rows with one slot per row (4 * nw slots).
+template <int NSRC>
+__host__ __device__ constexpr bool block_wave_sums() { return NSRC <= 9; }
+template <int NSRC>
+__host__ __device__ constexpr int block_slots_for(int nw) {
+    return block_wave_sums<NSRC>() ? block_slots(nw) : 4 * nw;
+}
+
 template <int NSRC, int CR>
 struct BlockShared {
-    int row_slots;  // 16-lane rows in the workgroup
-    float* part;    // [2][kVals][row_slots] row sums
+    int row_slots;  // wave slots per value (block_slots(nw))
+    float* part;    // [2][kVals][row_slots] wave sums
 };
+
+// Wave sums of the KV values of one read, stored to the wave's slots: values
+// 0..G are the frozen-source dots (slots 0..G), G + 1 the partial-sum dot
+// (slot NSRC), G + 2 its sum of squares (slot NSRC + 1).  Groups of up to 8
+// values share one transposing reduction.
+template <int G, int NSRC, int BASE, int KV>
+__device__ __forceinline__ void block_reduce_store(const float (&v)[KV], float* pp, int slots, int lane) {
+    constexpr int REM = KV - BASE;
+    constexpr int P = REM > 4 ? 8 : 4;
+    float g[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) g[j] = BASE + j < KV ? v[BASE + j < KV ? BASE + j : 0] : 0.f;
+    const float tot = wave_sum_transposed<P>(g, lane);
+    const int j = BASE + wave_sum_index<P>(lane);
+    if (wave_sum_holder<P>(lane) && j < KV) {
+        const int slot = j <= G ? j : (j == G + 1 ? NSRC : NSRC + 1);
+        pp[slot * slots] = tot;
+    }
+    if constexpr (REM > 8) block_reduce_store<G, NSRC, BASE + 8, KV>(v, pp, slots, lane);
+}
 
 // Everything one chunk does, for a chunk of block group G (sources 0..G).
 // l0: first read of the chunk, n: reads in the chunk, [nl0, nl1): next chunk.
@@ -79,7 +114,7 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
     const int kRowSlots = sh.row_slots;
     float* const part = sh.part + st.buf * kVals * kRowSlots;
     const int tid = threadIdx.x;
-    const int row_slot = tid >> 4;
+    const int wave = tid >> 6, lane = tid & 63;
     const int64_t row_elems = p.T * (int64_t)p.d;
     const uint64_t tok_in_bytes = (uint64_t)p.d * sizeof(TI);
     const int S = p.S;
@@ -141,15 +176,18 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
             }
     }
 
-    // ---- A2: partial dots, summed over 16-lane rows, into LDS --------------
-    // After the row butterfly all 16 lanes of a row hold the row's sum and all
-    // of them store it to the same LDS word.
+    // ---- A2: partial dots, summed over the wave, into the wave's LDS slots ---
     if (new_src) {
         float sq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) sq = fmaf(st.src[G][e], st.src[G][e], sq);
-        sq = tg_sum<16>(sq);
-        part[kSq * kRowSlots + row_slot] = sq;
+        if constexpr (block_wave_sums<NSRC>()) {
+            sq = tg_sum<64>(sq);
+            if (lane == 0) part[kSq * kRowSlots + wave] = sq;
+        } else {
+            sq = tg_sum<16>(sq);
+            part[kSq * kRowSlots + (tid >> 4)] = sq;
+        }
     }
 #pragma unroll
     for (int k = 0; k < CR; ++k) {
@@ -186,19 +224,25 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
                 v[G + 1] = dp;
                 v[G + 2] = sq;
             }
+            if constexpr (block_wave_sums<NSRC>()) {
+                block_reduce_store<G, NSRC, 0, kV>(v, part + k * kStride * kRowSlots + wave, kRowSlots, lane);
+            } else {
+                // all 16 lanes of a row hold the row's sum and store it to one word
+                // (one butterfly level at a time over all values)
 #pragma unroll
-            for (int c = 0; c < kV; ++c) v[c] += dpp<kDppXor1>(v[c]);
+                for (int c = 0; c < kV; ++c) v[c] += dpp<kDppXor1>(v[c]);
 #pragma unroll
-            for (int c = 0; c < kV; ++c) v[c] += dpp<kDppXor2>(v[c]);
+                for (int c = 0; c < kV; ++c) v[c] += dpp<kDppXor2>(v[c]);
 #pragma unroll
-            for (int c = 0; c < kV; ++c) v[c] += dpp<kDppHalfMirror>(v[c]);
+                for (int c = 0; c < kV; ++c) v[c] += dpp<kDppHalfMirror>(v[c]);
 #pragma unroll
-            for (int c = 0; c < kV; ++c) v[c] += dpp<kDppMirror>(v[c]);
-            float* pp = part + k * kStride * kRowSlots + row_slot;
+                for (int c = 0; c < kV; ++c) v[c] += dpp<kDppMirror>(v[c]);
+                float* pp = part + k * kStride * kRowSlots + (tid >> 4);
 #pragma unroll
-            for (int c = 0; c <= G; ++c) pp[c * kRowSlots] = v[c];
-            pp[NSRC * kRowSlots] = v[G + 1];
-            pp[(NSRC + 1) * kRowSlots] = v[G + 2];
+                for (int c = 0; c <= G; ++c) pp[c * kRowSlots] = v[c];
+                pp[NSRC * kRowSlots] = v[G + 1];
+                pp[(NSRC + 1) * kRowSlots] = v[G + 2];
+            }
         }
     }
     __syncthreads();
@@ -212,7 +256,6 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
     static_assert(CR <= 4 && NSRC + 1 <= 16, "one 16-lane row per read");
     float cv = 0.f;  // coefficient of (read k, source c)
     {
-        const int lane = tid & 63;
         const int k = lane >> 4, c = lane & 15;
         const int l = l0 + k;
         const bool read_ok = k < n && l >= p.q_begin;
@@ -312,12 +355,18 @@ __device__ __forceinline__ void block_chunk_dispatch(int g, const BlockFwdParams
 template <typename TI, int NSRC, int CR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void block_fwd_twophase_kernel(BlockFwdParams p) {
-    const int kRowSlots = blockDim.x / 16;
+    const int nw = blockDim.x / 64;
+    const int kRowSlots = block_slots_for<NSRC>(nw);
 
     extern __shared__ float lds[];
     BlockShared<NSRC, CR> sh;
     sh.row_slots = kRowSlots;
     sh.part = lds;
+    if (nw < kRowSlots) {  // padding slots: never written, read as zeros by A3
+        constexpr int kVals = BlockLds<NSRC, CR>::kVals;
+        for (int i = threadIdx.x; i < 2 * kVals * kRowSlots; i += blockDim.x)
+            if (i % kRowSlots >= nw) lds[i] = 0.f;
+    }
 
     const int ln = threadIdx.x;                   // chunk index of d owned by this lane
     const int64_t t = blockIdx.x;                 // token
@@ -383,7 +432,7 @@ namespace {
 template <typename TI, int NSRC, int CR>
 hipError_t launch_twophase(const BlockFwdParams& p, int nw, hipStream_t stream) {
     constexpr int kVals = BlockLds<NSRC, CR>::kVals;
-    const size_t lds = sizeof(float) * 2 * kVals * 4 * nw;
+    const size_t lds = sizeof(float) * 2 * kVals * block_slots_for<NSRC>(nw);
     hipLaunchKernelGGL((block_fwd_twophase_kernel<TI, NSRC, CR>), dim3((unsigned)p.T),
                        dim3(64 * nw), lds, stream, p);
     return hipGetLastError();

@@ -190,6 +190,59 @@ __device__ __forceinline__ float tg_max(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------------------
+// sums over the wave of several values at once.  A transposing step over lane
+// bit B (DPP control CTRL pairs lane i with lane i ^ (1 << B)): of each pair
+// of values (v[2j], v[2j+1]) a lane keeps the one its bit selects and sends
+// the other, so N values become N / 2, each summed over both lanes -- three
+// operations per pair where plain butterflies take one per value and level.
+
+constexpr int kDppRor8 = 0x128;  // row_ror:8 (lanes i and i ^ 8 of a 16-lane row)
+constexpr int kDppShr4 = 0x114;  // row_shr:4 (lane i takes lane i - 4 of its row)
+
+template <int CTRL, int B, int N>
+__device__ __forceinline__ void transpose_step(const float (&v)[N], float (&o)[N / 2], int lane) {
+    const bool hi = (lane >> B) & 1;
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+        const float keep = hi ? v[2 * j + 1] : v[2 * j];
+        const float send = hi ? v[2 * j] : v[2 * j + 1];
+        o[j] = keep + dpp<CTRL>(send);
+    }
+}
+
+// Wave sums of P in {4, 8} values: value k ends in lane bits 0, 1 (and 3 when
+// P = 8) equal to k; its total is complete in the lanes with bit 2 set and
+// bits 4, 5 (and 3 when P = 4) clear: lanes 4..7 (and 12..15).
+template <int P>
+__device__ __forceinline__ bool wave_sum_holder(int lane) {
+    return (lane & (P == 8 ? 0x34 : 0x3C)) == 0x04;
+}
+template <int P>
+__device__ __forceinline__ int wave_sum_index(int lane) {
+    return P == 8 ? (lane & 3) | (((lane >> 3) & 1) << 2) : (lane & 3);
+}
+template <int P>
+__device__ __forceinline__ float wave_sum_transposed(const float (&v)[P], int lane) {
+    static_assert(P == 4 || P == 8, "4 or 8 values");
+    float v2[P / 2], v1[P / 4];
+    transpose_step<kDppXor1, 0, P>(v, v2, lane);
+    transpose_step<kDppXor2, 1, P / 2>(v2, v1, lane);
+    float x;
+    if constexpr (P == 8) {
+        float v0[1];
+        transpose_step<kDppRor8, 3, 2>(v1, v0, lane);
+        x = v0[0];
+    } else {
+        x = v1[0];
+        x += dpp<kDppRor8>(x);  // lanes i and i ^ 8
+    }
+    x += dpp<kDppShr4>(x);  // lane i takes i - 4: complete where bit 2 is set
+    x = swap16_sum(x);
+    x = swap32_sum(x);
+    return x;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }

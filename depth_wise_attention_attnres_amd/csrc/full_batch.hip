@@ -42,42 +42,6 @@ constexpr int kBatchR = 4;
 // leave most of the workgroup's waves without a group.
 constexpr int kBatchMinReads = 16;
 
-constexpr int kDppRor8 = 0x128;  // row_ror:8 (lanes i and i ^ 8 of a 16-lane row)
-constexpr int kDppShr4 = 0x114;  // row_shr:4 (lane i takes lane i - 4 of its row)
-
-// One transposing step of a multi-value lane reduction over lane bit B, with
-// DPP control CTRL pairing lane i with lane i ^ (1 << B): of each pair of
-// values (v[2j], v[2j+1]) a lane keeps the one its bit selects and sends the
-// other, so N values become N / 2, each summed over both lanes.
-template <int CTRL, int B, int N>
-__device__ __forceinline__ void transpose_step(float (&v)[N], float (&o)[N / 2], int ln) {
-    const bool hi = (ln >> B) & 1;
-#pragma unroll
-    for (int j = 0; j < N / 2; ++j) {
-        const float keep = hi ? v[2 * j + 1] : v[2 * j];
-        const float send = hi ? v[2 * j] : v[2 * j + 1];
-        o[j] = keep + dpp<CTRL>(send);
-    }
-}
-
-// Sums over the wave of 4 values: value k ends in lane bits 0, 1 = k, and its
-// total is complete in lanes 4..7 (lane 4 + k holds value k).  The two
-// transposing steps cost 3 operations per pair where plain butterflies take
-// one DPP addition per value and level (15 operations instead of 32).
-__device__ __forceinline__ bool batch_holder(int ln) { return (ln & 0x3C) == 0x04; }
-
-__device__ __forceinline__ float wave_sum_transposed(float (&v)[4], int ln) {
-    float v2[2], v1[1];
-    transpose_step<kDppXor1, 0, 4>(v, v2, ln);
-    transpose_step<kDppXor2, 1, 2>(v2, v1, ln);
-    float x = v1[0];
-    x += dpp<kDppRor8>(x);  // lanes i and i ^ 8
-    x += dpp<kDppShr4>(x);  // lane i takes i - 4: complete where bit 2 is set
-    x = swap16_sum(x);
-    x = swap32_sum(x);
-    return x;
-}
-
 // 64-lane sums of R values, one DPP level at a time over all values so that
 // independent operations sit between the dependent ones
 template <int R>
@@ -277,8 +241,8 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
 #pragma unroll
                         for (int e = 0; e < 8; ++e) dot[r] = fmaf(wv[r][c][e], x[e], dot[r]);
                 }
-                const float tot = wave_sum_transposed(dot, ln);
-                if (batch_holder(ln)) {
+                const float tot = wave_sum_transposed<4>(dot, ln);
+                if (wave_sum_holder<4>(ln)) {
                     const int r = ln & 3;
                     tabf[i * R + r] = (r < nr && i <= l0 + r) ? rs[i] * kLog2e * tot : -INFINITY;
                 }
