@@ -112,6 +112,7 @@ def cpu_baseline(wl, hist, w, target_s: float = 15.0):
 PROFILE_WORKLOADS = {
     "block_S8_d2048_128k": "Block AttnRes two-phase forward, all 65 reads in one call, S=8",
     "block_S8_d2048_128k_model_order": "Block AttnRes S=8 in model order (phase 1 per group, phase 2 per row)",
+    "full_L32_d896_batched": "Full AttnRes forward, all 65 reads in one call (rows staged in LDS)",
 }
 
 
@@ -121,7 +122,7 @@ def profile_run(name):
     import depth_wise_attention_attnres_amd as ar
     from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs
     dev = torch.device("cuda:0")
-    wl = WORKLOADS["block_S8_d2048_128k"]
+    wl = WORKLOADS["full_L32_d896" if name == "full_L32_d896_batched" else "block_S8_d2048_128k"]
     h, w, _ = device_inputs(wl, dev)
     n, T, d = h.shape
     dst = torch.empty_like(h)
@@ -129,7 +130,9 @@ def profile_run(name):
     del dst
     out = torch.empty_like(h)
     lse = torch.empty((n, T), dtype=torch.float32, device=dev)
-    if name == "block_S8_d2048_128k":
+    if name == "full_L32_d896_batched":
+        fn = lambda: ar.full_fwd(h, w, out=out, lse=lse)
+    elif name == "block_S8_d2048_128k":
         fn = lambda: ar.block_fwd(h, w, wl.S, out=out, lse=lse)
     else:
         S = wl.S
