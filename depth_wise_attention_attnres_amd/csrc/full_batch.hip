@@ -6,11 +6,14 @@
 // history, and that working set -- rows x d per token, for the thousands of
 // tokens in flight -- does not stay in L2.  This kernel brings every row of
 // a token from HBM once, into LDS, and serves all of the token's reads from
-// there.
+// there.  When a token's rows exceed the LDS a workgroup may hold, the first
+// n_lds rows are staged and the rest (needed only by the last groups of
+// reads) are read from global memory in both passes.
 //
 // Mapping: one workgroup of kBatchWaves waves per token.
-//   prologue  the waves copy rows 0..l_max into LDS (input type, row-major,
-//             16-byte chunks along d) and form each row's RMS scale r_i: from
+//   prologue  the waves copy rows 0..n_lds-1 into LDS (input type, row-major,
+//             16-byte chunks along d) and form the RMS scale r_i of every row
+//             0..l_max: from
 //             the caller's cache when the row is valid there, else from the
 //             row's sum of squares (then written to the cache);
 //   groups    the reads are cut into groups of R consecutive reads, which the
@@ -67,6 +70,9 @@ template <> struct LdsChunk<bf16_t> {
     __device__ __forceinline__ void load(const bf16_t* row, int ch) {
         v = *reinterpret_cast<const u32x4*>(row + 8 * ch);
     }
+    __device__ __forceinline__ void load_global(rsrc_t r, uint32_t off) {
+        v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    }
     __device__ __forceinline__ void to_float(float (&f)[8]) const {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -80,6 +86,10 @@ template <> struct LdsChunk<float> {
     __device__ __forceinline__ void load(const float* row, int ch) {
         a = *reinterpret_cast<const u32x4*>(row + 8 * ch);
         b = *reinterpret_cast<const u32x4*>(row + 8 * ch + 4);
+    }
+    __device__ __forceinline__ void load_global(rsrc_t r, uint32_t off) {
+        a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
     }
     __device__ __forceinline__ void to_float(float (&f)[8]) const {
 #pragma unroll
@@ -98,14 +108,14 @@ __device__ __forceinline__ void store_raw(float* row, int ch, const Chunk<float>
     *reinterpret_cast<u32x4*>(row + 8 * ch + 4) = c.b;
 }
 
-// LDS layout of one workgroup: rows [n_rows][d] (input type), the RMS scales
+// LDS layout of one workgroup: rows [n_lds][d] (input type), the RMS scales
 // [n_pad], kBatchWaves score tables [n_pad][R], the group counter.
 struct BatchLayout {
     int64_t rows_bytes, rs_off, tab_off, counter_off, bytes;
 };
-__host__ __device__ inline BatchLayout batch_layout(int n_rows, int n_pad, int d, int elem) {
+__host__ __device__ inline BatchLayout batch_layout(int n_lds, int n_pad, int d, int elem) {
     BatchLayout L;
-    L.rows_bytes = (int64_t)n_rows * d * elem;  // d % 8 == 0: a multiple of 16
+    L.rows_bytes = (int64_t)n_lds * d * elem;  // d % 8 == 0: a multiple of 16
     L.rs_off = L.rows_bytes;
     L.tab_off = L.rs_off + (int64_t)n_pad * 4;  // n_pad % 4 == 0: 16-byte aligned
     L.counter_off = L.tab_off + (int64_t)kBatchWaves * n_pad * kBatchR * 4;
@@ -114,11 +124,12 @@ __host__ __device__ inline BatchLayout batch_layout(int n_rows, int n_pad, int d
 }
 
 template <typename TI, typename TO, int NCH>
-__global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams p, int n_rows, int n_pad) {
+__global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams p, int n_rows, int n_lds,
+                                                                      int n_pad) {
     constexpr int R = kBatchR;
     constexpr int RV = R / 4;  // f32x4 per row of the score table
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    const BatchLayout L = batch_layout(n_rows, n_pad, p.d, (int)sizeof(TI));
+    const BatchLayout L = batch_layout(n_lds, n_pad, p.d, (int)sizeof(TI));
     TI* const rows = reinterpret_cast<TI*>(lds_raw);
     float* const rs = reinterpret_cast<float*>(lds_raw + L.rs_off);
     int* const counter = reinterpret_cast<int*>(lds_raw + L.counter_off);
@@ -129,6 +140,7 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
     const int d = p.d;
     const int64_t row_elems = p.T * (int64_t)d;
     const TI* hist_tok = static_cast<const TI*>(p.hist) + t * d;
+    const uint64_t tok_bytes = (uint64_t)d * sizeof(TI);
 
     bool live[NCH];
     uint32_t in_off[NCH], out_off[NCH], w_off[NCH];
@@ -145,7 +157,6 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
     // ---- prologue: the token's rows into LDS, their RMS scales ------------
     {
         constexpr int U = 4;  // rows in flight per wave
-        const uint64_t tok_bytes = (uint64_t)d * sizeof(TI);
         const cf32_ptr cache = const_view(p.rinv);
         for (int ib = wave; ib < n_rows; ib += kBatchWaves * U) {
             Chunk<TI> ch[U][NCH];
@@ -162,10 +173,12 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
             for (int u = 0; u < U; ++u) {
                 const int i = ib + u * kBatchWaves;
                 if (i < n_rows) {
-                    TI* const row = rows + (int64_t)i * d;
+                    if (i < n_lds) {
+                        TI* const row = rows + (int64_t)i * d;
 #pragma unroll
-                    for (int c = 0; c < NCH; ++c)
-                        if (live[c]) store_raw(row, c * 64 + ln, ch[u][c]);
+                        for (int c = 0; c < NCH; ++c)
+                            if (live[c]) store_raw(row, c * 64 + ln, ch[u][c]);
+                    }
                     float r;
                     if (i < p.rinv_valid) {
                         r = cache[(int64_t)i * p.T + t];
@@ -188,6 +201,44 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
         }
     }
     __syncthreads();
+
+    // Rows 0..l_max in order, one row ahead in flight: first the rows staged in
+    // LDS, then (past n_lds) rows from global memory, in two loops so that each
+    // loop's registers are filled by one kind of load only.
+    auto walk_rows = [&](int l_max, auto&& body) {
+        const int i_lds = l_max < n_lds - 1 ? l_max : n_lds - 1;  // last row in LDS
+        {
+            LdsChunk<TI> cur[NCH], nxt[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+                if (live[c]) cur[c].load(rows, c * 64 + ln);
+            for (int i = 0; i <= i_lds; ++i) {
+                if (i < i_lds) {
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+                        if (live[c]) nxt[c].load(rows + (int64_t)(i + 1) * d, c * 64 + ln);
+                }
+                body(cur, i);
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) cur[c] = nxt[c];
+            }
+        }
+        if (i_lds < l_max) {
+            auto issue = [&](LdsChunk<TI> (&dst)[NCH], int i) {
+                const rsrc_t rr = make_rsrc(hist_tok + i * row_elems, tok_bytes);
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) dst[c].load_global(rr, in_off[c]);
+            };
+            LdsChunk<TI> cur[NCH], nxt[NCH];
+            issue(cur, i_lds + 1);
+            for (int i = i_lds + 1; i <= l_max; ++i) {
+                if (i < l_max) issue(nxt, i + 1);
+                body(cur, i);
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) cur[c] = nxt[c];
+            }
+        }
+    };
 
     // ---- groups of R reads ---------------------------------------------------
     f32x4* const tab = reinterpret_cast<f32x4*>(lds_raw + L.tab_off) + (int64_t)wave * n_pad * RV;
@@ -216,18 +267,8 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
             }
         }
 
-        // pass A: scores, one row ahead in flight
-        {
-            LdsChunk<TI> cur[NCH], nxt[NCH];
-#pragma unroll
-            for (int c = 0; c < NCH; ++c)
-                if (live[c]) cur[c].load(rows, c * 64 + ln);
-            for (int i = 0; i <= l_max; ++i) {
-                if (i < l_max) {
-#pragma unroll
-                    for (int c = 0; c < NCH; ++c)
-                        if (live[c]) nxt[c].load(rows + (int64_t)(i + 1) * d, c * 64 + ln);
-                }
+        // pass A: scores
+        walk_rows(l_max, [&](const LdsChunk<TI> (&cur)[NCH], int i) {
                 float dot[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) dot[r] = 0.f;
@@ -246,10 +287,7 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
                     const int r = ln & 3;
                     tabf[i * R + r] = (r < nr && i <= l0 + r) ? rs[i] * kLog2e * tot : -INFINITY;
                 }
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) cur[c] = nxt[c];
-            }
-        }
+        });
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
 
@@ -321,17 +359,7 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
             for (int c = 0; c < NCH; ++c)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[r][c][e] = 0.f;
-        {
-            LdsChunk<TI> cur[NCH], nxt[NCH];
-#pragma unroll
-            for (int c = 0; c < NCH; ++c)
-                if (live[c]) cur[c].load(rows, c * 64 + ln);
-            for (int i = 0; i <= l_max; ++i) {
-                if (i < l_max) {
-#pragma unroll
-                    for (int c = 0; c < NCH; ++c)
-                        if (live[c]) nxt[c].load(rows + (int64_t)(i + 1) * d, c * 64 + ln);
-                }
+        walk_rows(l_max, [&](const LdsChunk<TI> (&cur)[NCH], int i) {
                 float a[R];
 #pragma unroll
                 for (int q = 0; q < RV; ++q) {
@@ -349,10 +377,7 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
 #pragma unroll
                         for (int e = 0; e < 8; ++e) acc[r][c][e] = fmaf(a[r], x[e], acc[r][c][e]);
                 }
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) cur[c] = nxt[c];
-            }
-        }
+        });
         // the next group rewrites this wave's table only after these reads
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -399,58 +424,77 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
 }
 
 template <typename TI, typename TO, int NCH>
-hipError_t launch_batch(const FwdParams& p, int n_rows, int n_pad, size_t lds, hipStream_t stream) {
+hipError_t launch_batch(const FwdParams& p, int n_rows, int n_lds, int n_pad, size_t lds,
+                        hipStream_t stream) {
     const hipError_t e = hipFuncSetAttribute((const void*)full_batch_kernel<TI, TO, NCH>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((full_batch_kernel<TI, TO, NCH>), dim3((unsigned)p.T), dim3(64 * kBatchWaves), lds,
-                       stream, p, n_rows, n_pad);
+                       stream, p, n_rows, n_lds, n_pad);
     return hipGetLastError();
 }
 
 template <typename TI, typename TO>
-hipError_t dispatch_batch(const FwdParams& p, int n_rows, int n_pad, size_t lds, hipStream_t stream) {
+hipError_t dispatch_batch(const FwdParams& p, int n_rows, int n_lds, int n_pad, size_t lds,
+                          hipStream_t stream) {
     switch ((p.nc + 63) / 64) {
-        case 1: return launch_batch<TI, TO, 1>(p, n_rows, n_pad, lds, stream);
-        case 2: return launch_batch<TI, TO, 2>(p, n_rows, n_pad, lds, stream);
-        case 3: return launch_batch<TI, TO, 3>(p, n_rows, n_pad, lds, stream);
+        case 1: return launch_batch<TI, TO, 1>(p, n_rows, n_lds, n_pad, lds, stream);
+        case 2: return launch_batch<TI, TO, 2>(p, n_rows, n_lds, n_pad, lds, stream);
+        case 3: return launch_batch<TI, TO, 3>(p, n_rows, n_lds, n_pad, lds, stream);
         case 4:
-            if constexpr (sizeof(TI) == 2) return launch_batch<TI, TO, 4>(p, n_rows, n_pad, lds, stream);
-            return hipErrorInvalidValue;  // fp32 rows: full_batch_applies stops at 3
+            if constexpr (sizeof(TI) == 2) return launch_batch<TI, TO, 4>(p, n_rows, n_lds, n_pad, lds, stream);
+            return hipErrorInvalidValue;  // fp32 rows: batch_plan stops at 3
         default: return hipErrorInvalidValue;
     }
 }
 
-}  // namespace
+// Whether a call qualifies, and how many of its rows go to LDS.
+struct BatchPlan {
+    bool ok;
+    int n_rows, n_lds, n_pad;
+    size_t lds;
+};
 
-bool full_batch_applies(const FwdParams& p, attnres_dtype hist_dt) {
-    if (p.qtok != nullptr || p.n_q < kBatchMinReads) return false;
+BatchPlan batch_plan(const FwdParams& p, attnres_dtype hist_dt) {
+    BatchPlan b{false, 0, 0, 0, 0};
+    if (p.qtok != nullptr || p.n_q < kBatchMinReads) return b;
     // chunks per lane: up to 4 (bf16) or 3 (fp32 rows need twice the registers)
-    if (p.nc > (hist_dt == ATTNRES_BF16 ? 4 : 3) * 64) return false;
+    if (p.nc > (hist_dt == ATTNRES_BF16 ? 4 : 3) * 64) return b;
     // one workgroup of 64 * kBatchWaves work-items per token, in a 32-bit grid
-    if (p.T * 64 * kBatchWaves >= ((int64_t)1 << 32)) return false;
-    const int n_rows = p.q_begin + p.n_q;
-    const int n_pad = (n_rows + 3) & ~3;
-    const BatchLayout L = batch_layout(n_rows, n_pad, p.d, hist_dt == ATTNRES_BF16 ? 2 : 4);
+    if (p.T * 64 * kBatchWaves >= ((int64_t)1 << 32)) return b;
     int dev = 0, max_lds = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        return false;
-    return L.bytes <= max_lds;
+        return b;
+    const int elem = hist_dt == ATTNRES_BF16 ? 2 : 4;
+    b.n_rows = p.q_begin + p.n_q;
+    b.n_pad = (b.n_rows + 3) & ~3;
+    const int64_t room = (int64_t)max_lds - batch_layout(0, b.n_pad, p.d, elem).bytes;
+    const int64_t fit = room > 0 ? room / ((int64_t)p.d * elem) : 0;
+    b.n_lds = fit < b.n_rows ? (int)fit : b.n_rows;
+    // rows past n_lds are read from global memory in both passes of every group
+    // that sees them: worth it while at least two thirds of the rows are staged
+    if (3 * (int64_t)b.n_lds < 2 * (int64_t)b.n_rows) return b;
+    b.lds = (size_t)batch_layout(b.n_lds, b.n_pad, p.d, elem).bytes;
+    b.ok = true;
+    return b;
 }
+
+}  // namespace
+
+bool full_batch_applies(const FwdParams& p, attnres_dtype hist_dt) { return batch_plan(p, hist_dt).ok; }
 
 hipError_t launch_full_batch(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
                              hipStream_t stream) {
-    const int n_rows = p.q_begin + p.n_q;
-    const int n_pad = (n_rows + 3) & ~3;
-    const size_t lds = (size_t)batch_layout(n_rows, n_pad, p.d, hist_dt == ATTNRES_BF16 ? 2 : 4).bytes;
+    const BatchPlan b = batch_plan(p, hist_dt);
+    if (!b.ok) return hipErrorInvalidValue;
     if (hist_dt == ATTNRES_BF16 && out_dt == ATTNRES_BF16)
-        return dispatch_batch<bf16_t, bf16_t>(p, n_rows, n_pad, lds, stream);
+        return dispatch_batch<bf16_t, bf16_t>(p, b.n_rows, b.n_lds, b.n_pad, b.lds, stream);
     if (hist_dt == ATTNRES_BF16 && out_dt == ATTNRES_F32)
-        return dispatch_batch<bf16_t, float>(p, n_rows, n_pad, lds, stream);
+        return dispatch_batch<bf16_t, float>(p, b.n_rows, b.n_lds, b.n_pad, b.lds, stream);
     if (hist_dt == ATTNRES_F32 && out_dt == ATTNRES_F32)
-        return dispatch_batch<float, float>(p, n_rows, n_pad, lds, stream);
-    return dispatch_batch<float, bf16_t>(p, n_rows, n_pad, lds, stream);
+        return dispatch_batch<float, float>(p, b.n_rows, b.n_lds, b.n_pad, b.lds, stream);
+    return dispatch_batch<float, bf16_t>(p, b.n_rows, b.n_lds, b.n_pad, b.lds, stream);
 }
 
 }  // namespace attnres

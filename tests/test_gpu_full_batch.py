@@ -1,9 +1,10 @@
 """GPU parity of the Full forward for calls with many reads (run on an MI355X).
 
-A call with at least 16 reads whose rows fit in a workgroup's LDS is served by
-the kernel that stages each token's rows in LDS once (full_batch.hip); the
-shapes below are chosen to qualify (see ``_qualifies``), covering one to four
-16-byte chunks per lane, ragged last groups of reads (n_q not a multiple of 4),
+A call with at least 16 reads is served by the kernel that stages each token's
+rows in LDS once (full_batch.hip) when at least two thirds of the rows fit
+(the rest are then read from global memory); the shapes below are chosen to
+qualify (see ``_qualifies``), covering one to four 16-byte chunks per lane,
+ragged last groups of reads (n_q not a multiple of 4), rows past the LDS,
 reads that start past row 0, the RMS cache, the fused pre-norm and the weight
 probe.  Every output is compared with the fp64 oracle; the full-size
 workloads compare a token sample, which is exact per token because tokens are
@@ -26,15 +27,21 @@ def ar():
     return ar
 
 
-def _qualifies(n_rows, n_q, d, dtype):
-    """The rule the library applies: >= 16 reads, <= 4 (bf16) or 3 (fp32)
-    chunks of 8 per lane, and rows + scales + 8 score tables of 4 floats per
-    row in LDS."""
+def _lds_rows(n_rows, d, dtype):
+    """Rows the library stages in LDS: as many as fit next to the RMS scales,
+    8 score tables of 4 floats per row and the group counter."""
     elem = 2 if dtype == "bf16" else 4
     n_pad = (n_rows + 3) // 4 * 4
-    lds = n_rows * d * elem + 4 * n_pad + 8 * 16 * n_pad + 16
+    room = LDS_BYTES - (4 * n_pad + 8 * 16 * n_pad + 16)
+    return min(n_rows, room // (d * elem))
+
+
+def _qualifies(n_rows, n_q, d, dtype):
+    """The rule the library applies: >= 16 reads, <= 4 (bf16) or 3 (fp32)
+    chunks of 8 per lane, at least two thirds of the rows in LDS."""
     nch = (d // 8 + 63) // 64
-    return n_q >= 16 and nch <= (4 if dtype == "bf16" else 3) and lds <= LDS_BYTES
+    return (n_q >= 16 and nch <= (4 if dtype == "bf16" else 3)
+            and 3 * _lds_rows(n_rows, d, dtype) >= 2 * n_rows)
 
 
 def _inputs(n_hist, T, d, seed, dtype, w_sigma=0.3):
@@ -62,6 +69,27 @@ def test_batch_all_reads(ar, oracle, dtype, n_hist, T, d):
     ref, ref_lse = oracle.full_fwd(h64, w64)
     check_out(to_f64(out), ref, dtype)
     check_lse(to_f64(lse), ref_lse)
+
+
+@pytest.mark.parametrize("dtype,n_hist,T,d", [("bf16", 70, 19, 1536), ("f32", 40, 23, 1032)])
+def test_batch_rows_past_lds(ar, oracle, dtype, n_hist, T, d):
+    # more rows than LDS holds: the first are staged, the rest (seen only by
+    # the last groups of reads) come from global memory in both passes
+    n_lds = _lds_rows(n_hist, d, dtype)
+    assert _qualifies(n_hist, n_hist, d, dtype) and n_lds < n_hist
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=n_hist + d, dtype=dtype, w_sigma=0.05)
+    rinv = torch.empty((n_hist, T), device=DEV)
+    normed = torch.empty(h.shape, dtype=h.dtype, device=DEV)
+    out = torch.empty_like(normed)
+    lse = torch.empty((n_hist, T), device=DEV)
+    ar.full_fwd(h, w, out=out, lse=lse, rinv=rinv, normed=normed)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.full_fwd(h64, w64)
+    check_out(to_f64(out), ref, dtype)
+    check_lse(to_f64(lse), ref_lse)
+    check_out(to_f64(normed), oracle.prenorm(ref, None), dtype, what="normed")
+    r_ref = 1.0 / np.sqrt((h64 ** 2).mean(axis=2) + 1e-6)
+    np.testing.assert_allclose(to_f64(rinv), r_ref, rtol=2e-6)
 
 
 @pytest.mark.parametrize("hdt,odt", [("bf16", "f32"), ("f32", "bf16")])

@@ -151,9 +151,10 @@ def test_full_workload_model_order_sampled(ar, oracle, name):
     print(f"{name}: {stats}", flush=True)
 
 
-def test_full_workload_batched_streaming_sampled(ar, oracle):
-    # the L=70 / d=640 history in one call with all 141 reads: its rows do not
-    # fit in a workgroup's LDS, so the streaming kernel serves every read
+def test_full_workload_batched_l70_sampled(ar, oracle):
+    # the L=70 / d=640 history in one call with all 141 reads: its 180 KB of
+    # rows per token do not all fit in a workgroup's LDS, so the batched kernel
+    # stages the first rows and reads the rest from global memory
     from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs, token_sample
     wl = WORKLOADS["full_L70_d640"]
     h, w, _ = device_inputs(wl, DEV)
