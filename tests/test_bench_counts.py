@@ -51,3 +51,16 @@ def test_backward_fmas_full_equals_block_of_one():
     n = 49
     per_read = sum(2 * (l + 1) + 3 * (l + 1) for l in range(n))
     assert bench.bwd_fmas_per_token(n, n, 1) == 2 * n + per_read
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the benchmark measures one GPU; --gpus N > 1 exits with a message before
+    # touching any device
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode != 0
+    assert "one GPU only" in res.stdout + res.stderr
