@@ -13,12 +13,12 @@
 // Mapping: one workgroup of kBatchWaves waves per token.
 //   prologue  the waves copy rows 0..n_lds-1 into LDS (input type, row-major,
 //             16-byte chunks along d) and form the RMS scale r_i of every row
-//             0..l_max: from
-//             the caller's cache when the row is valid there, else from the
-//             row's sum of squares (then written to the cache);
+//             the call sees: from the caller's cache when the row is valid
+//             there, else from the row's sum of squares (then written to the
+//             cache);
 //   groups    the reads are cut into groups of R consecutive reads, which the
 //             waves take from a workgroup counter, the group with the most
-//             rows first.  A group is two passes over its rows in LDS:
+//             rows first.  A group is two passes over its rows:
 //     A  the R dots w_l . v_i of each row, reduced over the wave; the scores
 //        s = r_i (w_l . v_i) (log2 units) go to a per-wave LDS table; then,
 //        per read, the exact softmax over its rows i <= l: max, sum, weights
@@ -164,9 +164,16 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
             for (int u = 0; u < U; ++u) {
                 const int i = ib + u * kBatchWaves;
                 if (i < n_rows) {
+                    // staged rows are read from HBM once (non-temporal); rows past
+                    // the LDS are read again by the passes and keep the default policy
                     const rsrc_t rr = make_rsrc(hist_tok + i * row_elems, tok_bytes);
+                    if (i < n_lds) {
 #pragma unroll
-                    for (int c = 0; c < NCH; ++c) ch[u][c].template load<kAuxNT>(rr, in_off[c]);
+                        for (int c = 0; c < NCH; ++c) ch[u][c].template load<kAuxNT>(rr, in_off[c]);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < NCH; ++c) ch[u][c].load(rr, in_off[c]);
+                    }
                 }
             }
 #pragma unroll
