@@ -1,0 +1,392 @@
+// block_batch.hip -- Block AttnRes forward for calls with many reads, one wave
+// per group of reads, on gfx950.
+//
+// Block reading ("DepthBench reading notes" sec. 2.5; DataCamp, block
+// section): read l with m = floor(l / S) attends over v_0, the completed block
+// sums b_1..b_m and, when l mod S != 0, the partial sum p_l of rows mS+1..l.
+//
+// The two-phase kernel (block_fwd.hip) gives each of a token's waves a slice
+// of d and runs every read in every wave, so the per-read work that does not
+// scale with d -- the reductions of the dots, the softmax, the loop -- is paid
+// once per wave.  Here one wave owns all of d for a group of reads:
+//   prologue  the workgroup (one per token) forms the frozen sources v_0,
+//             b_1, b_2, ... in fp32 from the raw rows, stores them in LDS and
+//             forms their RMS scales;
+//   units     each block group g (reads gS .. gS+S-1) is cut into two halves;
+//             the waves take halves from a workgroup counter, latest group
+//             first.  A half streams the rows gS+1.. of its group again (from
+//             L2 or the last-level cache: the prologue read them) to form each
+//             read's partial sum in registers, and for every read: the dots of
+//             its query with the frozen sources (from LDS) and with the partial
+//             sum, one transposing wave reduction of all of them, the exact
+//             softmax over [frozen sources, partial] (equal to the two-phase
+//             merge), and the weighted sum, rounded once and stored.
+// Lane `ln` owns the 16-byte chunks ln, ln + 64, ... of d.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace attnres {
+
+namespace {
+
+constexpr int kBbWaves = 8;
+constexpr int kBbMinReads = 16;
+constexpr int kBbMaxSources = 13;  // v_0 + completed blocks a read of the call sees
+
+// LDS: sources [nb][d] fp32, their RMS scales [nb rounded up to 4], counter
+__host__ __device__ inline int64_t bb_lds_bytes(int nb, int d) {
+    return (int64_t)nb * d * 4 + (int64_t)((nb + 3) & ~3) * 4 + 16;
+}
+
+__device__ __forceinline__ void lds_src(const float* src, int64_t off, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(src + off);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(src + off + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        x[q] = a[q];
+        x[4 + q] = b[q];
+    }
+}
+
+// Wave totals of KV values, as wave-uniform scalars: groups of up to 8 values
+// share one transposing reduction; value k of a group is read from the lane
+// that holds it.
+template <int P>
+__device__ __forceinline__ int holder_lane(int k) {
+    return P == 8 ? (k & 3) | 4 | ((k >> 2) << 3) : 4 + k;
+}
+template <int BASE, int KV>
+__device__ __forceinline__ void wave_totals(const float (&v)[KV], float (&tot)[KV], int lane) {
+    constexpr int REM = KV - BASE;
+    constexpr int P = REM > 4 ? 8 : 4;
+    float g[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) g[j] = BASE + j < KV ? v[BASE + j < KV ? BASE + j : 0] : 0.f;
+    const float t = wave_sum_transposed<P>(g, lane);
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        if (BASE + j < KV)
+            tot[BASE + j < KV ? BASE + j : 0] =
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), holder_lane<P>(j)));
+    if constexpr (REM > 8) wave_totals<BASE + 8, KV>(v, tot, lane);
+}
+
+struct BbLane {
+    bool live[4];
+    uint32_t in_off[4], out_off[4], w_off[4];
+};
+
+// The reads la..lb of block group G, all in block group G (la >= G S).
+template <typename TO, int NCH, int G>
+__device__ __forceinline__ void bb_unit(const FwdParams& p, const float* src, const float* rsv,
+                                        const bf16_t* hist_tok, int64_t t, int ln, const BbLane& q,
+                                        int la, int lb) {
+    constexpr int kV = G + 3;  // frozen-source dots, partial dot, partial sum of squares
+    const int d = p.d;
+    const int64_t row_elems = p.T * (int64_t)d;
+    const uint64_t tok_bytes = (uint64_t)d * 2;
+    const int g0 = G * p.S;  // the group's first read; its partial sums start at row g0 + 1
+
+    float rs2[G + 1];  // RMS scales of the frozen sources, log2 units
+#pragma unroll
+    for (int c = 0; c <= G; ++c) rs2[c] = rsv[c] * kLog2e;
+
+    float part[NCH][8];
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[c2][e] = 0.f;
+    auto add_row = [&](const Chunk<bf16_t> (&r)[NCH]) {
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) {
+            float x[8];
+            r[c2].to_float(x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[c2][e] += x[e];
+        }
+    };
+    auto issue_row = [&](Chunk<bf16_t> (&r)[NCH], int i) {
+        const rsrc_t rr = make_rsrc(hist_tok + i * row_elems, tok_bytes);
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) r[c2].load(rr, q.in_off[c2]);
+    };
+    // rows g0+1 .. la-1 (the part of the partial sum before the first read), four at a time
+    for (int i0 = g0 + 1; i0 < la; i0 += 4) {
+        Chunk<bf16_t> cb[4][NCH];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + u < la) issue_row(cb[u], i0 + u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + u < la) add_row(cb[u]);
+    }
+    Chunk<bf16_t> rl[NCH];  // row l of the current read, in flight
+    if (la > g0) issue_row(rl, la);
+    Chunk<float> wq[NCH];   // query of the current read, in flight
+    auto issue_w = [&](int l) {
+        const rsrc_t wr = make_rsrc(p.w + (int64_t)(l - p.q_begin) * d, (uint64_t)d * 4);
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) wq[c2].load(wr, q.w_off[c2]);
+    };
+    issue_w(la);
+
+    for (int l = la; l <= lb; ++l) {
+        float wv[NCH][8];
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) wq[c2].to_float(wv[c2]);
+        if (l < lb) issue_w(l + 1);
+        const bool has_p = l > g0;
+        if (has_p) add_row(rl);             // row l joins the partial sum
+        if (l < lb) issue_row(rl, l + 1);   // the next read's row (always past g0)
+
+        // dots with the frozen sources and the partial sum
+        float v[kV];
+#pragma unroll
+        for (int j = 0; j < kV; ++j) v[j] = 0.f;
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) {
+            if (!q.live[c2]) continue;
+            const int64_t off = 8 * (int64_t)(c2 * 64 + ln);
+#pragma unroll
+            for (int c = 0; c <= G; ++c) {
+                float x[8];
+                lds_src(src, (int64_t)c * d + off, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[c] = fmaf(wv[c2][e], x[e], v[c]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[G + 1] = fmaf(wv[c2][e], part[c2][e], v[G + 1]);
+                v[G + 2] = fmaf(part[c2][e], part[c2][e], v[G + 2]);
+            }
+        }
+        float tot[kV];
+        wave_totals<0, kV>(v, tot, ln);
+
+        // exact softmax over [v_0, b_1..b_G, partial]
+        float s[G + 1];
+        float M = -INFINITY;
+#pragma unroll
+        for (int c = 0; c <= G; ++c) {
+            s[c] = rs2[c] * tot[c];
+            M = fmaxf(M, s[c]);
+        }
+        float sp = -INFINITY;
+        if (has_p) {
+            sp = fast_rsqrt(fmaf(tot[G + 2], p.inv_d, p.eps)) * tot[G + 1] * kLog2e;
+            M = fmaxf(M, sp);
+        }
+        float a[G + 1];
+        float Z = 0.f;
+#pragma unroll
+        for (int c = 0; c <= G; ++c) {
+            a[c] = fast_exp2(s[c] - M);
+            Z += a[c];
+        }
+        const float ep = has_p ? fast_exp2(sp - M) : 0.f;
+        Z += ep;
+        const float inv = 1.0f / Z;
+#pragma unroll
+        for (int c = 0; c <= G; ++c) a[c] *= inv;
+        const float ap = ep * inv;
+
+        // the weighted sum
+        const int64_t j = l - p.q_begin;
+        const rsrc_t orr = make_rsrc(static_cast<TO*>(p.out) + j * row_elems + t * d,
+                                     (uint64_t)d * sizeof(TO));
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = ap * part[c2][e];
+            if (q.live[c2]) {
+                const int64_t off = 8 * (int64_t)(c2 * 64 + ln);
+#pragma unroll
+                for (int c = 0; c <= G; ++c) {
+                    float x[8];
+                    lds_src(src, (int64_t)c * d + off, x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] = fmaf(a[c], x[e], o[e]);
+                }
+            }
+            store_chunk((TO*)nullptr, orr, q.out_off[c2], o);
+        }
+        if (p.lse != nullptr && ln == 0) p.lse[j * p.T + t] = (M + fast_log2(Z)) * kLn2;
+        if (p.alpha != nullptr) {  // weight probe in source order, zeros past the sources
+            const int ns = G + 1 + (has_p ? 1 : 0);
+            for (int x = ln; x < p.n_hist; x += 64) {
+                float ax = 0.f;
+#pragma unroll
+                for (int c = 0; c <= G; ++c)
+                    if (x == c) ax = a[c];
+                if (x == G + 1 && x < ns) ax = ap;
+                p.alpha[(j * p.n_hist + x) * p.T + t] = ax;
+            }
+        }
+    }
+}
+
+template <typename TO, int NCH, int NBMAX, int G = 0>
+__device__ __forceinline__ void bb_dispatch(int g, const FwdParams& p, const float* src, const float* rsv,
+                                            const bf16_t* hist_tok, int64_t t, int ln, const BbLane& q,
+                                            int la, int lb) {
+    if constexpr (G < NBMAX) {
+        if (g == G)
+            bb_unit<TO, NCH, G>(p, src, rsv, hist_tok, t, ln, q, la, lb);
+        else
+            bb_dispatch<TO, NCH, NBMAX, G + 1>(g, p, src, rsv, hist_tok, t, ln, q, la, lb);
+    }
+}
+
+template <typename TO, int NCH, int NBMAX>
+__global__ __launch_bounds__(64 * kBbWaves) void block_batch_kernel(FwdParams p, int nb) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    float* const src = reinterpret_cast<float*>(lds_raw);
+    float* const rsv = src + (int64_t)nb * p.d;
+    int* const counter = reinterpret_cast<int*>(rsv + ((nb + 3) & ~3));
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ln = threadIdx.x & 63;
+    const int64_t t = blockIdx.x;
+    const int d = p.d, S = p.S;
+    const int64_t row_elems = p.T * (int64_t)d;
+    const bf16_t* hist_tok = static_cast<const bf16_t*>(p.hist) + t * d;
+    const uint64_t tok_bytes = (uint64_t)d * 2;
+
+    BbLane q;
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+        const int ch = c2 * 64 + ln;
+        q.live[c2] = c2 < NCH && ch < p.nc;
+        q.in_off[c2] = q.live[c2] ? (uint32_t)(ch * 16) : kOOB;
+        q.out_off[c2] = q.live[c2] ? (uint32_t)(ch * 8 * sizeof(TO)) : kOOB;
+        q.w_off[c2] = q.live[c2] ? (uint32_t)(ch * 32) : kOOB;
+    }
+    if (threadIdx.x == 0) *counter = 0;
+
+    // ---- prologue: frozen sources v_0, b_1, ... in fp32, their RMS scales ------
+    for (int c = wave; c < nb; c += kBbWaves) {
+        const int i0 = c == 0 ? 0 : (c - 1) * S + 1;
+        const int i1 = c == 0 ? 0 : c * S;  // inclusive; c * S <= last read < n_hist
+        float acc[NCH][8];
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[c2][e] = 0.f;
+        for (int ib = i0; ib <= i1; ib += 4) {
+            Chunk<bf16_t> ch[4][NCH];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (ib + u <= i1) {
+                    const rsrc_t rr = make_rsrc(hist_tok + (ib + u) * row_elems, tok_bytes);
+#pragma unroll
+                    for (int c2 = 0; c2 < NCH; ++c2) ch[u][c2].load(rr, q.in_off[c2]);
+                }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (ib + u <= i1) {
+#pragma unroll
+                    for (int c2 = 0; c2 < NCH; ++c2) {
+                        float x[8];
+                        ch[u][c2].to_float(x);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[c2][e] += x[e];
+                    }
+                }
+        }
+        float sq = 0.f;
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sq = fmaf(acc[c2][e], acc[c2][e], sq);
+            if (q.live[c2]) {
+                float* dst = src + (int64_t)c * d + 8 * (c2 * 64 + ln);
+                *reinterpret_cast<f32x4*>(dst) = f32x4{acc[c2][0], acc[c2][1], acc[c2][2], acc[c2][3]};
+                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[c2][4], acc[c2][5], acc[c2][6], acc[c2][7]};
+            }
+        }
+        sq = tg_sum<64>(sq);
+        if (ln == 0) rsv[c] = fast_rsqrt(fmaf(sq, p.inv_d, p.eps));
+    }
+    __syncthreads();
+
+    // ---- halves of block groups, latest group first ------------------------------
+    const int l_last = p.q_begin + p.n_q - 1;
+    const int g_last = l_last / S;
+    const int n_units = 2 * (g_last + 1);
+    const int half = (S + 1) / 2;
+    for (;;) {
+        int u = 0;
+        if (ln == 0) u = atomicAdd(counter, 1);
+        u = __builtin_amdgcn_readfirstlane(u);
+        if (u >= n_units) break;
+        const int g = g_last - (u >> 1);
+        int la = g * S + (u & 1) * half;
+        int lb = la + half - 1;
+        if (lb > g * S + S - 1) lb = g * S + S - 1;
+        if (la < p.q_begin) la = p.q_begin;
+        if (lb > l_last) lb = l_last;
+        if (la > lb) continue;
+        bb_dispatch<TO, NCH, NBMAX>(g, p, src, rsv, hist_tok, t, ln, q, la, lb);
+    }
+}
+
+template <typename TO, int NCH>
+hipError_t launch_bb_nch(const FwdParams& p, int nb, size_t lds, hipStream_t stream) {
+    auto go = [&](auto kern) {
+        const hipError_t e =
+            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)p.T), dim3(64 * kBbWaves), lds, stream, p, nb);
+        return hipGetLastError();
+    };
+    // the group index dispatch is instantiated up to NBMAX - 1
+    if (nb <= 9) return go(block_batch_kernel<TO, NCH, 9>);
+    return go(block_batch_kernel<TO, NCH, kBbMaxSources>);
+}
+
+template <typename TO>
+hipError_t launch_bb(const FwdParams& p, int nb, size_t lds, hipStream_t stream) {
+    switch ((p.nc + 63) / 64) {
+        case 1: return launch_bb_nch<TO, 1>(p, nb, lds, stream);
+        case 2: return launch_bb_nch<TO, 2>(p, nb, lds, stream);
+        case 3: return launch_bb_nch<TO, 3>(p, nb, lds, stream);
+        case 4: return launch_bb_nch<TO, 4>(p, nb, lds, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// sources a read of the call can see (v_0 and the completed blocks), or 0 if
+// the call does not qualify
+int bb_sources(const FwdParams& p, attnres_dtype hist_dt, size_t* lds) {
+    if (hist_dt != ATTNRES_BF16 || p.S < 2 || p.n_q < kBbMinReads || p.nc > 4 * 64) return 0;
+    if (p.T * 64 * kBbWaves >= ((int64_t)1 << 32)) return 0;
+    const int nb = 1 + (p.q_begin + p.n_q - 1) / p.S;
+    if (nb > kBbMaxSources) return 0;
+    int dev = 0, max_lds = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return 0;
+    const int64_t bytes = bb_lds_bytes(nb, p.d);
+    if (bytes > max_lds) return 0;
+    *lds = (size_t)bytes;
+    return nb;
+}
+
+}  // namespace
+
+bool block_batch_applies(const FwdParams& p, attnres_dtype hist_dt) {
+    size_t lds = 0;
+    return bb_sources(p, hist_dt, &lds) > 0;
+}
+
+hipError_t launch_block_batch(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
+                              hipStream_t stream) {
+    size_t lds = 0;
+    const int nb = bb_sources(p, hist_dt, &lds);
+    if (nb == 0) return hipErrorInvalidValue;
+    return out_dt == ATTNRES_BF16 ? launch_bb<bf16_t>(p, nb, lds, stream)
+                                  : launch_bb<float>(p, nb, lds, stream);
+}
+
+}  // namespace attnres

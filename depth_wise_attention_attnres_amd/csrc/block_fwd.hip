@@ -464,6 +464,7 @@ hipError_t dispatch_block(const BlockFwdParams& p, hipStream_t stream) {
 
 hipError_t launch_block_fwd(const BlockFwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
                             hipStream_t stream) {
+    if (block_batch_applies(p, hist_dt)) return launch_block_batch(p, hist_dt, out_dt, stream);
     (void)out_dt;  // carried in p.out_dt, a uniform branch at the store
     return hist_dt == ATTNRES_BF16 ? dispatch_block<bf16_t>(p, stream)
                                    : dispatch_block<float>(p, stream);

@@ -56,6 +56,11 @@ hipError_t launch_block_fwd(const BlockFwdParams& p, attnres_dtype hist_dt, attn
 bool full_batch_applies(const FwdParams& p, attnres_dtype hist_dt);
 hipError_t launch_full_batch(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
                              hipStream_t stream);
+// Block reads of a call with many reads, one wave per half block group
+// (block_batch.hip): whether the call qualifies, and the launch
+bool block_batch_applies(const FwdParams& p, attnres_dtype hist_dt);
+hipError_t launch_block_batch(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
+                              hipStream_t stream);
 // streaming Block kernel (one pass over rows 0..l per read, sums formed on the fly)
 hipError_t launch_block_stream(const BlockFwdParams& p, hipStream_t stream);
 

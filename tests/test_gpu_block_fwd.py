@@ -56,6 +56,27 @@ def test_block_read_subsets(ar, oracle, n_hist, S, q_begin, n_q):
     check_lse(to_f64(lse), ref_lse)
 
 
+# Calls with >= 16 reads over a bf16 history and at most 13 sources are served by
+# the kernel with one wave per half block group (block_batch.hip): fp32 and
+# bf16 outputs, odd and even S (halves of unequal length), three chunks per
+# lane, and read ranges that start inside a half (the partial sum is caught up
+# from the group's first row).
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+@pytest.mark.parametrize("n_hist,T,d,S,q_begin", [(24, 9, 264, 2, 0), (22, 11, 1032, 3, 0),
+                                                  (31, 7, 520, 5, 3), (40, 5, 2048, 8, 13),
+                                                  (49, 6, 1024, 4, 0)])
+def test_block_group_kernel(ar, oracle, odt, n_hist, T, d, S, q_begin):
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=n_hist * 7 + S + q_begin, dtype="bf16", w_sigma=0.05)
+    n_q = n_hist - q_begin
+    assert n_q >= 16 and 1 + (n_hist - 1) // S <= 13
+    out, lse = ar.block_fwd(h, w[q_begin:], S, q_begin=q_begin, n_q=n_q,
+                            out_dtype=torch.float32 if odt == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.block_fwd(h64, w64[q_begin:], S, q_begin=q_begin, n_q=n_q)
+    check_out(to_f64(out), ref, odt)
+    check_lse(to_f64(lse), ref_lse)
+
+
 def test_block_S1_matches_full_kernel(ar):
     h, w, _, _ = _inputs(12, 300, 512, seed=4, dtype="f32")
     ob, lb = ar.block_fwd(h, w, 1)
