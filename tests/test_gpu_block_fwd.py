@@ -57,10 +57,9 @@ def test_block_read_subsets(ar, oracle, n_hist, S, q_begin, n_q):
 
 
 # Calls with >= 16 reads over a bf16 history and at most 13 sources are served by
-# the kernel with one wave per half block group (block_batch.hip): fp32 and
-# bf16 outputs, odd and even S (halves of unequal length), three chunks per
-# lane, and read ranges that start inside a half (the partial sum is caught up
-# from the group's first row).
+# the kernel with one wave per block group (block_batch.hip): fp32 and bf16
+# outputs, odd and even S, three chunks per lane, and read ranges that start
+# inside a group (the partial sum is caught up from the group's first row).
 @pytest.mark.parametrize("odt", ["f32", "bf16"])
 @pytest.mark.parametrize("n_hist,T,d,S,q_begin", [(24, 9, 264, 2, 0), (22, 11, 1032, 3, 0),
                                                   (31, 7, 520, 5, 3), (40, 5, 2048, 8, 13),
