@@ -37,39 +37,6 @@ __host__ __device__ inline int64_t bb_lds_bytes(int nb, int d) {
     return (int64_t)nb * d * 4 + (int64_t)((nb + 3) & ~3) * 4 + 16;
 }
 
-__device__ __forceinline__ void lds_src(const float* src, int64_t off, float (&x)[8]) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(src + off);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(src + off + 4);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        x[q] = a[q];
-        x[4 + q] = b[q];
-    }
-}
-
-// Wave totals of KV values, as wave-uniform scalars: groups of up to 8 values
-// share one transposing reduction; value k of a group is read from the lane
-// that holds it.
-template <int P>
-__device__ __forceinline__ int holder_lane(int k) {
-    return P == 8 ? (k & 3) | 4 | ((k >> 2) << 3) : 4 + k;
-}
-template <int BASE, int KV>
-__device__ __forceinline__ void wave_totals(const float (&v)[KV], float (&tot)[KV], int lane) {
-    constexpr int REM = KV - BASE;
-    constexpr int P = REM > 4 ? 8 : 4;
-    float g[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) g[j] = BASE + j < KV ? v[BASE + j < KV ? BASE + j : 0] : 0.f;
-    const float t = wave_sum_transposed<P>(g, lane);
-#pragma unroll
-    for (int j = 0; j < P; ++j)
-        if (BASE + j < KV)
-            tot[BASE + j < KV ? BASE + j : 0] =
-                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), holder_lane<P>(j)));
-    if constexpr (REM > 8) wave_totals<BASE + 8, KV>(v, tot, lane);
-}
-
 struct BbLane {
     bool live[4];
     uint32_t in_off[4], out_off[4], w_off[4];

@@ -1042,6 +1042,7 @@ hipError_t launch_scores(const BwdParams& p, hipStream_t stream) {
                            stream, p, rtp, nb);
         return hipGetLastError();
     }
+    if (bwd_scores_group_applies(p)) return launch_bwd_scores_group(p, stream);
     const int nch = (p.nc + 63) / 64;
     switch (nch) {
 #define ATTNRES_SCORES(N, PF, R)                                                          \

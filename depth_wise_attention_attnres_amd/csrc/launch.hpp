@@ -98,6 +98,10 @@ struct BwdParams {
     uint16_t* ws_wsplit;  // [3][n_q][d] bf16: w = hi + mid + lo (matrix-core scores)
 };
 hipError_t launch_bwd(const BwdParams& p, int n_chunks, int n_dw_groups, hipStream_t stream);
+// the backward's per-read coefficients for Block calls with many reads, one
+// wave per block group (bwd_group.hip): whether the call qualifies, the launch
+bool bwd_scores_group_applies(const BwdParams& p);
+hipError_t launch_bwd_scores_group(const BwdParams& p, hipStream_t stream);
 
 // Block AttnRes in model order (block_model.hip)
 struct Phase1Params {

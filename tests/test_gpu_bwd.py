@@ -110,3 +110,12 @@ def test_bwd_read_subsets_bf16(ar, oracle, variant, S, n_hist, q_begin, n_q, d):
     h, w, g = _case(n_hist, 11, d, seed=q_begin * 5 + n_q + d, dtype="bf16", n_q=n_q,
                     q_begin=q_begin)
     _check(ar, oracle, variant, S, h, w, g, "bf16", q_begin=q_begin)
+
+
+@pytest.mark.parametrize("n_hist,T,d,S,q_begin", [(33, 9, 1024, 4, 0), (26, 7, 200, 3, 5)])
+def test_bwd_group_kernel_fp32_dout(ar, oracle, n_hist, T, d, S, q_begin):
+    # bf16 history with an fp32 upstream gradient, >= 16 reads: the per-read
+    # coefficients come from the kernel with one wave per block group
+    h, w, g = _case(n_hist, T, d, seed=n_hist + S, dtype="bf16", q_begin=q_begin)
+    g = g.to(torch.float32)
+    _check(ar, oracle, BLOCK, S, h, w, g, "bf16", q_begin=q_begin)
