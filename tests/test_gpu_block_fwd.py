@@ -139,3 +139,21 @@ def test_block_alpha_probe(ar, oracle, dtype, n_hist, T, d, S):
     for l in range(n_hist):
         ns = oracle.num_sources(oracle.BLOCK, l, S)
         assert (a[l, ns:] == 0).all()
+
+
+@pytest.mark.parametrize("n_hist,T,d,S,q_begin,n_q", [(16, 1, 64, 4, 0, 16), (20, 3, 136, 20, 0, 20),
+                                                      (20, 3, 136, 25, 0, 20), (30, 2, 8, 6, 7, 16),
+                                                      (26, 5, 512, 2, 10, 16)])
+def test_block_group_kernel_edges(ar, oracle, n_hist, T, d, S, q_begin, n_q):
+    # exactly 16 reads, S at or past the history (only v_0 and the partial
+    # sum), one token, d = 8, and reads that start inside a group
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=T * 11 + S + q_begin, dtype="bf16", w_sigma=0.1)
+    alpha = torch.full((n_q, n_hist, T), float("nan"), device=DEV)
+    out, lse = ar.block_fwd(h, w[q_begin:q_begin + n_q].contiguous(), S, q_begin=q_begin, n_q=n_q,
+                            alpha=alpha)
+    torch.cuda.synchronize()
+    ref, ref_lse, ref_a = oracle.fwd(oracle.BLOCK, h64, w64[q_begin:q_begin + n_q], S=S,
+                                     q_begin=q_begin, n_q=n_q, want_alpha=True)
+    check_out(to_f64(out), ref, "bf16")
+    check_lse(to_f64(lse), ref_lse)
+    check_rel(to_f64(alpha), ref_a.transpose(0, 2, 1), 1e-5, "alpha")

@@ -119,3 +119,10 @@ def test_bwd_group_kernel_fp32_dout(ar, oracle, n_hist, T, d, S, q_begin):
     h, w, g = _case(n_hist, T, d, seed=n_hist + S, dtype="bf16", q_begin=q_begin)
     g = g.to(torch.float32)
     _check(ar, oracle, BLOCK, S, h, w, g, "bf16", q_begin=q_begin)
+
+
+@pytest.mark.parametrize("n_hist,T,d,S,q_begin", [(16, 1, 64, 4, 0), (18, 3, 136, 18, 0), (22, 2, 8, 5, 6)])
+def test_bwd_group_kernel_edges(ar, oracle, n_hist, T, d, S, q_begin):
+    # exactly 16 reads, S at the history length, one token, d = 8
+    h, w, g = _case(n_hist, T, d, seed=n_hist * 3 + T + S, dtype="bf16", q_begin=q_begin)
+    _check(ar, oracle, BLOCK, S, h, w, g, "bf16", q_begin=q_begin)

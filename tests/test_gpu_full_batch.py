@@ -190,3 +190,16 @@ def test_batch_workload_sampled(ar, oracle, name):
     stats = check_out(to_f64(out.index_select(1, ti)), ref, wl.dtype)
     check_lse(to_f64(lse.index_select(1, ti)), ref_lse)
     print(f"{name} batched: {stats}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_hist,T,d,q_begin", [(16, 1, 8, 0), (21, 2, 8, 5), (17, 1, 1024, 1)])
+def test_batch_edges(ar, oracle, dtype, n_hist, T, d, q_begin):
+    # one token, d = 8 (one chunk, 63 idle lanes), exactly 16 reads
+    n_q = n_hist - q_begin
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=n_hist + T + d, dtype=dtype)
+    out, lse = ar.full_fwd(h, w[q_begin:].contiguous(), q_begin=q_begin, n_q=n_q)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.full_fwd(h64, w64[q_begin:], q_begin=q_begin, n_q=n_q)
+    check_out(to_f64(out), ref, dtype)
+    check_lse(to_f64(lse), ref_lse)
