@@ -44,7 +44,7 @@ struct BbLane {
 
 // The reads la..lb of block group G, all in block group G (la >= G S).
 template <typename TO, int NCH, int G>
-__device__ __forceinline__ void bb_unit(const FwdParams& p, const float* src, const float* rsv,
+__device__ __forceinline__ void bb_group(const FwdParams& p, const float* src, const float* rsv,
                                         const bf16_t* hist_tok, int64_t t, int ln, const BbLane& q,
                                         int la, int lb) {
     constexpr int kV = G + 3;  // frozen-source dots, partial dot, partial sum of squares
@@ -198,7 +198,7 @@ __device__ __forceinline__ void bb_dispatch(int g, const FwdParams& p, const flo
                                             int la, int lb) {
     if constexpr (G < NBMAX) {
         if (g == G)
-            bb_unit<TO, NCH, G>(p, src, rsv, hist_tok, t, ln, q, la, lb);
+            bb_group<TO, NCH, G>(p, src, rsv, hist_tok, t, ln, q, la, lb);
         else
             bb_dispatch<TO, NCH, NBMAX, G + 1>(g, p, src, rsv, hist_tok, t, ln, q, la, lb);
     }
