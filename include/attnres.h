@@ -39,7 +39,9 @@
  * Memory and execution:
  *   * All tensor pointers are device pointers owned by the caller; the library
  *     allocates no device memory and keeps no state between calls apart from
- *     the thread-local error string.  The backward's scratch is caller-supplied.
+ *     the thread-local error string (and the dynamic-LDS limit of its own
+ *     kernels, which it raises to what a call needs before launching them).
+ *     The backward's scratch is caller-supplied.
  *   * d must be a multiple of 8 (8 <= d <= 4096); hist, out, dout, dhist and w
  *     must be 16-byte aligned, lse / rinv / dw 4-byte aligned.
  *   * T < 2^22 tokens and n_hist * T * d <= 2^40 elements per call
