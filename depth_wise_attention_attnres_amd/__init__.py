@@ -58,7 +58,7 @@ _lib.attnres_block_phase2.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp, _vp
                                       _int, _vp, _vp, _vp, _vp]
 _lib.attnres_bwd.restype = _int
 _lib.attnres_bwd.argtypes = [_int, _i64, _vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32,
-                             _vp, _int, _vp, _int, _vp, _vp, _sz, _vp]
+                             _vp, _int, _vp, _int, _int, _vp, _vp, _sz, _vp]
 _lib.attnres_bwd_workspace_bytes.restype = _sz
 _lib.attnres_bwd_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _i64, _i64, _i64]
 _lib.attnres_block_index_table.restype = _int
@@ -235,8 +235,16 @@ def block_phase1(blocks, n_src: int, v, w, *, partial=None, eps: float = 1e-6, r
     against blocks[0 .. n_src-1].  Returns (o, lse1); out0 / lse0 receive the
     group's first read if given."""
     import torch
+    # shapes first: the kernel writes blocks[n_src - 1] and rs[n_src - 1], so a
+    # wrong n_src or a short rs would write past the tensors
+    if blocks.dim() != 3:
+        raise ValueError(f"blocks must be [n_blocks, T, d], got shape {tuple(blocks.shape)}")
+    n_blocks, T, d = blocks.shape
+    if not 1 <= n_src <= n_blocks:
+        raise ValueError(f"n_src = {n_src} outside 1 .. blocks.shape[0] = {n_blocks}")
+    if rs is not None and (rs.dim() != 2 or rs.shape[0] < n_src or rs.shape[1] != T):
+        raise ValueError(f"rs must be [>= n_src = {n_src}, T = {T}], got shape {tuple(rs.shape)}")
     _require(blocks, "blocks", dtype=torch.float32)
-    _, T, d = blocks.shape
     _require(v, "v", shape=(T, d))
     n_reads = w.shape[0]
     _require(w, "w", dtype=torch.float32, shape=(n_reads, d))
@@ -357,10 +365,13 @@ def bwd_workspace_bytes(variant: int, S: int, n_hist: int, T: int, d: int, q_beg
 
 
 def bwd(variant: int, hist, w, dout, *, S: int = 1, q_begin: int = 0, eps: float = 1e-6,
-        dhist=None, dhist_dtype=None, dw=None, workspace=None):
+        dhist=None, dhist_dtype=None, dw=None, workspace=None, accumulate: bool = False):
     """Gradients of sum(out * dout) w.r.t. hist and w for the reads
-    q_begin .. q_begin + n_q - 1 (n_q = dout.shape[0]).  Returns (dhist, dw)."""
+    q_begin .. q_begin + n_q - 1 (n_q = dout.shape[0]).  Returns (dhist, dw).
+    accumulate=True adds them into the given fp32 dhist and dw instead."""
     import torch
+    if accumulate and (dhist is None or dw is None):
+        raise ValueError("accumulate=True needs the dhist and dw to add into")
     _require(hist, "hist")
     n_hist, T, d = hist.shape
     n_q = dout.shape[0]
@@ -381,8 +392,8 @@ def bwd(variant: int, hist, w, dout, *, S: int = 1, q_begin: int = 0, eps: float
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.attnres_bwd(variant, S, _ptr(hist), _dtype_code(hist), n_hist, T, d, _ptr(w),
                             q_begin, n_q, eps, _ptr(dout), _dtype_code(dout),
-                            _ptr(dhist), ddt, _ptr(dw), _ptr(workspace), ws_bytes,
-                            _stream(hist)))
+                            _ptr(dhist), ddt, 1 if accumulate else 0, _ptr(dw), _ptr(workspace),
+                            ws_bytes, _stream(hist)))
     return dhist, dw
 
 

@@ -362,8 +362,8 @@ size_t attnres_bwd_workspace_bytes(attnres_variant variant, int64_t S, int64_t n
 int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dtype hist_dtype,
                 int64_t n_hist, int64_t T, int64_t d, const float* w, int64_t q_begin, int64_t n_q,
                 float eps, const void* dout, attnres_dtype dout_dtype, void* dhist,
-                attnres_dtype dhist_dtype, float* dw, void* workspace, size_t workspace_bytes,
-                hipStream_t stream) {
+                attnres_dtype dhist_dtype, int accumulate, float* dw, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
     const char* fn = "attnres_bwd";
     if (variant != ATTNRES_FULL && variant != ATTNRES_BLOCK)
         return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad variant %d", fn, (int)variant);
@@ -375,6 +375,10 @@ int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dt
     if (S > n_hist) S = n_hist;  // S >= n_hist behaves like S = n_hist
     if (!valid_dtype(dout_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad dout dtype", fn);
     if (!valid_dtype(dhist_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad dhist dtype", fn);
+    if (accumulate != 0 && accumulate != 1)
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: accumulate must be 0 or 1", fn);
+    if (accumulate && dhist_dtype != ATTNRES_F32)
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: accumulate needs an fp32 dhist", fn);
     if (T == 0) return ok();
     if (dhist == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: dhist is NULL", fn);
     if (!aligned(dhist, 16)) return fail(ATTNRES_ERR_ALIGN, "%s: dhist is not 16-byte aligned", fn);
@@ -409,6 +413,7 @@ int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dt
     p.nq8 = (int)L.nq8;
     p.n_blk = (int)L.n_blk;
     p.nx = (int)L.nx;
+    p.accumulate = accumulate;
     p.eps = eps;
     p.inv_d = 1.0f / (float)d;
     p.hist_dt = hist_dtype;
@@ -424,10 +429,15 @@ int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dt
     p.ws_dwpart = reinterpret_cast<float*>(ws + L.off_dwpart);
     p.ws_dwstage = reinterpret_cast<float*>(ws + L.off_dwstage);
     if (n_q == 0) {
-        // no read: every history row gets a zero gradient
+        // no read: every history row gets a zero gradient (nothing to add)
+        if (accumulate) return ok();
         return hip_status(fn, attnres::launch_fill_zero(
                                   dhist, n_hist * T * d * (dhist_dtype == ATTNRES_BF16 ? 2 : 4), stream));
     }
+    if (!attnres::bwd_fits(p))
+        return fail(ATTNRES_ERR_UNSUPPORTED,
+                    "%s: the per-read coefficients of %" PRId64 " sources do not fit one workgroup's LDS",
+                    fn, L.nx);
     return hip_status(fn, attnres::launch_bwd(p, (int)L.n_chunks, (int)L.n_dw_groups, stream));
 }
 

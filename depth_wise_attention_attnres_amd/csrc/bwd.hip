@@ -821,6 +821,14 @@ __global__ __launch_bounds__(64) void bwd_dhist_kernel(BwdParams p) {
             const int j = rt0 + ii;
             if (j < rt1) {
                 const rsrc_t orr = make_rsrc(dh_tok + j * row_elems, (uint64_t)p.d * sizeof(TO));
+                if (p.accumulate) {  // uniform branch; the host allows it for fp32 dhist only
+                    Quad<TO> old;
+                    old.load(orr, o_off);
+                    float f[4];
+                    old.to_float(f);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dv[ii][e] += f[e];
+                }
                 Quad<TO>::store(orr, o_off, dv[ii]);
             }
         }
@@ -948,7 +956,7 @@ __global__ __launch_bounds__(256) void bwd_dw_final_kernel(BwdParams p, int grou
     if (idx >= total) return;
     float s = 0.f;
     for (int g = 0; g < groups; ++g) s += p.ws_dwstage[(int64_t)g * total + idx];
-    p.dw[idx] = s;
+    p.dw[idx] = p.accumulate ? p.dw[idx] + s : s;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* dst, int64_t n_words) {
@@ -1015,17 +1023,23 @@ int scores_mfma_tiles(const BwdParams& p, int& rtp) {
     return nb <= 4 ? nb : 0;
 }
 
-template <typename TI, typename TG>
-hipError_t launch_scores(const BwdParams& p, hipStream_t stream) {
+// streaming kernel: template arguments by chunks per lane
+constexpr int kStreamPF[9] = {0, 4, 2, 2, 2, 1, 1, 1, 1};
+constexpr int kStreamR[9] = {0, 4, 4, 2, 2, 1, 1, 1, 1};
+
+// Which kernel forms the per-read coefficients of a call, and its dynamic LDS.
+struct ScoresPlan {
+    enum Kind { NONE, MFMA, GROUP, STREAM } kind;
+    int rtp, nb, nwaves;  // MFMA: row tiling and waves per workgroup
+    size_t lds;           // MFMA, STREAM
+};
+
+ScoresPlan plan_scores(const BwdParams& p) {
+    ScoresPlan s{ScoresPlan::NONE, 0, 0, 0, 0};
+    const int max_lds = device_max_lds();
     int rtp = 0;
     const int nb = scores_mfma_tiles(p, rtp);
     if (nb > 0) {
-        const int64_t nw = (int64_t)p.n_q * p.d;
-        uint16_t* hi = p.ws_wsplit;
-        hipLaunchKernelGGL(split_w_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
-                           p.w, nw, hi, hi + nw, hi + 2 * nw);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
         const int nr = p.q_begin + p.n_q;
         // one wave per (row tile, read tile) pair whose reads see the tile
         const int na = (p.n_q + 31) / 32;
@@ -1038,31 +1052,67 @@ hipError_t launch_scores(const BwdParams& p, hipStream_t stream) {
         const size_t lds = sizeof(float) * (2 * (size_t)p.n_q * nr + (size_t)nb * 1024 + nr +
                                             2 * (size_t)p.n_q * p.nx + (size_t)nwaves * p.n_blk +
                                             p.nh8);
-        hipLaunchKernelGGL(bwd_scores_mfma_kernel, dim3((unsigned)p.T), dim3(64 * nwaves), lds,
-                           stream, p, rtp, nb);
+        if (lds <= (size_t)max_lds) {  // else one of the kernels below
+            s.kind = ScoresPlan::MFMA;
+            s.rtp = rtp;
+            s.nb = nb;
+            s.nwaves = nwaves;
+            s.lds = lds;
+            return s;
+        }
+    }
+    if (bwd_scores_group_applies(p)) {
+        s.kind = ScoresPlan::GROUP;
+        return s;
+    }
+    const int nch = (p.nc + 63) / 64;
+    if (nch < 1 || nch > 8) return s;
+    const size_t lds = sizeof(float) * (6 * (size_t)kStreamR[nch] * p.nx + p.n_blk);
+    if (lds > (size_t)max_lds) return s;  // too many sources for one token's LDS
+    s.kind = ScoresPlan::STREAM;
+    s.lds = lds;
+    return s;
+}
+
+template <typename TI, typename TG>
+hipError_t launch_scores(const BwdParams& p, const ScoresPlan& s, hipStream_t stream) {
+    if (s.kind == ScoresPlan::MFMA) {
+        const int64_t nw = (int64_t)p.n_q * p.d;
+        uint16_t* hi = p.ws_wsplit;
+        hipLaunchKernelGGL(split_w_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
+                           p.w, nw, hi, hi + nw, hi + 2 * nw);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = prepare_dynamic_lds((const void*)bwd_scores_mfma_kernel, s.lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(bwd_scores_mfma_kernel, dim3((unsigned)p.T), dim3(64 * s.nwaves), s.lds,
+                           stream, p, s.rtp, s.nb);
         return hipGetLastError();
     }
-    if (bwd_scores_group_applies(p)) return launch_bwd_scores_group(p, stream);
+    if (s.kind == ScoresPlan::GROUP) return launch_bwd_scores_group(p, stream);
+    if (s.kind != ScoresPlan::STREAM) return hipErrorInvalidValue;
     const int nch = (p.nc + 63) / 64;
+    auto go = [&](auto kern) {
+        const hipError_t e = prepare_dynamic_lds((const void*)kern, s.lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)p.T), dim3(64), s.lds, stream, p);
+        return hipGetLastError();
+    };
     switch (nch) {
-#define ATTNRES_SCORES(N, PF, R)                                                          \
-    case N:                                                                               \
-        hipLaunchKernelGGL((bwd_scores_kernel<TI, TG, N, PF, R>), dim3((unsigned)p.T),   \
-                           dim3(64), sizeof(float) * (6 * (size_t)R * p.nx + p.n_blk),    \
-                           stream, p);                                                    \
-        break;
-        ATTNRES_SCORES(1, 4, 4)
-        ATTNRES_SCORES(2, 2, 4)
-        ATTNRES_SCORES(3, 2, 2)
-        ATTNRES_SCORES(4, 2, 2)
-        ATTNRES_SCORES(5, 1, 1)
-        ATTNRES_SCORES(6, 1, 1)
-        ATTNRES_SCORES(7, 1, 1)
-        ATTNRES_SCORES(8, 1, 1)
+#define ATTNRES_SCORES(N)                                                                   \
+    case N:                                                                                 \
+        return go(bwd_scores_kernel<TI, TG, N, kStreamPF[N], kStreamR[N]>);
+        ATTNRES_SCORES(1)
+        ATTNRES_SCORES(2)
+        ATTNRES_SCORES(3)
+        ATTNRES_SCORES(4)
+        ATTNRES_SCORES(5)
+        ATTNRES_SCORES(6)
+        ATTNRES_SCORES(7)
+        ATTNRES_SCORES(8)
 #undef ATTNRES_SCORES
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <typename TI, typename TG, typename TO>
@@ -1100,12 +1150,15 @@ hipError_t dispatch_out(const BwdParams& p, int n_chunks, int groups, hipStream_
 
 template <typename TI, typename TG>
 hipError_t run_bwd(const BwdParams& p, int n_chunks, int groups, hipStream_t stream) {
-    hipError_t e = launch_scores<TI, TG>(p, stream);
+    const ScoresPlan s = plan_scores(p);
+    hipError_t e = launch_scores<TI, TG>(p, s, stream);
     if (e != hipSuccess) return e;
     return dispatch_out<TI, TG>(p, n_chunks, groups, stream);
 }
 
 }  // namespace
+
+bool bwd_fits(const BwdParams& p) { return plan_scores(p).kind != ScoresPlan::NONE; }
 
 hipError_t launch_bwd(const BwdParams& p, int n_chunks, int groups, hipStream_t stream) {
     if (p.hist_dt == ATTNRES_BF16)

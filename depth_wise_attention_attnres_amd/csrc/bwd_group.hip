@@ -327,8 +327,7 @@ __global__ __launch_bounds__(64 * kBgWaves) void bwd_scores_group_kernel(BwdPara
 template <typename TG, int NCH>
 hipError_t launch_bg_nch(const BwdParams& p, int nb, size_t lds, hipStream_t stream) {
     auto go = [&](auto kern) {
-        const hipError_t e =
-            hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const hipError_t e = prepare_dynamic_lds((const void*)kern, lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)p.T), dim3(64 * kBgWaves), lds, stream, p, nb);
         return hipGetLastError();
@@ -351,10 +350,7 @@ int bg_sources(const BwdParams& p, size_t* lds) {
     if (p.T * 64 * kBgWaves >= ((int64_t)1 << 32)) return 0;
     const int nb = 1 + (p.q_begin + p.n_q - 1) / p.S;
     if (nb > kBgMaxSources) return 0;
-    int dev = 0, max_lds = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        return 0;
+    const int max_lds = device_max_lds();
     const int64_t bytes = bg_lds_bytes(nb, p.d, p.n_q);
     if (bytes > max_lds) return 0;
     *lds = (size_t)bytes;

@@ -433,8 +433,7 @@ __global__ __launch_bounds__(64 * kBatchWaves) void full_batch_kernel(FwdParams 
 template <typename TI, typename TO, int NCH>
 hipError_t launch_batch(const FwdParams& p, int n_rows, int n_lds, int n_pad, size_t lds,
                         hipStream_t stream) {
-    const hipError_t e = hipFuncSetAttribute((const void*)full_batch_kernel<TI, TO, NCH>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = prepare_dynamic_lds((const void*)full_batch_kernel<TI, TO, NCH>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((full_batch_kernel<TI, TO, NCH>), dim3((unsigned)p.T), dim3(64 * kBatchWaves), lds,
                        stream, p, n_rows, n_lds, n_pad);
@@ -469,10 +468,8 @@ BatchPlan batch_plan(const FwdParams& p, attnres_dtype hist_dt) {
     if (p.nc > (hist_dt == ATTNRES_BF16 ? 4 : 3) * 64) return b;
     // one workgroup of 64 * kBatchWaves work-items per token, in a 32-bit grid
     if (p.T * 64 * kBatchWaves >= ((int64_t)1 << 32)) return b;
-    int dev = 0, max_lds = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        return b;
+    const int max_lds = device_max_lds();
+    if (max_lds <= 0) return b;
     const int elem = hist_dt == ATTNRES_BF16 ? 2 : 4;
     b.n_rows = p.q_begin + p.n_q;
     b.n_pad = (b.n_rows + 3) & ~3;

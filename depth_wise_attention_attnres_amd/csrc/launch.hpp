@@ -86,6 +86,7 @@ struct BwdParams {
     int64_t T;
     int d, nc, n_hist, q_begin, n_q, S;
     int nh8, nq8, n_blk, nx;
+    int accumulate;     // 1: dhist += (fp32 only) and dw += instead of overwriting
     float eps, inv_d;
     attnres_dtype hist_dt, dout_dt, dhist_dt;
     float* ws_a1;       // [T][n_q][nh8]   alpha of the source holding each row
@@ -98,6 +99,8 @@ struct BwdParams {
     uint16_t* ws_wsplit;  // [3][n_q][d] bf16: w = hi + mid + lo (matrix-core scores)
 };
 hipError_t launch_bwd(const BwdParams& p, int n_chunks, int n_dw_groups, hipStream_t stream);
+// whether some coefficient kernel takes the call (its LDS fits the device)
+bool bwd_fits(const BwdParams& p);
 // the backward's per-read coefficients for Block calls with many reads, one
 // wave per block group (bwd_group.hip): whether the call qualifies, the launch
 bool bwd_scores_group_applies(const BwdParams& p);
@@ -143,5 +146,14 @@ hipError_t launch_query_proj(const void* x, const void* W, float* q, int64_t n_q
 hipError_t launch_block_phase2(const Phase2Params& p, hipStream_t stream);
 // zero `bytes` (a multiple of 4) of device memory with a kernel
 hipError_t launch_fill_zero(void* dst, int64_t bytes, hipStream_t stream);
+
+// LDS per workgroup of the current device (0 if it cannot be queried)
+int device_max_lds();
+// Before launching `kernel` with `bytes` of dynamic LDS: raises the kernel's
+// limit on the current device to the device maximum, once per (kernel,
+// device) for the process (never per call, so concurrent callers cannot lower
+// it under each other), and returns hipErrorInvalidValue if `bytes` exceeds
+// that maximum.
+hipError_t prepare_dynamic_lds(const void* kernel, size_t bytes);
 
 }  // namespace attnres

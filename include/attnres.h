@@ -39,9 +39,10 @@
  * Memory and execution:
  *   * All tensor pointers are device pointers owned by the caller; the library
  *     allocates no device memory and keeps no state between calls apart from
- *     the thread-local error string (and the dynamic-LDS limit of its own
- *     kernels, which it raises to what a call needs before launching them).
- *     The backward's scratch is caller-supplied.
+ *     the thread-local error string and the dynamic-LDS limit of its
+ *     LDS-staged kernels, which it raises to the device maximum once per
+ *     kernel and device (never lowered).  The backward's scratch is
+ *     caller-supplied.
  *   * d must be a multiple of 8 (8 <= d <= 4096); hist, out, dout, dhist and w
  *     must be 16-byte aligned, lse / rinv / dw 4-byte aligned.
  *   * T < 2^22 tokens and n_hist * T * d <= 2^40 elements per call
@@ -53,7 +54,8 @@
  *     (asynchronous).  Outputs must not alias inputs.
  *   * T == 0 or n_q == 0 is a valid empty call: nothing is launched.
  *   * NaN / Inf inputs propagate; they are not checked.
- *   * Thread-safe: calls share no mutable state.
+ *   * Thread-safe: calls share no mutable state apart from the one-time LDS
+ *     limit above, which is set under a lock.
  *
  * Status: every entry point returns an attnres_status; attnres_last_error()
  * gives a human-readable detail of the last failure on the calling thread.
@@ -237,19 +239,29 @@ int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_
  *   (no lse argument: the softmax of each read is renormalised over its own
  *   recomputed scores, so a read with one source gets weight exactly 1)
  *   dout, dout_dtype   [n_q][T][d], F32 or BF16
- *   dhist, dhist_dtype [n_hist][T][d], F32 or BF16: overwritten; rows no read of
- *                      the call sees are set to zero
- *   dw                 [n_q][d] fp32: overwritten (summed over tokens in a fixed
- *                      order, so results are bitwise reproducible)
+ *   dhist, dhist_dtype [n_hist][T][d], F32 or BF16
+ *   accumulate         0: dhist and dw are overwritten (rows no read of the
+ *                      call sees get zero gradient).  1: the call's gradients
+ *                      are added, dhist += ... and dw += ..., so a model that
+ *                      runs the backward per group of reads (the schedule of
+ *                      DataCamp's "two-phase computation") or per token range
+ *                      sums the pieces in place; needs an F32 dhist
+ *                      (ATTNRES_ERR_INVALID_ARG otherwise), and leaves rows no
+ *                      read sees unchanged.
+ *   dw                 [n_q][d] fp32 (summed over tokens in a fixed order, so
+ *                      results are bitwise reproducible)
  *   workspace          device scratch of at least attnres_bwd_workspace_bytes()
  *                      bytes, 256-byte aligned; contents on entry are ignored
+ * The per-read coefficients of a token are formed in one workgroup's LDS;
+ * when a call's sources do not fit (Full with more than about 1600 rows) it
+ * returns ATTNRES_ERR_UNSUPPORTED.
  */
 int attnres_bwd(attnres_variant variant, int64_t S, const void* hist,
                 attnres_dtype hist_dtype, int64_t n_hist, int64_t T, int64_t d,
                 const float* w, int64_t q_begin, int64_t n_q, float eps,
                 const void* dout, attnres_dtype dout_dtype,
-                void* dhist, attnres_dtype dhist_dtype, float* dw, void* workspace,
-                size_t workspace_bytes, hipStream_t stream);
+                void* dhist, attnres_dtype dhist_dtype, int accumulate, float* dw,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace attnres_bwd needs for these sizes (0 on invalid sizes). */
 size_t attnres_bwd_workspace_bytes(attnres_variant variant, int64_t S, int64_t n_hist,

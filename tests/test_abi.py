@@ -150,9 +150,9 @@ def test_block_index_table_validation(ar):
 
 
 def _bwd(ar, variant=0, S=1, hist=P, hdt=BF16, n_hist=4, T=16, d=64, w=P2, q_begin=0, n_q=4,
-         eps=1e-6, dout=P, gdt=BF16, dhist=P2, ddt=BF16, dw=P3, ws=P, ws_bytes=1 << 40):
+         eps=1e-6, dout=P, gdt=BF16, dhist=P2, ddt=BF16, acc=0, dw=P3, ws=P, ws_bytes=1 << 40):
     return ar.raw().attnres_bwd(variant, S, hist, hdt, n_hist, T, d, w, q_begin, n_q, eps,
-                                dout, gdt, dhist, ddt, dw, ws, ws_bytes, None)
+                                dout, gdt, dhist, ddt, acc, dw, ws, ws_bytes, None)
 
 
 def test_bwd_validation(ar):
@@ -172,6 +172,10 @@ def test_bwd_validation(ar):
     assert "needed" in ar.last_error()
     assert _bwd(ar, ws=P + 64) == ALIGN
     assert _bwd(ar, T=0) == OK
+    assert _bwd(ar, acc=2) == INVALID
+    assert _bwd(ar, acc=1) == INVALID  # accumulating needs an fp32 dhist
+    assert "fp32" in ar.last_error()
+    assert _bwd(ar, acc=1, ddt=F32, T=0) == OK
 
 
 def test_bwd_workspace_size(ar):
@@ -267,3 +271,33 @@ def test_package_fails_loudly_without_the_library(tmp_path):
                        cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "not built" in r.stderr
+
+
+def test_block_phase1_binding_rejects_bad_n_src_and_rs(ar):
+    # the kernel writes blocks[n_src - 1] and rs[n_src - 1]: the binding checks
+    # both shapes before anything reaches the library (CPU tensors suffice,
+    # the shape checks come before the device check)
+    import torch
+    blocks = torch.zeros((3, 4, 16))
+    v = torch.zeros((4, 16))
+    w = torch.zeros((2, 16))
+    with pytest.raises(ValueError, match="n_src"):
+        ar.block_phase1(blocks, 4, v, w)
+    with pytest.raises(ValueError, match="n_src"):
+        ar.block_phase1(blocks, 0, v, w)
+    with pytest.raises(ValueError, match="rs"):
+        ar.block_phase1(blocks, 3, v, w, rs=torch.zeros((2, 4)))
+    with pytest.raises(ValueError, match="rs"):
+        ar.block_phase1(blocks, 2, v, w, rs=torch.zeros((3, 5)))
+    with pytest.raises(ValueError, match="blocks"):
+        ar.block_phase1(torch.zeros((4, 16)), 1, v, w)
+    # valid shapes get as far as the device check
+    with pytest.raises(ValueError, match="GPU"):
+        ar.block_phase1(blocks, 3, v, w, rs=torch.zeros((3, 4)))
+
+
+def test_bwd_binding_accumulate_needs_targets(ar):
+    import torch
+    h = torch.zeros((3, 4, 16))
+    with pytest.raises(ValueError, match="accumulate"):
+        ar.bwd(ar.FULL, h, torch.zeros((3, 16)), torch.zeros((3, 4, 16)), accumulate=True)

@@ -126,3 +126,88 @@ def test_bwd_group_kernel_edges(ar, oracle, n_hist, T, d, S, q_begin):
     # exactly 16 reads, S at the history length, one token, d = 8
     h, w, g = _case(n_hist, T, d, seed=n_hist * 3 + T + S, dtype="bf16", q_begin=q_begin)
     _check(ar, oracle, BLOCK, S, h, w, g, "bf16", q_begin=q_begin)
+
+
+@pytest.mark.parametrize("variant,S", [(FULL, 1), (BLOCK, 4)])
+def test_bwd_workload_full_dw(ar, oracle, variant, S):
+    # The 48-sublayer, d = 1024, 4 x 4096-token workload at its full size, in
+    # the launch configuration the benchmark times: dw is a reduction over all
+    # 16384 tokens (512 chunks of 32 tokens summed in 16 groups of 32), so the
+    # oracle runs on every token, 2048 at a time, its chunk dw summed in fp64.
+    # dhist is compared on every token too.
+    from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs
+    wl = WORKLOADS["fwdbwd_L24_d1024"]
+    h, w, g = device_inputs(wl, DEV)
+    dh, dw = _run(ar, variant, S, h, w, g)
+    ref_dw = np.zeros(tuple(dw.shape), np.float64)
+    step = 2048
+    for t0 in range(0, wl.T, step):
+        hs = to_f64(h[:, t0:t0 + step])
+        gs = to_f64(g[:, t0:t0 + step])
+        ref_dh, part_dw = oracle.bwd(variant, hs, to_f64(w), gs, S=S)
+        ref_dw += part_dw
+        check_out(to_f64(dh[:, t0:t0 + step])[None], ref_dh[None], "bf16",
+                  what=f"dhist tokens {t0}..{t0 + step}")
+    check_rel(to_f64(dw), ref_dw, 1e-5, "dw (all tokens)")
+
+
+@pytest.mark.parametrize("variant,S,dtype", [(FULL, 1, "f32"), (FULL, 1, "bf16"),
+                                             (BLOCK, 4, "f32"), (BLOCK, 4, "bf16")])
+def test_bwd_dw_many_chunks_per_group(ar, oracle, variant, S, dtype):
+    # 2080 tokens: 65 chunks of 32 (the last one ragged) in 16 reduction
+    # groups of 5, so every group sums several chunks and the last group fewer
+    h, w, g = _case(17, 2080, 64, seed=11 + S, dtype=dtype, w_sigma=0.2)
+    _check(ar, oracle, variant, S, h, w, g, dtype)
+
+
+@pytest.mark.parametrize("variant,S", [(FULL, 1), (BLOCK, 3)])
+def test_bwd_accumulate(ar, oracle, variant, S):
+    # accumulate=True: the gradients of two read ranges, added into the same
+    # fp32 dhist (starting from non-zero values), equal the oracle's gradient
+    # of all reads plus the start values; dw rows of the two ranges are
+    # disjoint.  Then dw accumulated over two token halves equals dw of all
+    # tokens.
+    n_hist, T, d, k = 14, 40, 136, 6
+    h, w, g = _case(n_hist, T, d, seed=21 + S, dtype="bf16")
+    ref_dh, ref_dw = oracle.bwd(variant, to_f64(h), to_f64(w), to_f64(g), S=S)
+    start = torch.randn((n_hist, T, d), generator=torch.Generator().manual_seed(3)).to(DEV)
+    dh = start.clone()
+    dw = torch.zeros((n_hist, d), dtype=torch.float32, device=DEV)
+    ar.bwd(variant, h, w[:k].contiguous(), g[:k].contiguous(), S=S, q_begin=0, dhist=dh,
+           dw=dw[:k], accumulate=True)
+    ar.bwd(variant, h, w[k:].contiguous(), g[k:].contiguous(), S=S, q_begin=k, dhist=dh,
+           dw=dw[k:], accumulate=True)
+    torch.cuda.synchronize()
+    check_rel(to_f64(dh) - to_f64(start), ref_dh, 1e-5, "dhist accumulated over read ranges")
+    check_rel(to_f64(dw), ref_dw, 1e-5, "dw of two read ranges")
+
+    half = T // 2
+    dw2 = torch.full((n_hist, d), 0.25, dtype=torch.float32, device=DEV)
+    for sl in (slice(0, half), slice(half, T)):
+        hs, gs = h[:, sl].contiguous(), g[:, sl].contiguous()
+        dhs = torch.zeros((n_hist, hs.shape[1], d), dtype=torch.float32, device=DEV)
+        ar.bwd(variant, hs, w, gs, S=S, dhist=dhs, dw=dw2, accumulate=True)
+    torch.cuda.synchronize()
+    check_rel(to_f64(dw2) - 0.25, ref_dw, 1e-5, "dw accumulated over token halves")
+
+
+def test_bwd_accumulate_rows_no_read_sees(ar, oracle):
+    # reads 0..4 of a 12-row history: rows 5.. get no gradient, so an
+    # accumulating call leaves them as they were
+    h, w, g = _case(12, 9, 64, seed=31, dtype="f32", n_q=5)
+    start = torch.randn((12, 9, 64), generator=torch.Generator().manual_seed(4)).to(DEV)
+    dh = start.clone()
+    dw = torch.zeros((5, 64), dtype=torch.float32, device=DEV)
+    ar.bwd(FULL, h, w, g, dhist=dh, dw=dw, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dh[5:], start[5:])
+    ref_dh, ref_dw = oracle.bwd(FULL, to_f64(h), to_f64(w), to_f64(g))
+    check_rel(to_f64(dh) - to_f64(start), ref_dh, 1e-5, "dhist")
+    check_rel(to_f64(dw), ref_dw, 1e-5, "dw")
+
+
+def test_bwd_mfma_scores_beyond_64k_lds(ar, oracle):
+    # Full, bf16, 64 reads from row 0: the matrix-core coefficient kernel
+    # needs about 80 KB of LDS per workgroup, above the 64 KB default limit
+    h, w, g = _case(64, 7, 128, seed=41, dtype="bf16", w_sigma=0.1)
+    _check(ar, oracle, FULL, 1, h, w, g, "bf16")

@@ -61,8 +61,9 @@ SHAPES = [(16, 37, 64), (19, 50, 200), (33, 70, 520), (21, 33, 1032), (18, 9, 20
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("n_hist,T,d", SHAPES)
 def test_batch_all_reads(ar, oracle, dtype, n_hist, T, d):
-    if not _qualifies(n_hist, n_hist, d, dtype):
-        pytest.skip("rows do not fit in LDS at this dtype (the streaming kernel serves it)")
+    # fp32 at (18, 9, 2048) and (65, 40, 896) does not qualify (the rows do
+    # not fit in LDS at 4 bytes): the streaming kernel serves those calls, and
+    # they are checked against the oracle all the same
     h, w, h64, w64 = _inputs(n_hist, T, d, seed=n_hist * 31 + d, dtype=dtype)
     out, lse = ar.full_fwd(h, w)
     torch.cuda.synchronize()
