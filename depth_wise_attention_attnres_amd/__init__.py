@@ -29,7 +29,8 @@ STATUS = {0: "ATTNRES_OK", 1: "ATTNRES_ERR_INVALID_ARG", 2: "ATTNRES_ERR_UNSUPPO
 # every symbol include/attnres.h declares
 EXPORTS = ["attnres_full_fwd", "attnres_full_fwd_q", "attnres_query_proj", "attnres_block_fwd",
            "attnres_block_phase1", "attnres_block_phase2",
-           "attnres_bwd", "attnres_bwd_workspace_bytes", "attnres_block_index_table",
+           "attnres_bwd", "attnres_bwd_noalloc", "attnres_bwd_noalloc_max_workspace",
+           "attnres_bwd_workspace_bytes", "attnres_block_index_table",
            "attnres_status_string", "attnres_last_error"]
 
 if not os.path.exists(LIBRARY):
@@ -59,6 +60,11 @@ _lib.attnres_block_phase2.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp, _vp
 _lib.attnres_bwd.restype = _int
 _lib.attnres_bwd.argtypes = [_int, _i64, _vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32,
                              _vp, _int, _vp, _int, _int, _vp, _vp, _sz, _vp]
+_lib.attnres_bwd_noalloc.restype = _int
+_lib.attnres_bwd_noalloc.argtypes = [_int, _i64, _vp, _int, _i64, _i64, _i64, _vp, _i64, _i64,
+                                     _f32, _vp, _int, _vp, _int, _int, _vp, _vp]
+_lib.attnres_bwd_noalloc_max_workspace.restype = _sz
+_lib.attnres_bwd_noalloc_max_workspace.argtypes = []
 _lib.attnres_bwd_workspace_bytes.restype = _sz
 _lib.attnres_bwd_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _i64, _i64, _i64]
 _lib.attnres_block_index_table.restype = _int
@@ -395,6 +401,30 @@ def bwd(variant: int, hist, w, dout, *, S: int = 1, q_begin: int = 0, eps: float
                             _ptr(dhist), ddt, 1 if accumulate else 0, _ptr(dw), _ptr(workspace),
                             ws_bytes, _stream(hist)))
     return dhist, dw
+
+
+def bwd_noalloc(variant: int, hist, w, dout, dhist, dw, *, S: int = 1, q_begin: int = 0,
+                eps: float = 1e-6, accumulate: bool = False):
+    """attnres_bwd_noalloc: as bwd, into the caller's dhist and dw, with the
+    library's static device workspace (no allocation, in the binding either).
+    Returns (dhist, dw)."""
+    import torch
+    _require(hist, "hist")
+    n_hist, T, d = hist.shape
+    n_q = dout.shape[0]
+    _require(w, "w", dtype=torch.float32, shape=(n_q, d))
+    _require(dout, "dout", shape=(n_q, T, d))
+    _require(dhist, "dhist", shape=(n_hist, T, d))
+    _require(dw, "dw", dtype=torch.float32, shape=(n_q, d))
+    _check(_lib.attnres_bwd_noalloc(variant, S, _ptr(hist), _dtype_code(hist), n_hist, T, d,
+                                    _ptr(w), q_begin, n_q, eps, _ptr(dout), _dtype_code(dout),
+                                    _ptr(dhist), _dtype_code(dhist), 1 if accumulate else 0,
+                                    _ptr(dw), _stream(hist)))
+    return dhist, dw
+
+
+def bwd_noalloc_max_workspace() -> int:
+    return int(_lib.attnres_bwd_noalloc_max_workspace())
 
 
 def block_index_table(n_hist: int, S: int, q_begin: int = 0, n_q: int | None = None) -> np.ndarray:

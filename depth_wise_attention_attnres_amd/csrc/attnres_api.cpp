@@ -359,12 +359,17 @@ size_t attnres_bwd_workspace_bytes(attnres_variant variant, int64_t S, int64_t n
     return (size_t)attnres::bwd_layout(S, n_hist, T, d, n_q).bytes;
 }
 
-int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dtype hist_dtype,
-                int64_t n_hist, int64_t T, int64_t d, const float* w, int64_t q_begin, int64_t n_q,
-                float eps, const void* dout, attnres_dtype dout_dtype, void* dhist,
-                attnres_dtype dhist_dtype, int accumulate, float* dw, void* workspace,
-                size_t workspace_bytes, hipStream_t stream) {
-    const char* fn = "attnres_bwd";
+}  // extern "C"
+
+namespace {
+
+// attnres_bwd and attnres_bwd_noalloc; the latter passes use_scratch and no
+// workspace, and takes the static device array instead
+int bwd_impl(const char* fn, bool use_scratch, attnres_variant variant, int64_t S,
+             const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T, int64_t d,
+             const float* w, int64_t q_begin, int64_t n_q, float eps, const void* dout,
+             attnres_dtype dout_dtype, void* dhist, attnres_dtype dhist_dtype, int accumulate,
+             float* dw, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (variant != ATTNRES_FULL && variant != ATTNRES_BLOCK)
         return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad variant %d", fn, (int)variant);
     int st = check_common(fn, hist, hist_dtype, n_hist, T, d, w, q_begin, n_q, eps);
@@ -389,6 +394,16 @@ int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dt
         if (!aligned(dw, 4)) return fail(ATTNRES_ERR_ALIGN, "%s: dw is not 4-byte aligned", fn);
     }
     const attnres::BwdLayout L = attnres::bwd_layout(S, n_hist, T, d, n_q);
+    if (use_scratch && n_q > 0) {
+        if (L.bytes > attnres::kBwdScratchBytes)
+            return fail(ATTNRES_ERR_UNSUPPORTED,
+                        "%s: needs %" PRId64 " bytes of workspace; the static scratch holds %" PRId64
+                        " (split the call by tokens, or use attnres_bwd with a workspace)",
+                        fn, L.bytes, attnres::kBwdScratchBytes);
+        const hipError_t e = attnres::bwd_scratch(&workspace);
+        if (e != hipSuccess) return hip_status(fn, e);
+        workspace_bytes = (size_t)attnres::kBwdScratchBytes;
+    }
     if (n_q > 0) {
         if (workspace == nullptr || workspace_bytes < (size_t)L.bytes)
             return fail(ATTNRES_ERR_WORKSPACE, "%s: workspace of %zu bytes, %" PRId64 " needed", fn,
@@ -440,5 +455,31 @@ int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dt
                     fn, L.nx);
     return hip_status(fn, attnres::launch_bwd(p, (int)L.n_chunks, (int)L.n_dw_groups, stream));
 }
+
+}  // namespace
+
+extern "C" {
+
+int attnres_bwd(attnres_variant variant, int64_t S, const void* hist, attnres_dtype hist_dtype,
+                int64_t n_hist, int64_t T, int64_t d, const float* w, int64_t q_begin, int64_t n_q,
+                float eps, const void* dout, attnres_dtype dout_dtype, void* dhist,
+                attnres_dtype dhist_dtype, int accumulate, float* dw, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+    return bwd_impl("attnres_bwd", false, variant, S, hist, hist_dtype, n_hist, T, d, w, q_begin,
+                    n_q, eps, dout, dout_dtype, dhist, dhist_dtype, accumulate, dw, workspace,
+                    workspace_bytes, stream);
+}
+
+int attnres_bwd_noalloc(attnres_variant variant, int64_t S, const void* hist,
+                        attnres_dtype hist_dtype, int64_t n_hist, int64_t T, int64_t d,
+                        const float* w, int64_t q_begin, int64_t n_q, float eps, const void* dout,
+                        attnres_dtype dout_dtype, void* dhist, attnres_dtype dhist_dtype,
+                        int accumulate, float* dw, hipStream_t stream) {
+    return bwd_impl("attnres_bwd_noalloc", true, variant, S, hist, hist_dtype, n_hist, T, d, w,
+                    q_begin, n_q, eps, dout, dout_dtype, dhist, dhist_dtype, accumulate, dw,
+                    nullptr, 0, stream);
+}
+
+size_t attnres_bwd_noalloc_max_workspace(void) { return (size_t)attnres::kBwdScratchBytes; }
 
 }  // extern "C"

@@ -101,6 +101,11 @@ struct BwdParams {
 hipError_t launch_bwd(const BwdParams& p, int n_chunks, int n_dw_groups, hipStream_t stream);
 // whether some coefficient kernel takes the call (its LDS fits the device)
 bool bwd_fits(const BwdParams& p);
+// Size of the static device array that serves as the backward's workspace for
+// callers that cannot allocate, and its address on the current device (taken
+// once per device; bwd_scratch.hip).
+constexpr int64_t kBwdScratchBytes = (int64_t)64 << 20;
+hipError_t bwd_scratch(void** ptr);
 // the backward's per-read coefficients for Block calls with many reads, one
 // wave per block group (bwd_group.hip): whether the call qualifies, the launch
 bool bwd_scores_group_applies(const BwdParams& p);

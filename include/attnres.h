@@ -263,6 +263,29 @@ int attnres_bwd(attnres_variant variant, int64_t S, const void* hist,
                 void* dhist, attnres_dtype dhist_dtype, int accumulate, float* dw,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * attnres_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments and results as attnres_bwd; the workspace is a static device
+ * array of attnres_bwd_noalloc_max_workspace() bytes (64 MiB) that the
+ * library holds on every GPU it runs on until the process ends.  A call
+ * whose attnres_bwd_workspace_bytes() exceeds it returns
+ * ATTNRES_ERR_UNSUPPORTED (split such calls by tokens).  The call allocates
+ * nothing; the first call on a device looks the array's address up once.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (two streams, two threads) race and must be serialised by the
+ * caller.
+ */
+int attnres_bwd_noalloc(attnres_variant variant, int64_t S, const void* hist,
+                        attnres_dtype hist_dtype, int64_t n_hist, int64_t T, int64_t d,
+                        const float* w, int64_t q_begin, int64_t n_q, float eps,
+                        const void* dout, attnres_dtype dout_dtype,
+                        void* dhist, attnres_dtype dhist_dtype, int accumulate, float* dw,
+                        hipStream_t stream);
+
+/* Bytes of the static workspace attnres_bwd_noalloc uses. */
+size_t attnres_bwd_noalloc_max_workspace(void);
+
 /* Bytes of workspace attnres_bwd needs for these sizes (0 on invalid sizes). */
 size_t attnres_bwd_workspace_bytes(attnres_variant variant, int64_t S, int64_t n_hist,
                                    int64_t T, int64_t d, int64_t q_begin, int64_t n_q);

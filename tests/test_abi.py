@@ -301,3 +301,21 @@ def test_bwd_binding_accumulate_needs_targets(ar):
     h = torch.zeros((3, 4, 16))
     with pytest.raises(ValueError, match="accumulate"):
         ar.bwd(ar.FULL, h, torch.zeros((3, 16)), torch.zeros((3, 4, 16)), accumulate=True)
+
+
+def test_bwd_noalloc_validation(ar):
+    lib = ar.raw()
+    assert lib.attnres_bwd_noalloc_max_workspace() == 64 << 20
+
+    def nb(n_hist=4, T=16, d=64, n_q=4, ddt=BF16, acc=0, dout=P, dw=P3):
+        return lib.attnres_bwd_noalloc(0, 1, P, BF16, n_hist, T, d, P2, 0, n_q, 1e-6, dout, BF16,
+                                       P2, ddt, acc, dw, None)
+    assert nb(d=12) == ALIGN
+    assert nb(dout=None) == INVALID
+    assert nb(acc=1) == INVALID
+    assert nb(T=0) == OK
+    # a call whose workspace exceeds the static array is refused on the host
+    need = lib.attnres_bwd_workspace_bytes(0, 1, 49, 4096, 1024, 0, 49)
+    assert need > 64 << 20
+    assert nb(n_hist=49, T=4096, d=1024, n_q=49) == UNSUPPORTED
+    assert "static scratch" in ar.last_error()
