@@ -32,26 +32,48 @@ constexpr int kBbWaves = 8;
 constexpr int kBbMinReads = 16;
 constexpr int kBbMaxSources = 13;  // v_0 + completed blocks a read of the call sees
 
-// LDS: sources [nb][d] fp32, their RMS scales [nb rounded up to 4], counter
-__host__ __device__ inline int64_t bb_lds_bytes(int nb, int d) {
-    return (int64_t)nb * d * 4 + (int64_t)((nb + 3) & ~3) * 4 + 16;
-}
-
-struct BbLane {
-    bool live[4];
-    uint32_t in_off[4], out_off[4], w_off[4];
+// LDS: the frozen sources in fp32, then their RMS scales [NBMAX] and the
+// group counter.  Element e of 16-byte chunk ch = 64 c2 + ln of source c sits
+// at float ((e / 4) NCH + c2) NBMAX + c) 256 + 4 ln + e % 4: every offset past
+// the lane's base is a compile-time constant (an immediate of the LDS
+// instruction, no address register per source), and a wave's 16-byte reads and
+// writes cover 1 KB of consecutive bytes (no bank conflicts).
+template <int NCH, int NBMAX>
+struct BbLds {
+    static constexpr int kSrcFloats = 2 * NCH * NBMAX * 256;
+    static constexpr int kBytes = kSrcFloats * 4 + ((NBMAX + 3) & ~3) * 4 + 16;
+    __device__ static constexpr int at(int plane, int c2, int c) {
+        return ((plane * NCH + c2) * NBMAX + c) * 256;
+    }
 };
 
+// 8 fp32 values of chunk c2 of source c (lane base `sl` = src + 4 ln)
+template <int NCH, int NBMAX>
+__device__ __forceinline__ void bb_lds_read(const float* sl, int c2, int c, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(sl + BbLds<NCH, NBMAX>::at(0, c2, c));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(sl + BbLds<NCH, NBMAX>::at(1, c2, c));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        x[q] = a[q];
+        x[4 + q] = b[q];
+    }
+}
+
 // The reads la..lb of block group G, all in block group G (la >= G S).
-template <typename TO, int NCH, int G>
-__device__ __forceinline__ void bb_group(const FwdParams& p, const float* src, const float* rsv,
-                                        const bf16_t* hist_tok, int64_t t, int ln, const BbLane& q,
-                                        int la, int lb) {
+// Lane ln owns chunks ch = c2 * 64 + ln (c2 < NCH) of d; chunks past d are
+// dead: their global loads return zeros and their stores are dropped (buffer
+// range checks), and they skip LDS.
+template <typename TO, int NCH, int NBMAX, int G>
+__device__ __forceinline__ void bb_group(const FwdParams& p, const float* sl, const float* rsv,
+                                        const bf16_t* hist_tok, int64_t t, int ln, int la, int lb) {
     constexpr int kV = G + 3;  // frozen-source dots, partial dot, partial sum of squares
     const int d = p.d;
     const int64_t row_elems = p.T * (int64_t)d;
     const uint64_t tok_bytes = (uint64_t)d * 2;
     const int g0 = G * p.S;  // the group's first read; its partial sums start at row g0 + 1
+    const uint32_t in_off = (uint32_t)ln * 16;   // bf16 chunk c2: + 1024 c2
+    const uint32_t w_off = (uint32_t)ln * 32;    // fp32 chunk c2: + 2048 c2
+    const uint32_t out_off = (uint32_t)ln * 8 * sizeof(TO);
 
     float rs2[G + 1];  // RMS scales of the frozen sources, log2 units
 #pragma unroll
@@ -74,7 +96,7 @@ __device__ __forceinline__ void bb_group(const FwdParams& p, const float* src, c
     auto issue_row = [&](Chunk<bf16_t> (&r)[NCH], int i) {
         const rsrc_t rr = make_rsrc(hist_tok + i * row_elems, tok_bytes);
 #pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2) r[c2].load(rr, q.in_off[c2]);
+        for (int c2 = 0; c2 < NCH; ++c2) r[c2].load(rr, in_off + 1024u * c2);
     };
     // rows g0+1 .. la-1 (the part of the partial sum before the first read), four at a time
     for (int i0 = g0 + 1; i0 < la; i0 += 4) {
@@ -88,44 +110,53 @@ __device__ __forceinline__ void bb_group(const FwdParams& p, const float* src, c
     }
     Chunk<bf16_t> rl[NCH];  // row l of the current read, in flight
     if (la > g0) issue_row(rl, la);
-    Chunk<float> wq[NCH];   // query of the current read, in flight
+    // query of the current read, in flight; its fp32 bits are used in place,
+    // and the next read's query is requested once the dots are done
+    Chunk<float> wq[NCH];
     auto issue_w = [&](int l) {
         const rsrc_t wr = make_rsrc(p.w + (int64_t)(l - p.q_begin) * d, (uint64_t)d * 4);
 #pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2) wq[c2].load(wr, q.w_off[c2]);
+        for (int c2 = 0; c2 < NCH; ++c2) wq[c2].load(wr, w_off + 2048u * c2);
     };
     issue_w(la);
 
     for (int l = la; l <= lb; ++l) {
-        float wv[NCH][8];
-#pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2) wq[c2].to_float(wv[c2]);
-        if (l < lb) issue_w(l + 1);
         const bool has_p = l > g0;
         if (has_p) add_row(rl);             // row l joins the partial sum
         if (l < lb) issue_row(rl, l + 1);   // the next read's row (always past g0)
 
         // dots with the frozen sources and the partial sum
+        // (source by source, each fenced off for the scheduler, so that only
+        // one source's chunks are in registers at a time)
         float v[kV];
 #pragma unroll
         for (int j = 0; j < kV; ++j) v[j] = 0.f;
 #pragma unroll
         for (int c2 = 0; c2 < NCH; ++c2) {
-            if (!q.live[c2]) continue;
-            const int64_t off = 8 * (int64_t)(c2 * 64 + ln);
-#pragma unroll
-            for (int c = 0; c <= G; ++c) {
-                float x[8];
-                lds_src(src, (int64_t)c * d + off, x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[c] = fmaf(wv[c2][e], x[e], v[c]);
-            }
+            float wv[8];
+            wq[c2].to_float(wv);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                v[G + 1] = fmaf(wv[c2][e], part[c2][e], v[G + 1]);
+                v[G + 1] = fmaf(wv[e], part[c2][e], v[G + 1]);
                 v[G + 2] = fmaf(part[c2][e], part[c2][e], v[G + 2]);
             }
         }
+#pragma unroll
+        for (int c = 0; c <= G; ++c) {
+#pragma unroll
+            for (int c2 = 0; c2 < NCH; ++c2) {
+                const int ch = c2 * 64 + ln;
+                if (ch < p.nc) {
+                    float wv[8], x[8];
+                    wq[c2].to_float(wv);
+                    bb_lds_read<NCH, NBMAX>(sl, c2, c, x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[c] = fmaf(wv[e], x[e], v[c]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (l < lb) issue_w(l + 1);
         float tot[kV];
         wave_totals<0, kV>(v, tot, ln);
 
@@ -162,20 +193,21 @@ __device__ __forceinline__ void bb_group(const FwdParams& p, const float* src, c
                                      (uint64_t)d * sizeof(TO));
 #pragma unroll
         for (int c2 = 0; c2 < NCH; ++c2) {
+            const int ch = c2 * 64 + ln;
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = ap * part[c2][e];
-            if (q.live[c2]) {
-                const int64_t off = 8 * (int64_t)(c2 * 64 + ln);
+            if (ch < p.nc) {
 #pragma unroll
                 for (int c = 0; c <= G; ++c) {
                     float x[8];
-                    lds_src(src, (int64_t)c * d + off, x);
+                    bb_lds_read<NCH, NBMAX>(sl, c2, c, x);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) o[e] = fmaf(a[c], x[e], o[e]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            store_chunk((TO*)nullptr, orr, q.out_off[c2], o);
+            store_chunk((TO*)nullptr, orr, out_off + 8u * sizeof(TO) * 64u * c2, o);
         }
         if (p.lse != nullptr && ln == 0) p.lse[j * p.T + t] = (M + fast_log2(Z)) * kLn2;
         if (p.alpha != nullptr) {  // weight probe in source order, zeros past the sources
@@ -193,23 +225,25 @@ __device__ __forceinline__ void bb_group(const FwdParams& p, const float* src, c
 }
 
 template <typename TO, int NCH, int NBMAX, int G = 0>
-__device__ __forceinline__ void bb_dispatch(int g, const FwdParams& p, const float* src, const float* rsv,
-                                            const bf16_t* hist_tok, int64_t t, int ln, const BbLane& q,
-                                            int la, int lb) {
+__device__ __forceinline__ void bb_dispatch(int g, const FwdParams& p, const float* sl, const float* rsv,
+                                            const bf16_t* hist_tok, int64_t t, int ln, int la, int lb) {
     if constexpr (G < NBMAX) {
         if (g == G)
-            bb_group<TO, NCH, G>(p, src, rsv, hist_tok, t, ln, q, la, lb);
+            bb_group<TO, NCH, NBMAX, G>(p, sl, rsv, hist_tok, t, ln, la, lb);
         else
-            bb_dispatch<TO, NCH, NBMAX, G + 1>(g, p, src, rsv, hist_tok, t, ln, q, la, lb);
+            bb_dispatch<TO, NCH, NBMAX, G + 1>(g, p, sl, rsv, hist_tok, t, ln, la, lb);
     }
 }
 
 template <typename TO, int NCH, int NBMAX>
-__global__ __launch_bounds__(64 * kBbWaves) void block_batch_kernel(FwdParams p, int nb) {
+// Four waves per SIMD (at most 128 VGPRs): two workgroups (tokens) per CU, so
+// one token's loads overlap the other's arithmetic.
+__global__ __launch_bounds__(64 * kBbWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void block_batch_kernel(FwdParams p, int nb) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     float* const src = reinterpret_cast<float*>(lds_raw);
-    float* const rsv = src + (int64_t)nb * p.d;
-    int* const counter = reinterpret_cast<int*>(rsv + ((nb + 3) & ~3));
+    float* const rsv = src + BbLds<NCH, NBMAX>::kSrcFloats;
+    int* const counter = reinterpret_cast<int*>(rsv + ((NBMAX + 3) & ~3));
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ln = threadIdx.x & 63;
@@ -219,15 +253,6 @@ __global__ __launch_bounds__(64 * kBbWaves) void block_batch_kernel(FwdParams p,
     const bf16_t* hist_tok = static_cast<const bf16_t*>(p.hist) + t * d;
     const uint64_t tok_bytes = (uint64_t)d * 2;
 
-    BbLane q;
-#pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) {
-        const int ch = c2 * 64 + ln;
-        q.live[c2] = c2 < NCH && ch < p.nc;
-        q.in_off[c2] = q.live[c2] ? (uint32_t)(ch * 16) : kOOB;
-        q.out_off[c2] = q.live[c2] ? (uint32_t)(ch * 8 * sizeof(TO)) : kOOB;
-        q.w_off[c2] = q.live[c2] ? (uint32_t)(ch * 32) : kOOB;
-    }
     if (threadIdx.x == 0) *counter = 0;
 
     // ---- prologue: frozen sources v_0, b_1, ... in fp32, their RMS scales ------
@@ -246,7 +271,7 @@ __global__ __launch_bounds__(64 * kBbWaves) void block_batch_kernel(FwdParams p,
                 if (ib + u <= i1) {
                     const rsrc_t rr = make_rsrc(hist_tok + (ib + u) * row_elems, tok_bytes);
 #pragma unroll
-                    for (int c2 = 0; c2 < NCH; ++c2) ch[u][c2].load(rr, q.in_off[c2]);
+                    for (int c2 = 0; c2 < NCH; ++c2) ch[u][c2].load(rr, (uint32_t)ln * 16 + 1024u * c2);
                 }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -265,10 +290,12 @@ __global__ __launch_bounds__(64 * kBbWaves) void block_batch_kernel(FwdParams p,
         for (int c2 = 0; c2 < NCH; ++c2) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) sq = fmaf(acc[c2][e], acc[c2][e], sq);
-            if (q.live[c2]) {
-                float* dst = src + (int64_t)c * d + 8 * (c2 * 64 + ln);
-                *reinterpret_cast<f32x4*>(dst) = f32x4{acc[c2][0], acc[c2][1], acc[c2][2], acc[c2][3]};
-                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[c2][4], acc[c2][5], acc[c2][6], acc[c2][7]};
+            if (c2 * 64 + ln < p.nc) {  // the two planes of the chunk (see BbLds)
+                float* dst = src + 4 * ln;
+                *reinterpret_cast<f32x4*>(dst + ((0 * NCH + c2) * NBMAX + c) * 256) =
+                    f32x4{acc[c2][0], acc[c2][1], acc[c2][2], acc[c2][3]};
+                *reinterpret_cast<f32x4*>(dst + ((1 * NCH + c2) * NBMAX + c) * 256) =
+                    f32x4{acc[c2][4], acc[c2][5], acc[c2][6], acc[c2][7]};
             }
         }
         sq = tg_sum<64>(sq);
@@ -293,62 +320,64 @@ __global__ __launch_bounds__(64 * kBbWaves) void block_batch_kernel(FwdParams p,
         if (la < p.q_begin) la = p.q_begin;
         if (lb > l_last) lb = l_last;
         if (la > lb) continue;
-        bb_dispatch<TO, NCH, NBMAX>(g, p, src, rsv, hist_tok, t, ln, q, la, lb);
+        bb_dispatch<TO, NCH, NBMAX>(g, p, src + 4 * ln, rsv, hist_tok, t, ln, la, lb);
     }
 }
 
 template <typename TO, int NCH>
-hipError_t launch_bb_nch(const FwdParams& p, int nb, size_t lds, hipStream_t stream) {
-    auto go = [&](auto kern) {
+hipError_t launch_bb_nch(const FwdParams& p, int nb, hipStream_t stream) {
+    auto go = [&](auto kern, size_t lds) {
         const hipError_t e = prepare_dynamic_lds((const void*)kern, lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)p.T), dim3(64 * kBbWaves), lds, stream, p, nb);
         return hipGetLastError();
     };
     // the group index dispatch is instantiated up to NBMAX - 1
-    if (nb <= 9) return go(block_batch_kernel<TO, NCH, 9>);
-    return go(block_batch_kernel<TO, NCH, kBbMaxSources>);
+    if (nb <= 9) return go(block_batch_kernel<TO, NCH, 9>, (size_t)BbLds<NCH, 9>::kBytes);
+    return go(block_batch_kernel<TO, NCH, kBbMaxSources>, (size_t)BbLds<NCH, kBbMaxSources>::kBytes);
 }
 
 template <typename TO>
-hipError_t launch_bb(const FwdParams& p, int nb, size_t lds, hipStream_t stream) {
+hipError_t launch_bb(const FwdParams& p, int nb, hipStream_t stream) {
     switch ((p.nc + 63) / 64) {
-        case 1: return launch_bb_nch<TO, 1>(p, nb, lds, stream);
-        case 2: return launch_bb_nch<TO, 2>(p, nb, lds, stream);
-        case 3: return launch_bb_nch<TO, 3>(p, nb, lds, stream);
-        case 4: return launch_bb_nch<TO, 4>(p, nb, lds, stream);
+        case 1: return launch_bb_nch<TO, 1>(p, nb, stream);
+        case 2: return launch_bb_nch<TO, 2>(p, nb, stream);
+        case 3: return launch_bb_nch<TO, 3>(p, nb, stream);
+        case 4: return launch_bb_nch<TO, 4>(p, nb, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
+// LDS bytes of the instantiation that serves nb sources at nch chunks per lane
+int64_t bb_lds_bytes(int nb, int nch) {
+    const int nbmax = nb <= 9 ? 9 : kBbMaxSources;
+    return (int64_t)2 * nch * nbmax * 1024 + ((nbmax + 3) & ~3) * 4 + 16;
+}
+
 // sources a read of the call can see (v_0 and the completed blocks), or 0 if
 // the call does not qualify
-int bb_sources(const FwdParams& p, attnres_dtype hist_dt, size_t* lds) {
+int bb_sources(const FwdParams& p, attnres_dtype hist_dt) {
     if (hist_dt != ATTNRES_BF16 || p.S < 2 || p.n_q < kBbMinReads || p.nc > 4 * 64) return 0;
     if (p.T * 64 * kBbWaves >= ((int64_t)1 << 32)) return 0;
     const int nb = 1 + (p.q_begin + p.n_q - 1) / p.S;
     if (nb > kBbMaxSources) return 0;
     const int max_lds = device_max_lds();
-    const int64_t bytes = bb_lds_bytes(nb, p.d);
-    if (bytes > max_lds) return 0;
-    *lds = (size_t)bytes;
+    if (bb_lds_bytes(nb, (p.nc + 63) / 64) > max_lds) return 0;
     return nb;
 }
 
 }  // namespace
 
 bool block_batch_applies(const FwdParams& p, attnres_dtype hist_dt) {
-    size_t lds = 0;
-    return bb_sources(p, hist_dt, &lds) > 0;
+    return bb_sources(p, hist_dt) > 0;
 }
 
 hipError_t launch_block_batch(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
                               hipStream_t stream) {
-    size_t lds = 0;
-    const int nb = bb_sources(p, hist_dt, &lds);
+    const int nb = bb_sources(p, hist_dt);
     if (nb == 0) return hipErrorInvalidValue;
-    return out_dt == ATTNRES_BF16 ? launch_bb<bf16_t>(p, nb, lds, stream)
-                                  : launch_bb<float>(p, nb, lds, stream);
+    return out_dt == ATTNRES_BF16 ? launch_bb<bf16_t>(p, nb, stream)
+                                  : launch_bb<float>(p, nb, stream);
 }
 
 }  // namespace attnres
