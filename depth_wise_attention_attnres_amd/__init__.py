@@ -28,7 +28,8 @@ STATUS = {0: "ATTNRES_OK", 1: "ATTNRES_ERR_INVALID_ARG", 2: "ATTNRES_ERR_UNSUPPO
 
 # every symbol include/attnres.h declares
 EXPORTS = ["attnres_full_fwd", "attnres_full_fwd_q", "attnres_query_proj", "attnres_block_fwd",
-           "attnres_block_phase1", "attnres_block_phase2",
+           "attnres_block_fwd_q", "attnres_block_phase1", "attnres_block_phase2",
+           "attnres_block_phase1_q", "attnres_block_phase2_q",
            "attnres_bwd", "attnres_bwd_noalloc", "attnres_bwd_noalloc_max_workspace",
            "attnres_bwd_workspace_bytes", "attnres_block_index_table",
            "attnres_status_string", "attnres_last_error"]
@@ -57,6 +58,15 @@ _lib.attnres_block_phase1.argtypes = [_vp, _i64, _i64, _i64, _vp, _int, _vp, _vp
 _lib.attnres_block_phase2.restype = _int
 _lib.attnres_block_phase2.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp, _vp, _vp, _f32, _vp,
                                       _int, _vp, _vp, _vp, _vp]
+_lib.attnres_block_fwd_q.restype = _int
+_lib.attnres_block_fwd_q.argtypes = [_vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _f32,
+                                     _vp, _int, _vp, _vp]
+_lib.attnres_block_phase1_q.restype = _int
+_lib.attnres_block_phase1_q.argtypes = [_vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _i64, _f32,
+                                        _vp, _vp, _vp, _vp, _int, _vp, _vp]
+_lib.attnres_block_phase2_q.restype = _int
+_lib.attnres_block_phase2_q.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp, _vp, _vp, _f32,
+                                        _vp, _int, _vp, _vp]
 _lib.attnres_bwd.restype = _int
 _lib.attnres_bwd.argtypes = [_int, _i64, _vp, _int, _i64, _i64, _i64, _vp, _i64, _i64, _f32,
                              _vp, _int, _vp, _int, _int, _vp, _vp, _sz, _vp]
@@ -234,6 +244,30 @@ def block_fwd(hist, w, S: int, *, q_begin: int = 0, n_q: int | None = None, eps:
     return out, lse
 
 
+def block_fwd_q(hist, q, S: int, *, q_begin: int = 0, eps: float = 1e-6, out=None,
+                out_dtype=None, lse=None, want_lse: bool = True):
+    """Block AttnRes reads q_begin .. q_begin + n_q - 1 (block size S) with a
+    query per (read, token): q [n_q, T, d] fp32.  Returns (out, lse)."""
+    import torch
+    _require(hist, "hist")
+    n_hist, T, d = hist.shape
+    n_q = q.shape[0]
+    _require(q, "q", dtype=torch.float32, shape=(n_q, T, d))
+    odt = _dtype_code(hist) if out_dtype is None else (F32 if out_dtype == torch.float32 else BF16)
+    if out is None:
+        out = torch.empty((n_q, T, d), dtype=_torch_dtype(odt), device=hist.device)
+    else:
+        _require(out, "out", shape=(n_q, T, d))
+        odt = _dtype_code(out)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, T), dtype=torch.float32, device=hist.device)
+    if lse is not None:
+        _require(lse, "lse", dtype=torch.float32, shape=(n_q, T))
+    _check(_lib.attnres_block_fwd_q(_ptr(hist), _dtype_code(hist), n_hist, T, d, S, _ptr(q),
+                                    q_begin, n_q, eps, _ptr(out), odt, _ptr(lse), _stream(hist)))
+    return out, lse
+
+
 def block_phase1(blocks, n_src: int, v, w, *, partial=None, eps: float = 1e-6, rs=None, o=None,
                  lse1=None, out0=None, lse0=None, normed0=None, norm_gain0=None):
     """Model-order Block AttnRes, phase 1: close block n_src-1 into blocks[n_src-1]
@@ -315,6 +349,75 @@ def block_phase2(v, partial, first_in_block: bool, w, o, lse1, *, eps: float = 1
     return out, lse
 
 
+def block_phase1_q(blocks, n_src: int, v, q, *, partial=None, eps: float = 1e-6, rs=None, o=None,
+                   lse1=None, out0=None, lse0=None):
+    """Model-order phase 1 with per-token queries q [n_reads, T, d] fp32.  With v
+    (row closing block n_src-1) it closes the block as block_phase1 does; with
+    v=None it only scores the frozen sources blocks[0 .. n_src-1] (no state is
+    written).  Returns (o, lse1)."""
+    import torch
+    if blocks.dim() != 3:
+        raise ValueError(f"blocks must be [n_blocks, T, d], got shape {tuple(blocks.shape)}")
+    n_blocks, T, d = blocks.shape
+    if not 1 <= n_src <= n_blocks:
+        raise ValueError(f"n_src = {n_src} outside 1 .. blocks.shape[0] = {n_blocks}")
+    if rs is not None and (rs.dim() != 2 or rs.shape[0] < n_src or rs.shape[1] != T):
+        raise ValueError(f"rs must be [>= n_src = {n_src}, T = {T}], got shape {tuple(rs.shape)}")
+    _require(blocks, "blocks", dtype=torch.float32)
+    if v is not None:
+        _require(v, "v", shape=(T, d))
+    elif partial is not None:
+        raise ValueError("partial needs the row v that closes the block")
+    n_reads = q.shape[0]
+    _require(q, "q", dtype=torch.float32, shape=(n_reads, T, d))
+    if partial is not None:
+        _require(partial, "partial", dtype=torch.float32, shape=(T, d))
+    if rs is not None:
+        _require(rs, "rs", dtype=torch.float32)
+    dev = blocks.device
+    if o is None:
+        o = torch.empty((n_reads, T, d), dtype=torch.float32, device=dev)
+    _require(o, "o", dtype=torch.float32, shape=(n_reads, T, d))
+    if lse1 is None:
+        lse1 = torch.empty((n_reads, T), dtype=torch.float32, device=dev)
+    _require(lse1, "lse1", dtype=torch.float32, shape=(n_reads, T))
+    odt = F32
+    if out0 is not None:
+        _require(out0, "out0", shape=(T, d))
+        odt = _dtype_code(out0)
+    if lse0 is not None:
+        _require(lse0, "lse0", dtype=torch.float32, shape=(T,))
+    _check(_lib.attnres_block_phase1_q(_ptr(blocks), n_src, T, d, _ptr(v),
+                                       F32 if v is None else _dtype_code(v), _ptr(partial), _ptr(q),
+                                       n_reads, eps, _ptr(rs), _ptr(o), _ptr(lse1), _ptr(out0), odt,
+                                       _ptr(lse0), _stream(blocks)))
+    return o, lse1
+
+
+def block_phase2_q(v, partial, first_in_block: bool, q, o, lse1, *, eps: float = 1e-6, out=None,
+                   out_dtype=None, lse=None):
+    """Model-order phase 2 with a per-token query q [T, d] fp32.  Returns (out, lse)."""
+    import torch
+    _require(v, "v")
+    T, d = v.shape
+    _require(partial, "partial", dtype=torch.float32, shape=(T, d))
+    _require(q, "q", dtype=torch.float32, shape=(T, d))
+    _require(o, "o", dtype=torch.float32, shape=(T, d))
+    _require(lse1, "lse1", dtype=torch.float32, shape=(T,))
+    odt = _dtype_code(v) if out_dtype is None else (F32 if out_dtype == torch.float32 else BF16)
+    if out is None:
+        out = torch.empty((T, d), dtype=_torch_dtype(odt), device=v.device)
+    else:
+        _require(out, "out", shape=(T, d))
+        odt = _dtype_code(out)
+    if lse is not None:
+        _require(lse, "lse", dtype=torch.float32, shape=(T,))
+    _check(_lib.attnres_block_phase2_q(_ptr(v), _dtype_code(v), T, d, _ptr(partial),
+                                       1 if first_in_block else 0, _ptr(q), _ptr(o), _ptr(lse1),
+                                       eps, _ptr(out), odt, _ptr(lse), _stream(v)))
+    return out, lse
+
+
 def block_model_order(hist, w, S: int, *, eps: float = 1e-6, out=None, lse=None, state=None,
                       normed=None, norm_gain=None):
     """All reads of a Block AttnRes history in model order through the two
@@ -362,6 +465,44 @@ def block_model_order(hist, w, S: int, *, eps: float = 1e-6, out=None, lse=None,
             block_phase2(hist[l0 + k], partial, k == 1, w[l0 + k], o[k], lse1[k], eps=eps,
                          out=out[l0 + k], lse=lse[l0 + k], normed=nd(l0 + k),
                          norm_gain=ng(l0 + k))
+    return out, lse
+
+
+def block_model_order_q(hist, W, S: int, *, eps: float = 1e-6, out=None, lse=None):
+    """All reads of a Block AttnRes history in model order with the
+    input-dependent query: read l projects the newest row, q_l = W[l] v_l
+    (query_proj on the matrix cores), then runs one phase-1 call over the
+    frozen sources (closing block l / S when l is a multiple of S) and, inside
+    a block, one phase-2 call that adds row l to the partial sum and merges
+    it.  hist bf16 [n_hist, T, d], W bf16 [n_hist, d, d].  Returns (out, lse)."""
+    import torch
+    _require(hist, "hist", dtype=torch.bfloat16)
+    n_hist, T, d = hist.shape
+    _require(W, "W", dtype=torch.bfloat16, shape=(n_hist, d, d))
+    dev = hist.device
+    n_blk = 1 + (n_hist - 1) // S
+    blocks = torch.empty((n_blk, T, d), dtype=torch.float32, device=dev)
+    partial = torch.empty((T, d), dtype=torch.float32, device=dev)
+    rs = torch.empty((n_blk, T), dtype=torch.float32, device=dev)
+    o = torch.empty((1, T, d), dtype=torch.float32, device=dev)
+    lse1 = torch.empty((1, T), dtype=torch.float32, device=dev)
+    q = torch.empty((1, T, d), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty_like(hist)
+    if lse is None:
+        lse = torch.empty((n_hist, T), dtype=torch.float32, device=dev)
+    for l in range(n_hist):
+        m, k = divmod(l, S)
+        query_proj(hist[l:l + 1], W[l:l + 1], q=q)
+        if k == 0:
+            block_phase1_q(blocks[: m + 1], m + 1, hist[l], q,
+                           partial=partial if (m > 0 and S > 1) else None, eps=eps,
+                           rs=rs[: m + 1], o=o, lse1=lse1, out0=out[l], lse0=lse[l])
+        else:
+            block_phase1_q(blocks[: m + 1], m + 1, None, q, eps=eps, rs=rs[: m + 1], o=o,
+                           lse1=lse1)
+            block_phase2_q(hist[l], partial, k == 1, q[0], o[0], lse1[0], eps=eps, out=out[l],
+                           lse=lse[l])
     return out, lse
 
 

@@ -205,12 +205,17 @@ int attnres_query_proj(const void* x, attnres_dtype x_dtype, int64_t n_q, int64_
     return hip_status(fn, attnres::launch_query_proj(x, W, q, n_q, T, (int)d, stream));
 }
 
-int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
-                      int64_t d, int64_t S, const float* w, int64_t q_begin, int64_t n_q,
-                      float eps, void* out, attnres_dtype out_dtype, float* lse, float* alpha,
-                      hipStream_t stream) {
-    const char* fn = "attnres_block_fwd";
-    int st = check_common(fn, hist, hist_dtype, n_hist, T, d, w, q_begin, n_q, eps);
+}  // extern "C"
+
+namespace {
+
+// w (one query per read) or qtok (one per read and token; w must be NULL)
+int block_fwd_impl(const char* fn, const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
+                   int64_t T, int64_t d, int64_t S, const float* w, const float* qtok,
+                   int64_t q_begin, int64_t n_q, float eps, void* out, attnres_dtype out_dtype,
+                   float* lse, float* alpha, hipStream_t stream) {
+    int st = check_common(fn, hist, hist_dtype, n_hist, T, d, qtok != nullptr ? qtok : w, q_begin,
+                          n_q, eps);
     if (st != ATTNRES_OK) return st;
     if (S < 1) return fail(ATTNRES_ERR_INVALID_ARG, "%s: S must be >= 1 (got %" PRId64 ")", fn, S);
     if (!valid_dtype(out_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad out dtype %d", fn, (int)out_dtype);
@@ -222,7 +227,7 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
 
     attnres::BlockFwdParams p;
     p.alpha = alpha;
-    p.qtok = nullptr;
+    p.qtok = qtok;
     p.hist = hist;
     p.w = w;
     p.rinv = nullptr;
@@ -245,20 +250,51 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
     return hip_status(fn, attnres::launch_block_fwd(p, hist_dtype, out_dtype, stream));
 }
 
-int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d, const void* v,
-                         attnres_dtype v_dtype, const float* partial, const float* w,
-                         int64_t n_reads, float eps, float* rs, float* o, float* lse1, void* out0,
-                         attnres_dtype out_dtype, float* lse0, const float* norm_gain0,
-                         void* normed0, hipStream_t stream) {
-    const char* fn = "attnres_block_phase1";
+}  // namespace
+
+extern "C" {
+
+int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
+                      int64_t d, int64_t S, const float* w, int64_t q_begin, int64_t n_q,
+                      float eps, void* out, attnres_dtype out_dtype, float* lse, float* alpha,
+                      hipStream_t stream) {
+    return block_fwd_impl("attnres_block_fwd", hist, hist_dtype, n_hist, T, d, S, w, nullptr,
+                          q_begin, n_q, eps, out, out_dtype, lse, alpha, stream);
+}
+
+int attnres_block_fwd_q(const void* hist, attnres_dtype hist_dtype, int64_t n_hist, int64_t T,
+                        int64_t d, int64_t S, const float* q, int64_t q_begin, int64_t n_q,
+                        float eps, void* out, attnres_dtype out_dtype, float* lse,
+                        hipStream_t stream) {
+    return block_fwd_impl("attnres_block_fwd_q", hist, hist_dtype, n_hist, T, d, S, nullptr, q,
+                          q_begin, n_q, eps, out, out_dtype, lse, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// w (one query per read) or qtok (per read and token); v may be NULL only
+// with qtok (no new source: every source is read from blocks)
+int phase1_impl(const char* fn, float* blocks, int64_t n_src, int64_t T, int64_t d, const void* v,
+                attnres_dtype v_dtype, const float* partial, const float* w, const float* qtok,
+                int64_t n_reads, float eps, float* rs, float* o, float* lse1, void* out0,
+                attnres_dtype out_dtype, float* lse0, const float* norm_gain0, void* normed0,
+                hipStream_t stream) {
+    if (v == nullptr && qtok == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: v is NULL", fn);
+    if (v == nullptr && partial != nullptr)
+        return fail(ATTNRES_ERR_INVALID_ARG, "%s: partial given without a row v to close a block", fn);
     if (n_src < 1 || n_src > attnres::kBlockMaxRegSources)
         return fail(n_src < 1 ? ATTNRES_ERR_INVALID_ARG : ATTNRES_ERR_UNSUPPORTED,
                     "%s: n_src = %" PRId64 " outside 1 .. %d", fn, n_src, attnres::kBlockMaxRegSources);
     if (n_reads < 1 || n_reads > 64)
         return fail(n_reads < 1 ? ATTNRES_ERR_INVALID_ARG : ATTNRES_ERR_UNSUPPORTED,
                     "%s: n_reads = %" PRId64 " outside 1 .. 64", fn, n_reads);
-    // v is the new history row; one query row is checked like a read
-    int st = check_common(fn, v, v_dtype, n_src, T, d, w, 0, 1, eps);
+    // v is the new history row (or, without one, the block store is checked in
+    // its place); one query row is checked like a read
+    int st = check_common(fn, v != nullptr ? v : (const void*)blocks,
+                          v != nullptr ? v_dtype : ATTNRES_F32, n_src, T, d,
+                          qtok != nullptr ? qtok : w, 0, 1, eps);
     if (st != ATTNRES_OK) return st;
     if (!valid_dtype(out_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad out dtype %d", fn, (int)out_dtype);
     if (T == 0) return ok();
@@ -286,6 +322,7 @@ int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d, con
     p.v = v;
     p.partial = partial;
     p.w = w;
+    p.qtok = qtok;
     p.rs = rs;
     p.o = o;
     p.lse1 = lse1;
@@ -303,12 +340,38 @@ int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d, con
     return hip_status(fn, attnres::launch_block_phase1(p, stream));
 }
 
-int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_t d, float* partial,
-                         int first_in_block, const float* w, const float* o, const float* lse1,
-                         float eps, void* out, attnres_dtype out_dtype, float* lse,
-                         const float* norm_gain, void* normed, hipStream_t stream) {
-    const char* fn = "attnres_block_phase2";
-    int st = check_common(fn, v, v_dtype, 1, T, d, w, 0, 1, eps);
+}  // namespace
+
+extern "C" {
+
+int attnres_block_phase1(float* blocks, int64_t n_src, int64_t T, int64_t d, const void* v,
+                         attnres_dtype v_dtype, const float* partial, const float* w,
+                         int64_t n_reads, float eps, float* rs, float* o, float* lse1, void* out0,
+                         attnres_dtype out_dtype, float* lse0, const float* norm_gain0,
+                         void* normed0, hipStream_t stream) {
+    return phase1_impl("attnres_block_phase1", blocks, n_src, T, d, v, v_dtype, partial, w,
+                       nullptr, n_reads, eps, rs, o, lse1, out0, out_dtype, lse0, norm_gain0,
+                       normed0, stream);
+}
+
+int attnres_block_phase1_q(float* blocks, int64_t n_src, int64_t T, int64_t d, const void* v,
+                           attnres_dtype v_dtype, const float* partial, const float* q,
+                           int64_t n_reads, float eps, float* rs, float* o, float* lse1,
+                           void* out0, attnres_dtype out_dtype, float* lse0, hipStream_t stream) {
+    return phase1_impl("attnres_block_phase1_q", blocks, n_src, T, d, v, v_dtype, partial, nullptr,
+                       q, n_reads, eps, rs, o, lse1, out0, out_dtype, lse0, nullptr, nullptr,
+                       stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int phase2_impl(const char* fn, const void* v, attnres_dtype v_dtype, int64_t T, int64_t d,
+                float* partial, int first_in_block, const float* w, const float* qtok,
+                const float* o, const float* lse1, float eps, void* out, attnres_dtype out_dtype,
+                float* lse, const float* norm_gain, void* normed, hipStream_t stream) {
+    int st = check_common(fn, v, v_dtype, 1, T, d, qtok != nullptr ? qtok : w, 0, 1, eps);
     if (st != ATTNRES_OK) return st;
     if (!valid_dtype(out_dtype)) return fail(ATTNRES_ERR_INVALID_ARG, "%s: bad out dtype %d", fn, (int)out_dtype);
     if (first_in_block != 0 && first_in_block != 1)
@@ -334,6 +397,7 @@ int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_
     p.v = v;
     p.partial = partial;
     p.w = w;
+    p.qtok = qtok;
     p.o = o;
     p.lse1 = lse1;
     p.out = out;
@@ -347,6 +411,26 @@ int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_
     p.eps = eps;
     p.inv_d = 1.0f / (float)d;
     return hip_status(fn, attnres::launch_block_phase2(p, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_t d, float* partial,
+                         int first_in_block, const float* w, const float* o, const float* lse1,
+                         float eps, void* out, attnres_dtype out_dtype, float* lse,
+                         const float* norm_gain, void* normed, hipStream_t stream) {
+    return phase2_impl("attnres_block_phase2", v, v_dtype, T, d, partial, first_in_block, w,
+                       nullptr, o, lse1, eps, out, out_dtype, lse, norm_gain, normed, stream);
+}
+
+int attnres_block_phase2_q(const void* v, attnres_dtype v_dtype, int64_t T, int64_t d,
+                           float* partial, int first_in_block, const float* q, const float* o,
+                           const float* lse1, float eps, void* out, attnres_dtype out_dtype,
+                           float* lse, hipStream_t stream) {
+    return phase2_impl("attnres_block_phase2_q", v, v_dtype, T, d, partial, first_in_block,
+                       nullptr, q, o, lse1, eps, out, out_dtype, lse, nullptr, nullptr, stream);
 }
 
 size_t attnres_bwd_workspace_bytes(attnres_variant variant, int64_t S, int64_t n_hist, int64_t T,

@@ -114,7 +114,9 @@ __device__ __forceinline__ void bb_group(const FwdParams& p, const float* sl, co
     // and the next read's query is requested once the dots are done
     Chunk<float> wq[NCH];
     auto issue_w = [&](int l) {
-        const rsrc_t wr = make_rsrc(p.w + (int64_t)(l - p.q_begin) * d, (uint64_t)d * 4);
+        const int64_t jq = l - p.q_begin;  // one query per read, or one per read and token
+        const float* wrow = p.qtok != nullptr ? p.qtok + (jq * p.T + t) * d : p.w + jq * d;
+        const rsrc_t wr = make_rsrc(wrow, (uint64_t)d * 4);
 #pragma unroll
         for (int c2 = 0; c2 < NCH; ++c2) wq[c2].load(wr, w_off + 2048u * c2);
     };

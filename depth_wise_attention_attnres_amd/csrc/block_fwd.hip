@@ -38,6 +38,12 @@
 
 namespace attnres {
 
+// the query of read l at token t: one row per read, or one per read and token
+__device__ __forceinline__ const float* block_query_row(const BlockFwdParams& p, int l, int64_t t) {
+    const int64_t j = l - p.q_begin;
+    return p.qtok != nullptr ? p.qtok + (j * p.T + t) * p.d : p.w + j * p.d;
+}
+
 template <int NSRC, int CR>
 struct BlockLds {
     static constexpr int kStride = NSRC + 2;     // values per read: NSRC dots, p dot, p sumsq
@@ -123,7 +129,7 @@ __device__ __forceinline__ void block_chunk(const BlockFwdParams& p, BlockState<
     const uint32_t out_off_bf = ln < p.nc ? (uint32_t)(ln * 16) : kOOB;  // bf16 chunk; fp32 is twice
 
     auto issue_w = [&](int slot, int l) {
-        const rsrc_t wr = make_rsrc(p.w + (int64_t)(l - p.q_begin) * p.d, (uint64_t)p.d * 4);
+        const rsrc_t wr = make_rsrc(block_query_row(p, l, t), (uint64_t)p.d * 4);
         st.wbuf[slot].load(wr, w_off);
     };
     // the first query of the chunk was requested by the previous chunk (or
@@ -407,7 +413,7 @@ void block_fwd_twophase_kernel(BlockFwdParams p) {
     {
         const int nk = p.q_begin > 0 ? p.q_begin : 0;  // first read with an output
         if (nk < l1) {
-            const rsrc_t wr = make_rsrc(p.w + (int64_t)(nk - p.q_begin) * p.d, (uint64_t)p.d * 4);
+            const rsrc_t wr = make_rsrc(block_query_row(p, nk, t), (uint64_t)p.d * 4);
             if (nk & 1)
                 st.wbuf[1].load(wr, w_off);
             else

@@ -66,21 +66,22 @@ void block_phase1_kernel(Phase1Params p) {
     const int64_t row_elems = p.T * (int64_t)p.d;
     const bool ok = tid < p.nc;
     const uint32_t chunk = (uint32_t)tid;
-    const int m = p.n_src - 1;  // index of the new source
+    const int m = p.n_src - 1;  // index of the new source (the last frozen one when v is null)
+    const bool fresh = p.v != nullptr;  // a new source is formed here
     extern __shared__ float lds[];  // [2][kVals][row_slots], then [row_slots] for the pre-norm
 
     // ---- sources: the frozen ones, then the new one formed here -----------
     float src[NSRC][8];
 #pragma unroll
     for (int c = 0; c < NSRC; ++c) {
-        if (c < m) {
+        if (c < m || (c == m && !fresh)) {
             load8(p.blocks + c * row_elems + t * p.d, ATTNRES_F32, p.d, chunk, ok, src[c]);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) src[c][e] = 0.f;
         }
     }
-    {
+    if (fresh) {
         float x[8];
         load8(static_cast<const char*>(p.v) + t * p.d * (p.v_dt == ATTNRES_BF16 ? 2 : 4), p.v_dt, p.d,
               chunk, ok, x);
@@ -108,7 +109,9 @@ void block_phase1_kernel(Phase1Params p) {
         for (int k = 0; k < CR; ++k) {
             if (k < n) {
                 float wv[8];
-                load8(p.w + (int64_t)(k0 + k) * p.d, ATTNRES_F32, p.d, chunk, ok, wv);
+                const float* wrow = p.qtok != nullptr ? p.qtok + ((int64_t)(k0 + k) * p.T + t) * p.d
+                                                      : p.w + (int64_t)(k0 + k) * p.d;
+                load8(wrow, ATTNRES_F32, p.d, chunk, ok, wv);
                 float v[NSRC];
 #pragma unroll
                 for (int c = 0; c < NSRC; ++c) {
@@ -129,7 +132,7 @@ void block_phase1_kernel(Phase1Params p) {
         if (k0 == 0) {  // squared norms of the sources whose scale is not cached
 #pragma unroll
             for (int c = 0; c < NSRC; ++c) {
-                if (c <= m && (p.rs == nullptr || c == m)) {
+                if (c <= m && (p.rs == nullptr || (c == m && fresh))) {
                     float sq = 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) sq = fmaf(src[c][e], src[c][e], sq);
@@ -154,11 +157,11 @@ void block_phase1_kernel(Phase1Params p) {
             return s;
         };
         if (k0 == 0 && cc <= m) {
-            if (p.rs != nullptr && cc < m)
+            if (p.rs != nullptr && (cc < m || !fresh))
                 rsv = p.rs[(int64_t)cc * p.T + t];
             else
                 rsv = fast_rsqrt(fmaf(total(kSq + cc), p.inv_d, p.eps));
-            if (p.rs != nullptr && cc == m && kk == 0 && tid == lane)
+            if (p.rs != nullptr && fresh && cc == m && kk == 0 && tid == lane)
                 p.rs[(int64_t)m * p.T + t] = rsv;
         }
         const bool live = kk < n && cc <= m;
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(256) void block_phase2_kernel(Phase2Params p) {
             for (int e = 0; e < 8; ++e) x[c][e] = q[e] + x[c][e];
         }
         float wv[8];
-        load8(p.w, ATTNRES_F32, p.d, ch, ok, wv);
+        load8(p.qtok != nullptr ? p.qtok + t * p.d : p.w, ATTNRES_F32, p.d, ch, ok, wv);
         load8(o_row, ATTNRES_F32, p.d, ch, ok, o[c]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {

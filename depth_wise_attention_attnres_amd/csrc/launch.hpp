@@ -113,10 +113,12 @@ hipError_t launch_bwd_scores_group(const BwdParams& p, hipStream_t stream);
 
 // Block AttnRes in model order (block_model.hip)
 struct Phase1Params {
-    float* blocks;          // [n_src][T][d] fp32; row n_src-1 written
-    const void* v;          // [T][d] history row closing the block
+    float* blocks;          // [n_src][T][d] fp32; row n_src-1 written (unless v is null)
+    const void* v;          // [T][d] history row closing the block, or null: no new
+                            // source, all n_src sources are read from blocks
     const float* partial;   // [T][d] fp32 or null
     const float* w;         // [n_reads][d]
+    const float* qtok;      // [n_reads][T][d] per-token queries (then w is unused), or null
     float* rs;              // [n_src][T] or null
     float* o;               // [n_reads][T][d] fp32
     float* lse1;            // [n_reads][T]
@@ -133,6 +135,7 @@ struct Phase2Params {
     const void* v;          // [T][d]
     float* partial;         // [T][d] fp32, in place
     const float* w;         // [d]
+    const float* qtok;      // [T][d] per-token query (then w is unused), or null
     const float* o;         // [T][d] fp32
     const float* lse1;      // [T]
     void* out;              // [T][d]

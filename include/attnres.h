@@ -174,6 +174,19 @@ int attnres_block_fwd(const void* hist, attnres_dtype hist_dtype, int64_t n_hist
                       hipStream_t stream);
 
 /*
+ * Block AttnRes forward with a query per (read, token) (the input-dependent
+ * query of "Kimi K3 notes 2", sec. 6, applied to the Block read of
+ * "DepthBench reading notes" sec. 2.5): the same reads as attnres_block_fwd,
+ * scored with q[j][t] ([n_q][T][d] fp32, 16-byte aligned; from
+ * attnres_query_proj or any caller) instead of one w[j] per read.  No weight
+ * probe.  Other arguments and requirements as attnres_block_fwd.
+ */
+int attnres_block_fwd_q(const void* hist, attnres_dtype hist_dtype, int64_t n_hist,
+                        int64_t T, int64_t d, int64_t S, const float* q,
+                        int64_t q_begin, int64_t n_q, float eps, void* out,
+                        attnres_dtype out_dtype, float* lse, hipStream_t stream);
+
+/*
  * Block AttnRes in model order, phase 1 (DataCamp, "two-phase computation":
  * the reads of one block group share the frozen sources and are batched;
  * block reading of "DepthBench reading notes" sec. 2.5).  Called when history
@@ -227,6 +240,36 @@ int attnres_block_phase2(const void* v, attnres_dtype v_dtype, int64_t T, int64_
                          const float* o, const float* lse1, float eps, void* out,
                          attnres_dtype out_dtype, float* lse, const float* norm_gain,
                          void* normed, hipStream_t stream);
+
+/*
+ * The two model-order phases with a query per token (the input-dependent
+ * query of "Kimi K3 notes 2", sec. 6).  The pages name the price of that
+ * query: read l's query is a projection of v_l, which exists only once
+ * sublayer l has run, so the reads of a block group can no longer be scored
+ * ahead in one batch -- the serial access the pages describe.  A model
+ * therefore calls, for each read l with m = floor(l/S):
+ *   l mod S == 0:  attnres_block_phase1_q with v = row l (closing block m,
+ *                  n_src = m + 1), n_reads = 1, q = q_l: out0 receives h_l;
+ *   otherwise:     attnres_block_phase1_q with v = NULL (no block closed;
+ *                  all n_src = m + 1 sources are read from blocks, rs holds
+ *                  all their scales or is NULL), n_reads = 1, q = q_l, into
+ *                  o / lse1; then attnres_block_phase2_q with row l, q_l and
+ *                  that o / lse1.
+ *   attnres_block_phase1_q: arguments as attnres_block_phase1 with
+ *     q [n_reads][T][d] fp32 in place of w; v may be NULL (then partial must
+ *     be NULL and nothing is written to blocks or rs); no pre-norm.
+ *   attnres_block_phase2_q: arguments as attnres_block_phase2 with q [T][d]
+ *     fp32 in place of w; no pre-norm.
+ */
+int attnres_block_phase1_q(float* blocks, int64_t n_src, int64_t T, int64_t d,
+                           const void* v, attnres_dtype v_dtype, const float* partial,
+                           const float* q, int64_t n_reads, float eps, float* rs,
+                           float* o, float* lse1, void* out0, attnres_dtype out_dtype,
+                           float* lse0, hipStream_t stream);
+int attnres_block_phase2_q(const void* v, attnres_dtype v_dtype, int64_t T, int64_t d,
+                           float* partial, int first_in_block, const float* q,
+                           const float* o, const float* lse1, float eps, void* out,
+                           attnres_dtype out_dtype, float* lse, hipStream_t stream);
 
 /*
  * Backward of attnres_full_fwd (variant ATTNRES_FULL) or attnres_block_fwd

@@ -319,3 +319,33 @@ def test_bwd_noalloc_validation(ar):
     assert need > 64 << 20
     assert nb(n_hist=49, T=4096, d=1024, n_q=49) == UNSUPPORTED
     assert "static scratch" in ar.last_error()
+
+
+def test_block_q_entry_points_validation(ar):
+    lib = ar.raw()
+
+    def bq(n_hist=9, T=16, d=64, S=4, q=P2, q_begin=0, n_q=9, out=P3):
+        return lib.attnres_block_fwd_q(P, BF16, n_hist, T, d, S, q, q_begin, n_q, 1e-6, out, BF16,
+                                       None, None)
+    assert bq(d=12) == ALIGN
+    assert bq(S=0) == INVALID
+    assert bq(q=None) == INVALID
+    assert bq(q=P2 + 4) == ALIGN
+    assert bq(out=None) == INVALID
+    assert bq(q_begin=3) == INVALID  # reads past the history
+    assert bq(T=0) == OK
+
+    def p1(v=P2, partial=None, q=P3, n_src=2, n_reads=1):
+        return lib.attnres_block_phase1_q(P, n_src, 16, 64, v, BF16, partial, q, n_reads, 1e-6,
+                                          None, P, P2, None, BF16, None, None)
+    assert p1(q=None) == INVALID
+    assert p1(v=None, partial=P) == INVALID  # a partial sum needs the row closing the block
+    assert "partial" in ar.last_error()
+    assert p1(n_src=0) == INVALID
+    assert p1(n_reads=65) == UNSUPPORTED
+
+    def p2(q=P3, first=1):
+        return lib.attnres_block_phase2_q(P, BF16, 16, 64, P, first, q, P2, P3, 1e-6, P, BF16,
+                                          None, None)
+    assert p2(q=None) == INVALID
+    assert p2(first=2) == INVALID
