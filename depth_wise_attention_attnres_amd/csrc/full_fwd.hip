@@ -114,8 +114,12 @@ __global__ __launch_bounds__(kStreamThreads) void full_fwd_stream_kernel(FwdPara
                 for (int c = 0; c < NCH; ++c) buf[u][c].load(rr, in_off[c]);
             }
             if (i < p.rinv_valid) {
-                const rsrc_t cr = make_rsrc(p.rinv + (int64_t)i * p.T + tok0, (uint64_t)blk_tok * 4);
-                rbuf[u] = load_f32(cr, tok_f32_off);
+                if constexpr (LPT == 64) {  // one token per wave: a scalar load
+                    rbuf[u] = const_view(p.rinv)[(int64_t)i * p.T + t];
+                } else {
+                    const rsrc_t cr = make_rsrc(p.rinv + (int64_t)i * p.T + tok0, (uint64_t)blk_tok * 4);
+                    rbuf[u] = load_f32(cr, tok_f32_off);
+                }
             }
         };
 #pragma unroll
@@ -263,6 +267,26 @@ hipError_t launch_stream(const FwdParams& p, hipStream_t stream) {
 
 template <typename TI, typename TO, bool BLOCK>
 hipError_t dispatch_stream(const FwdParams& p, hipStream_t stream) {
+    // Full reads of bf16 rows with d <= 896: 16 lanes per token (four tokens
+    // per wave), ceil(d / 128) chunks per lane.  At d = 896 or 640 every lane
+    // is busy (64 lanes per token leave 12.5% / 37.5% of the lanes idle), each
+    // wave reads four tokens' rows contiguously, and a wave sum takes four DPP
+    // steps instead of six.  One row in flight per token: the registers of the
+    // wider tiles leave room for no more at two waves per SIMD.  Measured on
+    // the read-by-read sweeps: L=32 / d=896 11.54 -> 10.80 ms, L=70 / d=640
+    // 37.2 -> 34.1 ms (a second row in flight: 11.45 and 34.6 ms).
+    if constexpr (!BLOCK && sizeof(TI) == 2) {
+        switch (p.nc <= 112 ? (p.nc + 15) / 16 : 0) {
+            case 1: return launch_stream<TI, TO, 16, 1, 4, BLOCK>(p, stream);
+            case 2: return launch_stream<TI, TO, 16, 2, 4, BLOCK>(p, stream);
+            case 3: return launch_stream<TI, TO, 16, 3, 2, BLOCK>(p, stream);
+            case 4: return launch_stream<TI, TO, 16, 4, 2, BLOCK>(p, stream);
+            case 5: return launch_stream<TI, TO, 16, 5, 1, BLOCK>(p, stream);
+            case 6: return launch_stream<TI, TO, 16, 6, 1, BLOCK>(p, stream);
+            case 7: return launch_stream<TI, TO, 16, 7, 1, BLOCK>(p, stream);
+            default: break;
+        }
+    }
     // LPT = 64 lanes per token, NCH chunks per lane: one token per wave
     const int nch = (p.nc + 63) / 64;
     switch (nch) {
