@@ -8,9 +8,10 @@ reuses the per-(row, token) RMS-scale cache).  Inputs are synthetic, seeded
 and already resident in HBM when the timed region starts.
 
 Printed: ONE JSON line with the throughput (tokens/s), a roofline object for
-the dominant kernel (algorithmic bytes per launch / mean launch duration from
-HIP events, against 8 TB/s), and the fp64 CPU oracle timed on a bounded token
-sample of the same workload.
+the dominant kernel (mean algorithmic bytes per launch / mean launch duration,
+the latter from HIP events over the timed region, which holds only that
+kernel's launches; against 8 TB/s), and the fp64 CPU oracle timed on a bounded
+token sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -111,6 +112,8 @@ def cpu_baseline(wl, hist, w, target_s: float = 15.0):
 
 PROFILE_WORKLOADS = {
     "block_S8_d2048_128k": "Block AttnRes two-phase forward, all 65 reads in one call, S=8",
+    "bwd_L24_d1024_full": "Full AttnRes backward, 48 sublayers + embedding, d=1024, 16384 tokens",
+    "bwd_L24_d1024_block_S4": "Block AttnRes (S=4) backward, 48 sublayers + embedding, d=1024, 16384 tokens",
     "block_S8_d2048_128k_model_order": "Block AttnRes S=8 in model order (phase 1 per group, phase 2 per row)",
     "full_L32_d896_batched": "Full AttnRes forward, all 65 reads in one call (rows staged in LDS)",
 }
@@ -122,6 +125,24 @@ def profile_run(name):
     import depth_wise_attention_attnres_amd as ar
     from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs
     dev = torch.device("cuda:0")
+    if name.startswith("bwd_"):
+        wl = WORKLOADS["fwdbwd_L24_d1024"]
+        h, w, g = device_inputs(wl, dev)
+        n, T, d = h.shape
+        dst = torch.empty_like(h)
+        dst.copy_(h)
+        del dst
+        variant, S = (ar.FULL, 1) if name.endswith("_full") else (ar.BLOCK, wl.S)
+        ws = torch.empty(ar.bwd_workspace_bytes(variant, S, n, T, d, 0, n), dtype=torch.uint8,
+                         device=dev)
+        dh = torch.empty_like(h)
+        dw = torch.empty((n, d), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            ar.bwd(variant, h, w, g, S=S, dhist=dh, dw=dw, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"profile run done: {name} ({PROFILE_WORKLOADS[name]}), history copy "
+              f"{h.numel() * h.element_size()} bytes", flush=True)
+        return
     wl = WORKLOADS["full_L32_d896" if name == "full_L32_d896_batched" else "block_S8_d2048_128k"]
     h, w, _ = device_inputs(wl, dev)
     n, T, d = h.shape
@@ -209,22 +230,32 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # per-launch durations of the dominant kernel: HIP events around each
-    # launch on the stream the library launches on (one extra sweep)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
-    torch.cuda.synchronize()
-    for l in range(n):
-        ev[l][0].record(stream)
-        ar.full_fwd(hist, w_rows[l], q_begin=l, n_q=1, rinv=rinv, rinv_valid_rows=l,
-                    out=out_rows[l], lse=lse_rows[l])
-        ev[l][1].record(stream)
-    torch.cuda.synchronize()
-    dur_ms = [a.elapsed_time(b) for a, b in ev]
+    # The step is nothing but the n launches of the dominant kernel, back to
+    # back on the library's stream (the rocprofv3 trace of this command shows
+    # no gaps), so its mean launch duration is the timed region over the
+    # launches it holds: HIP events on that stream, over the timed region.
     bytes_per_launch = [read_bytes_per_token(l, d) * T for l in range(n)]
     mean_bytes = sum(bytes_per_launch) / n
-    mean_ms = sum(dur_ms) / n
+    mean_ms = ms_per_step / n
     achieved = mean_bytes / (mean_ms * 1e-3) / 1e9
+
+    # diagnostic: the rate of single launches of a few lengths, from HIP events
+    # around each launch (these intervals include the launch gaps, so they are
+    # a lower bound of each kernel's own rate)
+    probe = [0, 8, 16, 32, n - 1]
+    ev = {l: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for l in probe}
+    torch.cuda.synchronize()
+    for l in range(n):
+        if l in ev:
+            ev[l][0].record(stream)
+        ar.full_fwd(hist, w_rows[l], q_begin=l, n_q=1, rinv=rinv, rinv_valid_rows=l,
+                    out=out_rows[l], lse=lse_rows[l])
+        if l in ev:
+            ev[l][1].record(stream)
+    torch.cuda.synchronize()
+    launch_gbs = {str(l): bytes_per_launch[l] / (ev[l][0].elapsed_time(ev[l][1]) * 1e-3) / 1e9
+                  for l in probe}
 
     # context: a plain device-to-device copy of the same size as one step's
     # history (read + write), the achievable streaming rate on this machine
@@ -271,6 +302,7 @@ def main():
             "kernel": "full_fwd_stream_kernel<bf16,bf16,16,7,1>",
             "mean_launch_ms": mean_ms,
             "mean_algorithmic_bytes_per_launch": mean_bytes,
+            "launch_GBps_by_read": launch_gbs,
         },
         "step_gbs": sum(bytes_per_launch) / (ms_per_step * 1e-3) / 1e9,
         "copy_gbs": copy_gbs,
