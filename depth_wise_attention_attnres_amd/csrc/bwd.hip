@@ -320,18 +320,17 @@ __global__ __launch_bounds__(64) void bwd_scores_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core scores (bf16 history and dout).  Per token the dots the
-// backward needs are  P = W X^T,  Q = G X^T  (reads x rows) and the Gram matrix
-// X X^T inside each block, all contractions over d with d contiguous in
-// memory -- the operand layout of v_mfma_f32_32x32x16_bf16, where lane j
-// supplies 8 consecutive elements k = 8 (j / 32) .. + 7 of row j % 32 of
-// both A and B.  bf16 x bf16 products are exact in fp32; the fp32 queries are
-// split once per call into three bf16 parts whose sum is w, so P keeps fp32
-// accuracy.  Row tiles are aligned to blocks (tile 0: rows 0 .. RT',
-// tile b: rows 1 + b RT' .. ; RT' a multiple of S, at most 31), so every
-// block sum and partial sum lies inside one tile and its squared norm is a
-// sum of that tile's Gram entries.  A source's dots are sums of row dots.
-// Then the per-read softmax and coefficients follow the streaming kernel.
+// Matrix-core coefficients of Full reads (bf16 history and dout).  Per token
+// the dots the backward needs are  P = W X^T  and  Q = G X^T  (reads x rows),
+// contractions over d with d contiguous in memory -- the operand layout of
+// v_mfma_f32_32x32x16_bf16, where lane j supplies 8 consecutive elements
+// k = 8 (j / 32) .. + 7 of row j % 32 of both A and B.  bf16 x bf16 products
+// are exact in fp32; the fp32 queries are split once per call into three bf16
+// parts whose sum is w, so P keeps fp32 accuracy.  A Full read's sources are
+// single rows, so the RMS scales need only |x_i|^2, which the waves form on
+// the vector ALUs from the row fragments they already hold.  Then, per read,
+// the softmax over its rows, delta, ds, and the coefficient rows written
+// straight to the workspace.
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -357,17 +356,19 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* ptr, bool ok) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// One wave per (row tile b, read tile a) pair whose reads see rows of the
-// tile (pairs in order of b, then a); the first pair of each row tile also
-// forms the tile's Gram matrix.  Every wave then takes reads lq = wave,
-// wave + nwaves, ... for the softmax.  n_q <= 64 (at most two read tiles).
-__global__ __launch_bounds__(512) void bwd_scores_mfma_kernel(BwdParams p, int rtp, int nb) {
+// Eight waves per token.  Wave k < (number of pairs) takes the k-th (row tile
+// b, read tile a) pair whose reads see rows of the tile: row tile b is rows
+// 32 b .. 32 b + 31, read tile a reads 32 a .. ; the first pair of each row
+// tile also forms the tile's |x_i|^2.  All waves load the operand slices and
+// then take reads lq = wave, wave + 8, ... for the softmax.  n_q <= 64 (at
+// most two read tiles), q_begin + n_q <= 128 (at most four row tiles: at most
+// eight pairs).
+__global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int nb) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6, ln = tid & 63;
     const int h = ln >> 5, m = ln & 31;
     const int nwaves = blockDim.x >> 6;
     const int64_t t = blockIdx.x;
-    const int S = p.S;
     const int nr = p.q_begin + p.n_q;  // rows any read of the call sees
     const int na = (p.n_q + 31) / 32;  // read tiles
     const int64_t row_elems = p.T * (int64_t)p.d;
@@ -377,24 +378,19 @@ __global__ __launch_bounds__(512) void bwd_scores_mfma_kernel(BwdParams p, int r
     extern __shared__ float lds[];
     float* P = lds;                          // [n_q][nr] w_l . x_i
     float* Q = P + p.n_q * nr;               // [n_q][nr] g_l . x_i
-    float* G = Q + p.n_q * nr;               // [nb][32][32] Gram tiles
-    float* pn = G + nb * 1024;               // [nr] squared norm of the in-block prefix sum ending at the row
-    float* c1a = pn + nr;                    // [n_q][nx] alpha of each read's sources
-    float* c2a = c1a + p.n_q * p.nx;         // [n_q][nx] ds r of each read's sources
-    float* c3w = c2a + p.n_q * p.nx;         // [nwaves][n_blk]
-    int* blk = reinterpret_cast<int*>(c3w + nwaves * p.n_blk);  // [nh8] block of each row (v_0: 0)
-    for (int i = tid; i < p.nh8; i += blockDim.x) blk[i] = i == 0 ? 0 : (i - 1) / S + 1;
-
-    for (int i = tid; i < nwaves * p.n_blk; i += blockDim.x) c3w[i] = 0.f;
+    float* pn = Q + p.n_q * nr;              // [nr] |x_i|^2
+    float* c3w = pn + nr;                    // [nwaves][nr] C3 summed over each wave's reads
+    for (int i = tid; i < nwaves * nr; i += blockDim.x) c3w[i] = 0.f;
 
     // ---- dots on the matrix cores -------------------------------------------
-    // this wave's pair: walk the row tiles, each with read tiles a_min(b) .. na-1
+    // this wave's pair: walk the row tiles, each with read tiles amin(b) .. na-1
+    // (read l sees rows 0..l, so a read tile sees row tile b when its last
+    // read reaches 32 b)
     int b = -1, a = 0, first_a = 0;
     {
         int k = wave;
         for (int bb = 0; bb < nb && b < 0; ++bb) {
-            const int f = bb == 0 ? 0 : 1 + bb * rtp;
-            const int amin = f - p.q_begin - 31 > 0 ? (f - p.q_begin) / 32 : 0;
+            const int amin = 32 * bb - p.q_begin - 31 > 0 ? (32 * bb - p.q_begin) / 32 : 0;
             const int cnt = na - amin;
             if (k < cnt) {
                 b = bb;
@@ -405,58 +401,104 @@ __global__ __launch_bounds__(512) void bwd_scores_mfma_kernel(BwdParams p, int r
             }
         }
     }
-    if (b >= 0) {
-        const int f = b == 0 ? 0 : 1 + b * rtp;  // first row of the tile
-        int e = 1 + (b + 1) * rtp;                // end of the tile
-        if (e > nr) e = nr;
-        const bool gram = a == first_a;
-        const int row = f + m;
-        const bool row_ok = row < e;
-        const bf16_t* xp = hist_tok + (int64_t)(row_ok ? row : 0) * row_elems + 8 * h;
-        const int lq = 32 * a + m;
-        const bool rd_ok = lq < p.n_q;
-        const int lqc = rd_ok ? lq : 0;
-        const bf16_t* wp0 = reinterpret_cast<const bf16_t*>(p.ws_wsplit) + (int64_t)lqc * p.d + 8 * h;
-        const int64_t wsz = (int64_t)p.n_q * p.d;
-        const bf16_t* gp = dout_tok + (int64_t)lqc * row_elems + 8 * h;
+    // K goes in stages of kStage elements.  The stage's slices of the rows
+    // (X), the reads' upstream gradients (G) and the three query parts (W) --
+    // nr + 4 n_q slices of kStage bf16 each -- are brought into LDS with
+    // coalesced 16-byte loads (eight lanes per 128-byte slice), staged in
+    // registers while the previous stage multiplies, then every wave reads
+    // its matrix operands from LDS.  (Loaded straight from memory, each
+    // operand load touched 32 rows' cache lines for 32 bytes each.)
+    constexpr int kStage = 64, kRowLds = kStage + 8;  // bf16 per LDS row (padded)
+    const int n_sl = nr + 4 * p.n_q;                   // X, G, W0, W1, W2 slices
+    // [n_sl][kRowLds], 16-byte aligned
+    bf16_t* sl = reinterpret_cast<bf16_t*>(lds + ((2 * p.n_q * nr + nr + nwaves * nr + 3) & ~3));
+    const int64_t wsz = (int64_t)p.n_q * p.d;
+    auto slice_src = [&](int r) -> const bf16_t* {  // start of slice r's row
+        if (r < nr) return hist_tok + (int64_t)r * row_elems;
+        r -= nr;
+        if (r < p.n_q) return dout_tok + (int64_t)r * row_elems;
+        r -= p.n_q;
+        return reinterpret_cast<const bf16_t*>(p.ws_wsplit) + (int64_t)(r / p.n_q) * wsz +
+               (int64_t)(r % p.n_q) * p.d;
+    };
+    const int n_chunks = n_sl * (kStage / 8);  // 16-byte chunks per stage
+    // chunks per thread with the 512 threads of the launch (at most 128 rows
+    // and 64 reads: 384 slices)
+    constexpr int kMaxPer = (128 + 4 * 64) * (kStage / 8) / 512;
+    const int per = (n_chunks + blockDim.x - 1) / blockDim.x;
+    u32x4 stg[kMaxPer];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int c = 0; c < kMaxPer; ++c) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            const int idx = tid + blockDim.x * c;
+            if (c < per && idx < n_chunks) {
+                const int r = idx >> 3, k = k0 + 8 * (idx & 7);
+                if (k < p.d) v = *reinterpret_cast<const u32x4*>(slice_src(r) + k);
+            }
+            stg[c] = v;
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int c = 0; c < kMaxPer; ++c) {
+            const int idx = tid + blockDim.x * c;
+            if (c < per && idx < n_chunks)
+                *reinterpret_cast<u32x4*>(sl + (idx >> 3) * kRowLds + 8 * (idx & 7)) = stg[c];
+        }
+    };
+    auto frag = [&](int r, int k) {  // 8 bf16 of LDS slice r at element k
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(sl + r * kRowLds + k));
+    };
 
-        // The matrix accumulators are folded into fp32 totals every kFold
-        // K-steps, so no sum runs longer than d / (16 kFold) + kFold terms
-        // (the scores feed exponentials, whose relative error is the
-        // absolute error of the score).
-        constexpr int kFold = 16;
-        f32x16 accG, accP, accQ, totP, totQ;
+    const bool norms = b >= 0 && a == first_a;
+    const int row = 32 * (b < 0 ? 0 : b) + m;
+    const bool row_ok = b >= 0 && row < nr;
+    const int lq_w = 32 * a + m;
+    const bool rd_ok = b >= 0 && lq_w < p.n_q;
+    const int xr = row_ok ? row : 0, lr = rd_ok ? lq_w : 0;
+    // The matrix accumulators are folded into fp32 totals every kFold
+    // K-steps, so no sum runs longer than d / (16 kFold) + kFold terms (the
+    // scores feed exponentials, whose relative error is the absolute error
+    // of the score).
+    constexpr int kFold = 16;
+    f32x16 accP, accQ, totP, totQ;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) accG[r] = accP[r] = accQ[r] = totP[r] = totQ[r] = 0.f;
-        // operands of the next kPD K-steps, in a ring (one slot per step)
-        constexpr int kPD = 2;
-        bf16x8_t rx[kPD], rw0[kPD], rw1[kPD], rw2[kPD], rg[kPD];
-        auto fetch = [&](int u, int k0) {
-            const bool kok = k0 + 8 * h < p.d;  // d % 8 == 0: all eight or none
-            const bool ok = rd_ok && kok;
-            rx[u] = load_bf16x8(xp + k0, row_ok && kok);
-            rw0[u] = load_bf16x8(wp0 + k0, ok);
-            rw1[u] = load_bf16x8(wp0 + wsz + k0, ok);
-            rw2[u] = load_bf16x8(wp0 + 2 * wsz + k0, ok);
-            rg[u] = load_bf16x8(gp + k0, ok);
-        };
+    for (int r = 0; r < 16; ++r) accP[r] = accQ[r] = totP[r] = totQ[r] = 0.f;
+    float sq = 0.f;  // this lane's part of |x_row|^2
+    const int n_stages = (p.d + kStage - 1) / kStage;
+    gload(0);
+    lstore();
+    __syncthreads();
+    int st = 0;  // K-steps of 16 done
+    for (int sg = 0; sg < n_stages; ++sg) {
+        if (sg + 1 < n_stages) gload((sg + 1) * kStage);
+        if (b >= 0) {
 #pragma unroll
-        for (int u = 0; u < kPD; ++u)
-            if (16 * u < p.d) fetch(u, 16 * u);
-        const int n_steps = (p.d + 15) / 16;
-        for (int s0 = 0; s0 < n_steps; s0 += kPD) {
+            for (int sub = 0; sub < kStage / 16; ++sub) {
+                const int k = 16 * sub + 8 * h;
+                if (16 * (sg * (kStage / 16) + sub) >= p.d) break;
+                const bf16x8_t x = frag(xr, k);
+                const bf16x8_t g = frag(nr + lr, k);
+                const bf16x8_t w0 = frag(nr + p.n_q + lr, k);
+                const bf16x8_t w1 = frag(nr + 2 * p.n_q + lr, k);
+                const bf16x8_t w2 = frag(nr + 3 * p.n_q + lr, k);
+                if (norms) {
+                    const u32x4 xv = __builtin_bit_cast(u32x4, x);
 #pragma unroll
-            for (int u = 0; u < kPD; ++u) {
-                const int st = s0 + u;
-                if (st >= n_steps) break;
-                const bf16x8_t x = rx[u], w0 = rw0[u], w1 = rw1[u], w2 = rw2[u], g = rg[u];
-                if (st + kPD < n_steps) fetch(u, 16 * (st + kPD));
-                if (gram) accG = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, x, accG, 0, 0, 0);
+                    for (int e = 0; e < 4; ++e) {
+                        const float lo = __uint_as_float(xv[e] << 16);
+                        const float hi = __uint_as_float(xv[e] & 0xffff0000u);
+                        sq = fmaf(lo, lo, sq);
+                        sq = fmaf(hi, hi, sq);
+                    }
+                }
                 accP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w2, x, accP, 0, 0, 0);
                 accP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1, x, accP, 0, 0, 0);
                 accP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w0, x, accP, 0, 0, 0);
                 accQ = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g, x, accQ, 0, 0, 0);
-                if ((st + 1) % kFold == 0 || st + 1 == n_steps) {
+                ++st;
+                if (st % kFold == 0) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         totP[r] += accP[r];
@@ -466,11 +508,26 @@ __global__ __launch_bounds__(512) void bwd_scores_mfma_kernel(BwdParams p, int r
                 }
             }
         }
+        if (sg + 1 < n_stages) {
+            __syncthreads();  // every wave is done with this stage's slices
+            lstore();
+            __syncthreads();
+        }
+    }
+    if (b >= 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            totP[r] += accP[r];
+            totQ[r] += accQ[r];
+        }
+        if (norms) {  // lanes m and m + 32 hold the two halves of each step's k
+            sq = swap32_sum(sq);
+            if (h == 0 && row_ok) pn[row] = sq;
+        }
         // lane j, register r holds D[i][n = m], i = 8 (r / 4) + 4 h + r % 4
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = 8 * (r / 4) + 4 * h + r % 4;
-            if (gram) G[b * 1024 + i * 32 + m] = accG[r];
             const int lqo = 32 * a + i;
             if (row_ok && lqo < p.n_q) {
                 P[lqo * nr + row] = totP[r];
@@ -480,135 +537,60 @@ __global__ __launch_bounds__(512) void bwd_scores_mfma_kernel(BwdParams p, int r
     }
     __syncthreads();
 
-    // squared norm of the in-block prefix sum ending at each row (v_0 alone)
-    for (int r = tid; r < nr; r += blockDim.x) {
-        const int b = r == 0 ? 0 : (r - 1) / rtp;
-        const int f = b == 0 ? 0 : 1 + b * rtp;
-        const int bs = r == 0 ? 0 : ((r - 1) / S) * S + 1;
-        const float* g = G + b * 1024;
-        float sq = 0.f;
-        for (int i = bs; i <= r; ++i)
-            for (int i2 = bs; i2 <= r; ++i2) sq += g[(i - f) * 32 + (i2 - f)];
-        pn[r] = sq;
-    }
-    __syncthreads();
-
-    // ---- per read: softmax over the sources, ds, coefficients --------------
+    // ---- per read: softmax over its rows, ds, coefficients ------------------
     float* A1 = p.ws_a1 + t * (int64_t)p.n_q * p.nh8;
     float* A2 = p.ws_a2 + t * (int64_t)p.n_q * p.nh8;
     float* A2T = p.ws_a2t + t * (int64_t)p.n_hist * p.nq8;
-    float* c3s = c3w + wave * p.n_blk;
+    float* c3s = c3w + wave * nr;
     for (int lq = wave; lq < p.n_q; lq += nwaves) {
         const int l = p.q_begin + lq;
-        const int mb = l / S;                         // completed blocks
-        const int ns = mb + 1 + (l % S != 0 ? 1 : 0);  // v_0, blocks, partial
+        const int ns = l + 1;  // rows 0..l, one source each
         const float* Pl = P + lq * nr;
         const float* Ql = Q + lq * nr;
-        float* c1s = c1a + lq * p.nx;
-        float* c2s = c2a + lq * p.nx;
-        // lanes hold sources ln, ln + 64, ...: rows [r0, r1] of source xs
-        auto src_rows = [&](int xs, int& r0, int& r1) {
-            if (xs == 0) {
-                r0 = r1 = 0;
-            } else if (xs <= mb) {
-                r0 = (xs - 1) * S + 1;
-                r1 = xs * S;
-            } else {
-                r0 = mb * S + 1;
-                r1 = l;
-            }
-        };
-        // one pass forms each lane's first source; later sources (more than
-        // 64 of them) are recomputed in the later passes
+        // lanes hold rows ln, ln + 64, ...; later rows (more than 64) are
+        // recomputed in each pass
         float mx = -INFINITY;
-        for (int xs = ln; xs < ns; xs += 64) {
-            int r0, r1;
-            src_rows(xs, r0, r1);
-            float wx = 0.f;
-            for (int i = r0; i <= r1; ++i) wx += Pl[i];
-            const float r = fast_rsqrt(fmaf(pn[r1], p.inv_d, p.eps));
-            mx = fmaxf(mx, r * wx);
-        }
+        for (int i = ln; i < ns; i += 64)
+            mx = fmaxf(mx, fast_rsqrt(fmaf(pn[i], p.inv_d, p.eps)) * Pl[i]);
         mx = tg_max<64>(mx);
-        float z = 0.f;
-        for (int xs = ln; xs < ns; xs += 64) {
-            int r0, r1;
-            src_rows(xs, r0, r1);
-            float wx = 0.f;
-            for (int i = r0; i <= r1; ++i) wx += Pl[i];
-            const float r = fast_rsqrt(fmaf(pn[r1], p.inv_d, p.eps));
-            z += fast_exp2((r * wx - mx) * kLog2e);
+        float z = 0.f, zd = 0.f;  // sum of e and of e * a
+        for (int i = ln; i < ns; i += 64) {
+            const float e = fast_exp2((fast_rsqrt(fmaf(pn[i], p.inv_d, p.eps)) * Pl[i] - mx) * kLog2e);
+            z += e;
+            zd = fmaf(e, Ql[i], zd);
         }
         z = tg_sum<64>(z);
+        zd = tg_sum<64>(zd);
         const float inv_z = 1.0f / z;
-        float delta = 0.f;
-        for (int xs = ln; xs < ns; xs += 64) {
-            int r0, r1;
-            src_rows(xs, r0, r1);
-            float wx = 0.f, gx = 0.f;
-            for (int i = r0; i <= r1; ++i) {
-                wx += Pl[i];
-                gx += Ql[i];
-            }
-            const float r = fast_rsqrt(fmaf(pn[r1], p.inv_d, p.eps));
-            const float alpha = fast_exp2((r * wx - mx) * kLog2e) * inv_z;
-            delta = fmaf(alpha, gx, delta);
-        }
-        delta = tg_sum<64>(delta);
-        for (int xs = ln; xs < ns; xs += 64) {
-            int r0, r1;
-            src_rows(xs, r0, r1);
-            float wx = 0.f, gx = 0.f;
-            for (int i = r0; i <= r1; ++i) {
-                wx += Pl[i];
-                gx += Ql[i];
-            }
-            const float r = fast_rsqrt(fmaf(pn[r1], p.inv_d, p.eps));
-            const float s = r * wx;
-            const float alpha = fast_exp2((s - mx) * kLog2e) * inv_z;
-            const float ds = alpha * (gx - delta);
-            c1s[xs] = alpha;
-            c2s[xs] = ds * r;
-            const float c3 = ds * r * r * s * p.inv_d;
-            if (xs <= mb)
-                c3s[xs] += c3;  // same lane for a slot on every read of this wave
-            else
-                p.ws_kappa[t * p.n_q + lq] = c3;  // the partial sum of this read
-        }
-        if (ln == 0 && l % S == 0) p.ws_kappa[t * p.n_q + lq] = 0.f;  // no partial
-        // the coefficient arrays of this read are written and read by this wave
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float delta = zd * inv_z;
         for (int i = ln; i < p.nh8; i += 64) {  // row-major A1 / A2: contiguous in i
             float c1 = 0.f, c2 = 0.f;
-            if (i <= l) {
-                const int c = blk[i];
-                const int xs = c <= mb ? c : mb + 1;
-                c1 = c1s[xs];
-                c2 = c2s[xs];
+            if (i < ns) {
+                const float r = fast_rsqrt(fmaf(pn[i], p.inv_d, p.eps));
+                const float s = r * Pl[i];
+                const float alpha = fast_exp2((s - mx) * kLog2e) * inv_z;
+                const float ds = alpha * (Ql[i] - delta);
+                c1 = alpha;
+                c2 = ds * r;
+                c3s[i] += ds * r * r * s * p.inv_d;  // same lane for a row on every read of this wave
             }
             A1[(int64_t)lq * p.nh8 + i] = c1;
             A2[(int64_t)lq * p.nh8 + i] = c2;
+            if (i < p.n_hist) A2T[(int64_t)i * p.nq8 + lq] = c2;
         }
+        if (ln == 0) p.ws_kappa[t * p.n_q + lq] = 0.f;  // Full: no partial sums
+    }
+    // the padding reads n_q .. nq8 - 1 of A2T are zero
+    for (int k = tid; k < p.n_hist * (p.nq8 - p.n_q); k += blockDim.x) {
+        const int i = k / (p.nq8 - p.n_q);
+        A2T[(int64_t)i * p.nq8 + p.n_q + k % (p.nq8 - p.n_q)] = 0.f;
     }
     __syncthreads();
-    // transposed A2: contiguous in the read (the padding reads are zero)
-    for (int k = tid; k < p.n_hist * p.nq8; k += blockDim.x) {
-        const int i = k / p.nq8, lq = k - i * p.nq8;
-        float c2 = 0.f;
-        const int l = p.q_begin + lq;
-        if (lq < p.n_q && i <= l) {
-            const int mb = l / S;
-            const int c = blk[i];
-            c2 = c2a[lq * p.nx + (c <= mb ? c : mb + 1)];
-        }
-        A2T[k] = c2;
-    }
-    // C3 summed over the waves in a fixed order
+    // C3 summed over the waves in a fixed order; rows no read sees get 0
     for (int i = tid; i < p.n_blk; i += blockDim.x) {
         float c3 = 0.f;
-        for (int w = 0; w < nwaves; ++w) c3 += c3w[w * p.n_blk + i];
+        if (i < nr)
+            for (int w = 0; w < nwaves; ++w) c3 += c3w[w * nr + i];
         p.ws_c3[t * p.n_blk + i] = c3;
     }
 }
@@ -1007,19 +989,17 @@ BwdLayout bwd_layout(int64_t S, int64_t n_hist, int64_t T, int64_t d, int64_t n_
 namespace {
 
 
-// Row tiling of the matrix-core scores: tile 0 holds rows 0 .. rtp, tile b
-// rows 1 + b rtp .. (rtp a multiple of S, at most 31).  Returns the number of
-// tiles, or 0 when the call does not take the matrix-core kernel (then the
-// streaming kernel runs).  The kernel itself handles any S <= 31.
-int scores_mfma_tiles(const BwdParams& p, int& rtp) {
+// Row tiles of the matrix-core coefficients (Full reads, bf16 history and
+// upstream gradient, at most 64 reads and 128 rows): the number of 32-row
+// tiles, or 0 when another kernel forms the coefficients.  Block keeps the
+// other kernels: its sources are fewer than its rows, and the 32-row operand
+// loads cost more there than the dots they feed (measured at 49 rows,
+// d = 1024, S = 4: 3.6 against 2.5 ms).
+int scores_mfma_tiles(const BwdParams& p) {
     if (p.hist_dt != ATTNRES_BF16 || p.dout_dt != ATTNRES_BF16) return 0;
-    // Block (S > 1) keeps the streaming kernel: its sources are fewer than the
-    // rows, and the matrix-core kernel's 32-row operand loads cost more there
-    // than the dots they feed (measured at 49 rows, d = 1024, S = 4)
     if (p.S != 1 || p.n_q > 64) return 0;
-    rtp = p.S * (31 / p.S);
     const int nr = p.q_begin + p.n_q;
-    const int nb = nr <= 1 + rtp ? 1 : 1 + (nr - 1 - rtp + rtp - 1) / rtp;
+    const int nb = (nr + 31) / 32;
     return nb <= 4 ? nb : 0;
 }
 
@@ -1030,31 +1010,27 @@ constexpr int kStreamR[9] = {0, 4, 4, 2, 2, 1, 1, 1, 1};
 // Which kernel forms the per-read coefficients of a call, and its dynamic LDS.
 struct ScoresPlan {
     enum Kind { NONE, MFMA, GROUP, STREAM } kind;
-    int rtp, nb, nwaves;  // MFMA: row tiling and waves per workgroup
+    int nb, nwaves;       // MFMA: row tiles and waves per workgroup
     size_t lds;           // MFMA, STREAM
 };
 
 ScoresPlan plan_scores(const BwdParams& p) {
-    ScoresPlan s{ScoresPlan::NONE, 0, 0, 0, 0};
+    ScoresPlan s{ScoresPlan::NONE, 0, 0, 0};
     const int max_lds = device_max_lds();
-    int rtp = 0;
-    const int nb = scores_mfma_tiles(p, rtp);
+    const int nb = scores_mfma_tiles(p);
     if (nb > 0) {
         const int nr = p.q_begin + p.n_q;
         // one wave per (row tile, read tile) pair whose reads see the tile
         const int na = (p.n_q + 31) / 32;
         int nwaves = 0;
         for (int b = 0; b < nb; ++b) {
-            const int f = b == 0 ? 0 : 1 + b * rtp;
-            const int amin = f - p.q_begin - 31 > 0 ? (f - p.q_begin) / 32 : 0;
+            const int amin = 32 * b - p.q_begin - 31 > 0 ? (32 * b - p.q_begin) / 32 : 0;
             nwaves += na - amin;
         }
-        const size_t lds = sizeof(float) * (2 * (size_t)p.n_q * nr + (size_t)nb * 1024 + nr +
-                                            2 * (size_t)p.n_q * p.nx + (size_t)nwaves * p.n_blk +
-                                            p.nh8);
+        const size_t lds = sizeof(float) * ((2 * (size_t)p.n_q * nr + nr + 8 * (size_t)nr + 3) & ~(size_t)3) +
+                           2 * (size_t)(nr + 4 * p.n_q) * (64 + 8);  // the stage's bf16 slices
         if (lds <= (size_t)max_lds) {  // else one of the kernels below
             s.kind = ScoresPlan::MFMA;
-            s.rtp = rtp;
             s.nb = nb;
             s.nwaves = nwaves;
             s.lds = lds;
@@ -1083,10 +1059,10 @@ hipError_t launch_scores(const BwdParams& p, const ScoresPlan& s, hipStream_t st
                            p.w, nw, hi, hi + nw, hi + 2 * nw);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        e = prepare_dynamic_lds((const void*)bwd_scores_mfma_kernel, s.lds);
+        e = prepare_dynamic_lds((const void*)bwd_scores_full_kernel, s.lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_scores_mfma_kernel, dim3((unsigned)p.T), dim3(64 * s.nwaves), s.lds,
-                           stream, p, s.rtp, s.nb);
+        hipLaunchKernelGGL(bwd_scores_full_kernel, dim3((unsigned)p.T), dim3(512), s.lds, stream,
+                           p, s.nb);
         return hipGetLastError();
     }
     if (s.kind == ScoresPlan::GROUP) return launch_bwd_scores_group(p, stream);
