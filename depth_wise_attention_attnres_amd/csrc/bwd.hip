@@ -356,39 +356,51 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* ptr, bool ok) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Eight waves per token.  Wave k < (number of pairs) takes the k-th (row tile
-// b, read tile a) pair whose reads see rows of the tile: row tile b is rows
+// Eight waves per workgroup, TT tokens per workgroup (the three query parts
+// are the same for every token, so two tokens share their slices).  Wave
+// w < TT * npairs takes token w / npairs and the (w % npairs)-th (row tile b,
+// read tile a) pair whose reads see rows of the tile: row tile b is rows
 // 32 b .. 32 b + 31, read tile a reads 32 a .. ; the first pair of each row
 // tile also forms the tile's |x_i|^2.  All waves load the operand slices and
-// then take reads lq = wave, wave + 8, ... for the softmax.  n_q <= 64 (at
-// most two read tiles), q_begin + n_q <= 128 (at most four row tiles: at most
-// eight pairs).
-__global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int nb) {
+// then take (token, read) jobs wave, wave + 8, ... for the softmax.  n_q <= 64
+// (at most two read tiles), q_begin + n_q <= 128 (at most four row tiles).
+constexpr int kScStage = 64;                  // K elements per stage
+constexpr int kScRowLds = kScStage + 8;       // bf16 per LDS slice row (padded)
+constexpr int kScMaxPer = 6;                  // 16-byte chunks per thread and stage
+constexpr int kScMaxSlices = kScMaxPer * 512 / (kScStage / 8);  // 384
+
+// LDS floats before the slices (P, Q, |x|^2, per-wave C3), rounded up to 16 bytes
+__host__ __device__ inline int sc_lds_floats(int tt, int n_q, int nr) {
+    return (2 * tt * n_q * nr + tt * nr + 8 * tt * nr + 3) & ~3;
+}
+
+template <int TT>
+__global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int nb, int npairs) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6, ln = tid & 63;
     const int h = ln >> 5, m = ln & 31;
-    const int nwaves = blockDim.x >> 6;
-    const int64_t t = blockIdx.x;
+    constexpr int nwaves = 8;
+    const int64_t t0 = (int64_t)blockIdx.x * TT;
+    const int ntok = p.T - t0 < TT ? (int)(p.T - t0) : TT;
     const int nr = p.q_begin + p.n_q;  // rows any read of the call sees
     const int na = (p.n_q + 31) / 32;  // read tiles
     const int64_t row_elems = p.T * (int64_t)p.d;
-    const bf16_t* hist_tok = static_cast<const bf16_t*>(p.hist) + t * p.d;
-    const bf16_t* dout_tok = static_cast<const bf16_t*>(p.dout) + t * p.d;
 
     extern __shared__ float lds[];
-    float* P = lds;                          // [n_q][nr] w_l . x_i
-    float* Q = P + p.n_q * nr;               // [n_q][nr] g_l . x_i
-    float* pn = Q + p.n_q * nr;              // [nr] |x_i|^2
-    float* c3w = pn + nr;                    // [nwaves][nr] C3 summed over each wave's reads
-    for (int i = tid; i < nwaves * nr; i += blockDim.x) c3w[i] = 0.f;
+    float* P = lds;                          // [TT][n_q][nr] w_l . x_i
+    float* Q = P + TT * p.n_q * nr;          // [TT][n_q][nr] g_l . x_i
+    float* pn = Q + TT * p.n_q * nr;         // [TT][nr] |x_i|^2
+    float* c3w = pn + TT * nr;               // [nwaves][TT][nr] C3 summed over each wave's reads
+    for (int i = tid; i < nwaves * TT * nr; i += blockDim.x) c3w[i] = 0.f;
 
     // ---- dots on the matrix cores -------------------------------------------
     // this wave's pair: walk the row tiles, each with read tiles amin(b) .. na-1
     // (read l sees rows 0..l, so a read tile sees row tile b when its last
     // read reaches 32 b)
+    const int u = wave / npairs;  // this wave's token in the workgroup
     int b = -1, a = 0, first_a = 0;
-    {
-        int k = wave;
+    if (u < ntok) {
+        int k = wave - u * npairs;
         for (int bb = 0; bb < nb && b < 0; ++bb) {
             const int amin = 32 * bb - p.q_begin - 31 > 0 ? (32 * bb - p.q_begin) / 32 : 0;
             const int cnt = na - amin;
@@ -401,54 +413,54 @@ __global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int n
             }
         }
     }
-    // K goes in stages of kStage elements.  The stage's slices of the rows
-    // (X), the reads' upstream gradients (G) and the three query parts (W) --
-    // nr + 4 n_q slices of kStage bf16 each -- are brought into LDS with
-    // coalesced 16-byte loads (eight lanes per 128-byte slice), staged in
-    // registers while the previous stage multiplies, then every wave reads
-    // its matrix operands from LDS.  (Loaded straight from memory, each
-    // operand load touched 32 rows' cache lines for 32 bytes each.)
-    constexpr int kStage = 64, kRowLds = kStage + 8;  // bf16 per LDS row (padded)
-    const int n_sl = nr + 4 * p.n_q;                   // X, G, W0, W1, W2 slices
-    // [n_sl][kRowLds], 16-byte aligned
-    bf16_t* sl = reinterpret_cast<bf16_t*>(lds + ((2 * p.n_q * nr + nr + nwaves * nr + 3) & ~3));
+    // K goes in stages of kScStage elements.  The stage's slices of each
+    // token's rows (X) and upstream gradients (G), and of the three query
+    // parts (W) -- TT (nr + n_q) + 3 n_q slices of kScStage bf16 each -- are
+    // brought into LDS with coalesced 16-byte loads (eight lanes per 128-byte
+    // slice), staged in registers while the previous stage multiplies, then
+    // every wave reads its matrix operands from LDS.  (Loaded straight from
+    // memory, each operand load touched 32 rows' cache lines for 32 bytes.)
+    const int per_tok = nr + p.n_q;
+    const int n_sl = TT * per_tok + 3 * p.n_q;
+    bf16_t* sl = reinterpret_cast<bf16_t*>(lds + sc_lds_floats(TT, p.n_q, nr));  // [n_sl][kScRowLds]
     const int64_t wsz = (int64_t)p.n_q * p.d;
-    auto slice_src = [&](int r) -> const bf16_t* {  // start of slice r's row
-        if (r < nr) return hist_tok + (int64_t)r * row_elems;
-        r -= nr;
-        if (r < p.n_q) return dout_tok + (int64_t)r * row_elems;
-        r -= p.n_q;
+    auto slice_src = [&](int r) -> const bf16_t* {  // start of slice r's row, or null (zeros)
+        if (r < TT * per_tok) {
+            const int tu = r / per_tok, rr = r - tu * per_tok;
+            if (tu >= ntok) return nullptr;
+            const int64_t t = t0 + tu;
+            if (rr < nr) return static_cast<const bf16_t*>(p.hist) + rr * row_elems + t * p.d;
+            return static_cast<const bf16_t*>(p.dout) + (rr - nr) * row_elems + t * p.d;
+        }
+        r -= TT * per_tok;
         return reinterpret_cast<const bf16_t*>(p.ws_wsplit) + (int64_t)(r / p.n_q) * wsz +
                (int64_t)(r % p.n_q) * p.d;
     };
-    const int n_chunks = n_sl * (kStage / 8);  // 16-byte chunks per stage
-    // chunks per thread with the 512 threads of the launch (at most 128 rows
-    // and 64 reads: 384 slices)
-    constexpr int kMaxPer = (128 + 4 * 64) * (kStage / 8) / 512;
-    const int per = (n_chunks + blockDim.x - 1) / blockDim.x;
-    u32x4 stg[kMaxPer];
+    const int n_chunks = n_sl * (kScStage / 8);  // 16-byte chunks per stage (<= kScMaxPer * 512)
+    u32x4 stg[kScMaxPer];
     auto gload = [&](int k0) {
 #pragma unroll
-        for (int c = 0; c < kMaxPer; ++c) {
+        for (int c = 0; c < kScMaxPer; ++c) {
             u32x4 v = {0u, 0u, 0u, 0u};
-            const int idx = tid + blockDim.x * c;
-            if (c < per && idx < n_chunks) {
+            const int idx = tid + 512 * c;
+            if (idx < n_chunks) {
                 const int r = idx >> 3, k = k0 + 8 * (idx & 7);
-                if (k < p.d) v = *reinterpret_cast<const u32x4*>(slice_src(r) + k);
+                const bf16_t* src = slice_src(r);
+                if (src != nullptr && k < p.d) v = *reinterpret_cast<const u32x4*>(src + k);
             }
             stg[c] = v;
         }
     };
     auto lstore = [&]() {
 #pragma unroll
-        for (int c = 0; c < kMaxPer; ++c) {
-            const int idx = tid + blockDim.x * c;
-            if (c < per && idx < n_chunks)
-                *reinterpret_cast<u32x4*>(sl + (idx >> 3) * kRowLds + 8 * (idx & 7)) = stg[c];
+        for (int c = 0; c < kScMaxPer; ++c) {
+            const int idx = tid + 512 * c;
+            if (idx < n_chunks)
+                *reinterpret_cast<u32x4*>(sl + (idx >> 3) * kScRowLds + 8 * (idx & 7)) = stg[c];
         }
     };
     auto frag = [&](int r, int k) {  // 8 bf16 of LDS slice r at element k
-        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(sl + r * kRowLds + k));
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(sl + r * kScRowLds + k));
     };
 
     const bool norms = b >= 0 && a == first_a;
@@ -456,7 +468,10 @@ __global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int n
     const bool row_ok = b >= 0 && row < nr;
     const int lq_w = 32 * a + m;
     const bool rd_ok = b >= 0 && lq_w < p.n_q;
-    const int xr = row_ok ? row : 0, lr = rd_ok ? lq_w : 0;
+    const int uu = u < TT ? u : 0;
+    const int xs = uu * per_tok + (row_ok ? row : 0);             // X slice of this lane's row
+    const int gs = uu * per_tok + nr + (rd_ok ? lq_w : 0);        // G slice of this lane's read
+    const int ws0 = TT * per_tok + (rd_ok ? lq_w : 0);            // W0 slice; W1, W2 follow by n_q
     // The matrix accumulators are folded into fp32 totals every kFold
     // K-steps, so no sum runs longer than d / (16 kFold) + kFold terms (the
     // scores feed exponentials, whose relative error is the absolute error
@@ -466,23 +481,23 @@ __global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int n
 #pragma unroll
     for (int r = 0; r < 16; ++r) accP[r] = accQ[r] = totP[r] = totQ[r] = 0.f;
     float sq = 0.f;  // this lane's part of |x_row|^2
-    const int n_stages = (p.d + kStage - 1) / kStage;
+    const int n_stages = (p.d + kScStage - 1) / kScStage;
     gload(0);
     lstore();
     __syncthreads();
     int st = 0;  // K-steps of 16 done
     for (int sg = 0; sg < n_stages; ++sg) {
-        if (sg + 1 < n_stages) gload((sg + 1) * kStage);
+        if (sg + 1 < n_stages) gload((sg + 1) * kScStage);
         if (b >= 0) {
 #pragma unroll
-            for (int sub = 0; sub < kStage / 16; ++sub) {
+            for (int sub = 0; sub < kScStage / 16; ++sub) {
                 const int k = 16 * sub + 8 * h;
-                if (16 * (sg * (kStage / 16) + sub) >= p.d) break;
-                const bf16x8_t x = frag(xr, k);
-                const bf16x8_t g = frag(nr + lr, k);
-                const bf16x8_t w0 = frag(nr + p.n_q + lr, k);
-                const bf16x8_t w1 = frag(nr + 2 * p.n_q + lr, k);
-                const bf16x8_t w2 = frag(nr + 3 * p.n_q + lr, k);
+                if (16 * (sg * (kScStage / 16) + sub) >= p.d) break;
+                const bf16x8_t x = frag(xs, k);
+                const bf16x8_t g = frag(gs, k);
+                const bf16x8_t w0 = frag(ws0, k);
+                const bf16x8_t w1 = frag(ws0 + p.n_q, k);
+                const bf16x8_t w2 = frag(ws0 + 2 * p.n_q, k);
                 if (norms) {
                     const u32x4 xv = __builtin_bit_cast(u32x4, x);
 #pragma unroll
@@ -522,40 +537,45 @@ __global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int n
         }
         if (norms) {  // lanes m and m + 32 hold the two halves of each step's k
             sq = swap32_sum(sq);
-            if (h == 0 && row_ok) pn[row] = sq;
+            if (h == 0 && row_ok) pn[u * nr + row] = sq;
         }
         // lane j, register r holds D[i][n = m], i = 8 (r / 4) + 4 h + r % 4
+        float* Pu = P + u * p.n_q * nr;
+        float* Qu = Q + u * p.n_q * nr;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = 8 * (r / 4) + 4 * h + r % 4;
             const int lqo = 32 * a + i;
             if (row_ok && lqo < p.n_q) {
-                P[lqo * nr + row] = totP[r];
-                Q[lqo * nr + row] = totQ[r];
+                Pu[lqo * nr + row] = totP[r];
+                Qu[lqo * nr + row] = totQ[r];
             }
         }
     }
     __syncthreads();
 
-    // ---- per read: softmax over its rows, ds, coefficients ------------------
-    float* A1 = p.ws_a1 + t * (int64_t)p.n_q * p.nh8;
-    float* A2 = p.ws_a2 + t * (int64_t)p.n_q * p.nh8;
-    float* A2T = p.ws_a2t + t * (int64_t)p.n_hist * p.nq8;
-    float* c3s = c3w + wave * nr;
-    for (int lq = wave; lq < p.n_q; lq += nwaves) {
+    // ---- per (token, read): softmax over the read's rows, ds, coefficients --
+    for (int job = wave; job < ntok * p.n_q; job += nwaves) {
+        const int tu = job / p.n_q, lq = job - tu * p.n_q;
+        const int64_t t = t0 + tu;
+        float* A1 = p.ws_a1 + t * (int64_t)p.n_q * p.nh8;
+        float* A2 = p.ws_a2 + t * (int64_t)p.n_q * p.nh8;
+        float* A2T = p.ws_a2t + t * (int64_t)p.n_hist * p.nq8;
+        const float* pnu = pn + tu * nr;
+        float* c3s = c3w + (wave * TT + tu) * nr;
         const int l = p.q_begin + lq;
         const int ns = l + 1;  // rows 0..l, one source each
-        const float* Pl = P + lq * nr;
-        const float* Ql = Q + lq * nr;
+        const float* Pl = P + (tu * p.n_q + lq) * nr;
+        const float* Ql = Q + (tu * p.n_q + lq) * nr;
         // lanes hold rows ln, ln + 64, ...; later rows (more than 64) are
         // recomputed in each pass
         float mx = -INFINITY;
         for (int i = ln; i < ns; i += 64)
-            mx = fmaxf(mx, fast_rsqrt(fmaf(pn[i], p.inv_d, p.eps)) * Pl[i]);
+            mx = fmaxf(mx, fast_rsqrt(fmaf(pnu[i], p.inv_d, p.eps)) * Pl[i]);
         mx = tg_max<64>(mx);
         float z = 0.f, zd = 0.f;  // sum of e and of e * a
         for (int i = ln; i < ns; i += 64) {
-            const float e = fast_exp2((fast_rsqrt(fmaf(pn[i], p.inv_d, p.eps)) * Pl[i] - mx) * kLog2e);
+            const float e = fast_exp2((fast_rsqrt(fmaf(pnu[i], p.inv_d, p.eps)) * Pl[i] - mx) * kLog2e);
             z += e;
             zd = fmaf(e, Ql[i], zd);
         }
@@ -566,13 +586,13 @@ __global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int n
         for (int i = ln; i < p.nh8; i += 64) {  // row-major A1 / A2: contiguous in i
             float c1 = 0.f, c2 = 0.f;
             if (i < ns) {
-                const float r = fast_rsqrt(fmaf(pn[i], p.inv_d, p.eps));
-                const float s = r * Pl[i];
-                const float alpha = fast_exp2((s - mx) * kLog2e) * inv_z;
+                const float r = fast_rsqrt(fmaf(pnu[i], p.inv_d, p.eps));
+                const float s2 = r * Pl[i];
+                const float alpha = fast_exp2((s2 - mx) * kLog2e) * inv_z;
                 const float ds = alpha * (Ql[i] - delta);
                 c1 = alpha;
                 c2 = ds * r;
-                c3s[i] += ds * r * r * s * p.inv_d;  // same lane for a row on every read of this wave
+                c3s[i] += ds * r * r * s2 * p.inv_d;  // same lane for a row on every job of this wave
             }
             A1[(int64_t)lq * p.nh8 + i] = c1;
             A2[(int64_t)lq * p.nh8 + i] = c2;
@@ -581,17 +601,20 @@ __global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int n
         if (ln == 0) p.ws_kappa[t * p.n_q + lq] = 0.f;  // Full: no partial sums
     }
     // the padding reads n_q .. nq8 - 1 of A2T are zero
-    for (int k = tid; k < p.n_hist * (p.nq8 - p.n_q); k += blockDim.x) {
-        const int i = k / (p.nq8 - p.n_q);
-        A2T[(int64_t)i * p.nq8 + p.n_q + k % (p.nq8 - p.n_q)] = 0.f;
+    const int npad = p.nq8 - p.n_q;
+    for (int k = tid; k < ntok * p.n_hist * npad; k += blockDim.x) {
+        const int tu = k / (p.n_hist * npad), rem = k - tu * p.n_hist * npad;
+        const int i = rem / npad;
+        p.ws_a2t[(t0 + tu) * (int64_t)p.n_hist * p.nq8 + (int64_t)i * p.nq8 + p.n_q + rem % npad] = 0.f;
     }
     __syncthreads();
     // C3 summed over the waves in a fixed order; rows no read sees get 0
-    for (int i = tid; i < p.n_blk; i += blockDim.x) {
+    for (int k = tid; k < ntok * p.n_blk; k += blockDim.x) {
+        const int tu = k / p.n_blk, i = k - tu * p.n_blk;
         float c3 = 0.f;
         if (i < nr)
-            for (int w = 0; w < nwaves; ++w) c3 += c3w[w * nr + i];
-        p.ws_c3[t * p.n_blk + i] = c3;
+            for (int w = 0; w < nwaves; ++w) c3 += c3w[(w * TT + tu) * nr + i];
+        p.ws_c3[(t0 + tu) * p.n_blk + i] = c3;
     }
 }
 
@@ -1010,30 +1033,38 @@ constexpr int kStreamR[9] = {0, 4, 4, 2, 2, 1, 1, 1, 1};
 // Which kernel forms the per-read coefficients of a call, and its dynamic LDS.
 struct ScoresPlan {
     enum Kind { NONE, MFMA, GROUP, STREAM } kind;
-    int nb, nwaves;       // MFMA: row tiles and waves per workgroup
+    int nb, nwaves, tt;   // MFMA: row tiles, (row, read) tile pairs, tokens per workgroup
     size_t lds;           // MFMA, STREAM
 };
 
 ScoresPlan plan_scores(const BwdParams& p) {
-    ScoresPlan s{ScoresPlan::NONE, 0, 0, 0};
+    ScoresPlan s{ScoresPlan::NONE, 0, 0, 0, 0};
     const int max_lds = device_max_lds();
     const int nb = scores_mfma_tiles(p);
     if (nb > 0) {
         const int nr = p.q_begin + p.n_q;
         // one wave per (row tile, read tile) pair whose reads see the tile
         const int na = (p.n_q + 31) / 32;
-        int nwaves = 0;
+        int npairs = 0;
         for (int b = 0; b < nb; ++b) {
             const int amin = 32 * b - p.q_begin - 31 > 0 ? (32 * b - p.q_begin) / 32 : 0;
-            nwaves += na - amin;
+            npairs += na - amin;
         }
-        const size_t lds = sizeof(float) * ((2 * (size_t)p.n_q * nr + nr + 8 * (size_t)nr + 3) & ~(size_t)3) +
-                           2 * (size_t)(nr + 4 * p.n_q) * (64 + 8);  // the stage's bf16 slices
-        if (lds <= (size_t)max_lds) {  // else one of the kernels below
+        auto lds_for = [&](int tt) {
+            return sizeof(float) * (size_t)sc_lds_floats(tt, p.n_q, nr) +
+                   2 * (size_t)(tt * (nr + p.n_q) + 3 * p.n_q) * kScRowLds;
+        };
+        // two tokens per workgroup when their pairs fit the eight waves and
+        // their slices the staging registers
+        int tt = 2 * npairs <= 8 && 2 * (nr + p.n_q) + 3 * p.n_q <= kScMaxSlices && p.T >= 2 &&
+                         lds_for(2) <= (size_t)max_lds ? 2 : 1;
+        if (tt == 1 && (nr + 4 * p.n_q > kScMaxSlices || lds_for(1) > (size_t)max_lds)) tt = 0;
+        if (tt > 0) {  // else one of the kernels below
             s.kind = ScoresPlan::MFMA;
             s.nb = nb;
-            s.nwaves = nwaves;
-            s.lds = lds;
+            s.nwaves = npairs;
+            s.tt = tt;
+            s.lds = lds_for(tt);
             return s;
         }
     }
@@ -1059,11 +1090,14 @@ hipError_t launch_scores(const BwdParams& p, const ScoresPlan& s, hipStream_t st
                            p.w, nw, hi, hi + nw, hi + 2 * nw);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        e = prepare_dynamic_lds((const void*)bwd_scores_full_kernel, s.lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_scores_full_kernel, dim3((unsigned)p.T), dim3(512), s.lds, stream,
-                           p, s.nb);
-        return hipGetLastError();
+        auto go = [&](auto kern, int tt) {
+            hipError_t e2 = prepare_dynamic_lds((const void*)kern, s.lds);
+            if (e2 != hipSuccess) return e2;
+            hipLaunchKernelGGL(kern, dim3((unsigned)((p.T + tt - 1) / tt)), dim3(512), s.lds, stream,
+                               p, s.nb, s.nwaves);
+            return hipGetLastError();
+        };
+        return s.tt == 2 ? go(bwd_scores_full_kernel<2>, 2) : go(bwd_scores_full_kernel<1>, 1);
     }
     if (s.kind == ScoresPlan::GROUP) return launch_bwd_scores_group(p, stream);
     if (s.kind != ScoresPlan::STREAM) return hipErrorInvalidValue;
