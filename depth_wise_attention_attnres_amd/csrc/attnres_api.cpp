@@ -535,8 +535,9 @@ int bwd_impl(const char* fn, bool use_scratch, attnres_variant variant, int64_t 
     }
     if (!attnres::bwd_fits(p))
         return fail(ATTNRES_ERR_UNSUPPORTED,
-                    "%s: the per-read coefficients of %" PRId64 " sources do not fit one workgroup's LDS",
-                    fn, L.nx);
+                    "%s: the per-read coefficients of %" PRId64 " sources (%" PRId64
+                    " reads) do not fit one workgroup's LDS or one chunk's address range",
+                    fn, L.nx, n_q);
     return hip_status(fn, attnres::launch_bwd(p, (int)L.n_chunks, (int)L.n_dw_groups, stream));
 }
 

@@ -628,9 +628,14 @@ __global__ __launch_bounds__(64) void bwd_dhist_kernel(BwdParams p) {
     const int ln = threadIdx.x;
     // slices of one token are neighbours in dispatch order, so the token's
     // coefficients are fetched from HBM once and then served by L2
+    // the slices of one token share an XCD (and its L2): the token's
+    // coefficients are fetched from HBM once, then served by that L2
     const int slices = (p.d + kSlice - 1) / kSlice;
-    const int64_t t = blockIdx.x / slices;
-    const int e0 = (int)(blockIdx.x % slices) * kSlice + 4 * ln;  // this lane's four columns
+    int64_t t;
+    int slice;
+    xcd_group(blockIdx.x, slices, t, slice);
+    if (t >= p.T) return;  // whole workgroups of one wave
+    const int e0 = slice * kSlice + 4 * ln;  // this lane's four columns
     const bool valid = e0 < p.d;                   // d % 8 == 0: all four or none
     const int S = p.S;
     const int q_end = p.q_begin + p.n_q;
@@ -864,9 +869,16 @@ __global__ __launch_bounds__(64) void bwd_dw_part_kernel(BwdParams p) {
     constexpr int QT = 32;
     const int ln = threadIdx.x;
     const int h = ln >> 5, m = ln & 31;
+    // the column slices of one chunk share an XCD, so the chunk's coefficients
+    // come from HBM once and are then served by that L2
     const int slices = (p.d + kDwSlice - 1) / kDwSlice;
-    const int c0 = (int)(blockIdx.x % slices) * kDwSlice;
-    const int chunk = (int)(blockIdx.x / slices);
+    int64_t chunk64;
+    int slice;
+    xcd_group(blockIdx.x, slices, chunk64, slice);
+    const int n_chunks_all = (int)((p.T + kChunkTokens - 1) / kChunkTokens);
+    if (chunk64 >= n_chunks_all) return;  // whole workgroups of one wave
+    const int chunk = (int)chunk64;
+    const int c0 = slice * kDwSlice;
     const bool valid = c0 + 4 * m < p.d;  // d % 8 == 0: all four columns or none
     const int64_t row_elems = p.T * (int64_t)p.d;
     const int64_t t_lo = (int64_t)chunk * kChunkTokens;
@@ -877,36 +889,43 @@ __global__ __launch_bounds__(64) void bwd_dw_part_kernel(BwdParams p) {
     const int64_t a2t_tok = (int64_t)p.n_hist * p.nq8;  // floats per token of A2T
     // fixed lane offsets inside a step's two-token window
     const uint32_t x_off = (uint32_t)((h * p.d + c0 + 4 * m) * sizeof(TI));
-    const uint64_t x_bytes = 2 * (uint64_t)p.d * sizeof(TI);
 
-    for (int qt0 = 0; qt0 < p.n_q; qt0 += QT) {
-        const int nqt = p.n_q - qt0 < QT ? p.n_q - qt0 : QT;
-        const int n_rows = p.q_begin + qt0 + nqt;  // rows 0 .. last read of the tile
+    // The chunk's (token pair, row) steps go in one pass for two tiles of 32
+    // reads at once (tile 0 stops at the last row its reads see), so the rows
+    // are read once per 64 reads.  One buffer descriptor spans the chunk's 32
+    // tokens of a row and one the chunk's coefficients; a step only moves the
+    // lane offsets.
+    const rsrc_t rc = make_rsrc(a2t_chunk, (uint64_t)n_tok * a2t_tok * 4);
+    for (int qt0 = 0; qt0 < p.n_q; qt0 += 2 * QT) {
+        const int nq0 = p.n_q - qt0 < QT ? p.n_q - qt0 : QT;      // reads of tile 0
+        const int nq1 = p.n_q - qt0 - QT < QT ? p.n_q - qt0 - QT : QT;  // of tile 1 (may be <= 0)
+        const int n_rows0 = p.q_begin + qt0 + nq0;                // rows tile 0 sees
+        const int n_rows = nq1 > 0 ? n_rows0 + nq1 : n_rows0;    // rows either tile sees
         const int n_steps = n_rows * n_pairs;
-        // coefficient of read qt0 + m; reads past n_q are zero in A2T, columns
-        // past nq8 would belong to the next row
-        const bool coef_ok = qt0 + m < p.nq8;
-        const uint32_t c_off = (uint32_t)((h * a2t_tok + (coef_ok ? qt0 + m : 0)) * 4);
-        f32x16 acc[4];
+        // coefficients of reads qt0 + m and qt0 + 32 + m (zero in A2T past n_q;
+        // columns past nq8 would belong to the next row)
+        const bool ok0 = qt0 + m < p.nq8, ok1 = nq1 > 0 && qt0 + QT + m < p.nq8;
+        f32x16 acc0[4], acc1[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[e][r] = 0.f;
+            for (int r = 0; r < 16; ++r) acc0[e][r] = acc1[e][r] = 0.f;
 
         Quad<TI> xr[PF];
-        float cr[PF];
+        float cr0[PF], cr1[PF];
         int ir = 0, iu = 0;  // (row, token pair) of the next step to issue
+        rsrc_t rx = make_rsrc(hist_chunk, (uint64_t)n_tok * p.d * sizeof(TI));
         auto issue = [&](int u) {
-            const int t0 = 2 * iu;
-            const bool live = t0 + h < n_tok && valid;
-            const rsrc_t rx = make_rsrc(hist_chunk + ir * row_elems + (int64_t)t0 * p.d, x_bytes);
-            xr[u].load(rx, live ? x_off : kOOB);
-            const rsrc_t rc = make_rsrc(a2t_chunk + t0 * a2t_tok + (int64_t)ir * p.nq8,
-                                        (uint64_t)(a2t_tok + p.nq8) * 4);
-            cr[u] = load_f32(rc, (t0 + h < n_tok && coef_ok) ? c_off : kOOB);
+            const int tk = 2 * iu + h;  // this lane's token in the chunk
+            const bool live = tk < n_tok;
+            xr[u].load(rx, live && valid ? x_off + (uint32_t)(2 * iu * p.d * sizeof(TI)) : kOOB);
+            const uint32_t cb = (uint32_t)(((int64_t)tk * a2t_tok + (int64_t)ir * p.nq8 + qt0 + m) * 4);
+            cr0[u] = load_f32(rc, live && ok0 ? cb : kOOB);
+            cr1[u] = load_f32(rc, live && ok1 ? cb + 4 * QT : kOOB);
             if (++iu == n_pairs) {
                 iu = 0;
                 ++ir;
+                rx = make_rsrc(hist_chunk + (int64_t)ir * row_elems, (uint64_t)n_tok * p.d * sizeof(TI));
             }
         };
 #pragma unroll
@@ -919,25 +938,33 @@ __global__ __launch_bounds__(64) void bwd_dw_part_kernel(BwdParams p) {
                 if (st >= n_steps) break;
                 float v[4];
                 xr[u].to_float(v);
-                const float c = cr[u];
+                const float c0v = cr0[u], c1v = cr1[u];
                 if (st + PF < n_steps) issue(u);
+                if (st < n_rows0 * n_pairs) {  // wave-uniform: rows tile 0 sees
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc[e] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[e], c, acc[e], 0, 0, 0);
-            }
-        }
-        if (m < nqt) {
-            float* part = p.ws_dwpart + ((int64_t)chunk * p.n_q + qt0 + m) * p.d;
+                    for (int e = 0; e < 4; ++e)
+                        acc0[e] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[e], c0v, acc0[e], 0, 0, 0);
+                }
+                if (nq1 > 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = 8 * (r / 4) + 4 * h + r % 4;
-                const int col = c0 + 4 * i;
-                if (col < p.d) {
-                    const float o[4] = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-                    *reinterpret_cast<f32x4*>(part + col) = {o[0], o[1], o[2], o[3]};
+                    for (int e = 0; e < 4; ++e)
+                        acc1[e] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[e], c1v, acc1[e], 0, 0, 0);
                 }
             }
         }
+        auto store_tile = [&](const f32x16 (&acc)[4], int q0, int nq) {
+            if (m < nq) {
+                float* part = p.ws_dwpart + ((int64_t)chunk * p.n_q + q0 + m) * p.d;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = 8 * (r / 4) + 4 * h + r % 4;
+                    const int col = c0 + 4 * i;
+                    if (col < p.d) *reinterpret_cast<f32x4*>(part + col) = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+                }
+            }
+        };
+        store_tile(acc0, qt0, nq0);
+        if (nq1 > 0) store_tile(acc1, qt0 + QT, nq1);
     }
 }
 
@@ -1127,18 +1154,21 @@ hipError_t launch_scores(const BwdParams& p, const ScoresPlan& s, hipStream_t st
 
 template <typename TI, typename TG, typename TO>
 hipError_t launch_rest(const BwdParams& p, int n_chunks, int groups, hipStream_t stream) {
+    // XCD-aware numbering (xcd_group): 8 slices ceil(T / 8) workgroups
     const unsigned slices = (unsigned)((p.d + kSlice - 1) / kSlice);
+    const unsigned dh_blocks = (unsigned)((p.T + kNumXcd - 1) / kNumXcd) * kNumXcd * slices;
     if (p.n_hist <= 8)
-        hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 8, 4>), dim3((unsigned)(p.T * slices)), dim3(64),
+        hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 8, 4>), dim3(dh_blocks), dim3(64),
                            0, stream, p);
     else  // 16-row tiles: 125 VGPRs, four waves per SIMD (32-row tiles: 192, two
           // waves, 1 ms slower at 49 rows / d = 1024 although they stream fewer reads)
-        hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 16, 4>), dim3((unsigned)(p.T * slices)),
+        hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 16, 4>), dim3(dh_blocks),
                            dim3(64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned dw_slices = (unsigned)((p.d + kDwSlice - 1) / kDwSlice);
-    hipLaunchKernelGGL((bwd_dw_part_kernel<TI, 8>), dim3(dw_slices * (unsigned)n_chunks), dim3(64), 0,
+    const unsigned dw_blocks = (unsigned)((n_chunks + kNumXcd - 1) / kNumXcd) * kNumXcd * dw_slices;
+    hipLaunchKernelGGL((bwd_dw_part_kernel<TI, 8>), dim3(dw_blocks), dim3(64), 0,
                        stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1168,7 +1198,12 @@ hipError_t run_bwd(const BwdParams& p, int n_chunks, int groups, hipStream_t str
 
 }  // namespace
 
-bool bwd_fits(const BwdParams& p) { return plan_scores(p).kind != ScoresPlan::NONE; }
+bool bwd_fits(const BwdParams& p) {
+    // bwd_dw_part addresses a chunk's coefficients (32 tokens of A2T) from one
+    // buffer descriptor, whose range is kOOB bytes
+    if ((int64_t)kChunkTokens * p.n_hist * p.nq8 * 4 >= (int64_t)kOOB) return false;
+    return plan_scores(p).kind != ScoresPlan::NONE;
+}
 
 hipError_t launch_bwd(const BwdParams& p, int n_chunks, int groups, hipStream_t stream) {
     if (p.hist_dt == ATTNRES_BF16)

@@ -277,6 +277,20 @@ __device__ __forceinline__ void wave_totals(const float (&v)[KV], float (&tot)[K
     if constexpr (REM > 8) wave_totals<BASE + 8, KV>(v, tot, lane);
 }
 
+// XCD-aware workgroup numbering.  The dispatcher hands workgroups to the
+// eight XCDs in turn (workgroup w runs on XCD w % 8), and each XCD has its own
+// L2.  For work split into groups of `members` workgroups that read the same
+// data, number the groups so that all members of a group share an XCD:
+// group = 8 (w / (8 members)) + w % 8, member = (w / 8) % members.  A grid of
+// 8 members ceil(groups / 8) workgroups covers every group; members of groups
+// past the last one return.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ void xcd_group(int64_t w, int members, int64_t& group, int& member) {
+    const int64_t q = w / kNumXcd;
+    member = (int)(q % members);
+    group = (q / members) * kNumXcd + w % kNumXcd;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }

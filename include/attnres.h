@@ -296,8 +296,9 @@ int attnres_block_phase2_q(const void* v, attnres_dtype v_dtype, int64_t T, int6
  *   workspace          device scratch of at least attnres_bwd_workspace_bytes()
  *                      bytes, 256-byte aligned; contents on entry are ignored
  * The per-read coefficients of a token are formed in one workgroup's LDS;
- * when a call's sources do not fit (Full with more than about 1600 rows) it
- * returns ATTNRES_ERR_UNSUPPORTED.
+ * when a call's sources do not fit (Full with more than about 1600 rows), or
+ * when n_hist * n_q exceeds about 8 million (the coefficients of 32 tokens
+ * then pass 1 GiB), it returns ATTNRES_ERR_UNSUPPORTED.
  */
 int attnres_bwd(attnres_variant variant, int64_t S, const void* hist,
                 attnres_dtype hist_dtype, int64_t n_hist, int64_t T, int64_t d,
