@@ -527,6 +527,7 @@ int bwd_impl(const char* fn, bool use_scratch, attnres_variant variant, int64_t 
     p.ws_kappa = reinterpret_cast<float*>(ws + L.off_kappa);
     p.ws_dwpart = reinterpret_cast<float*>(ws + L.off_dwpart);
     p.ws_dwstage = reinterpret_cast<float*>(ws + L.off_dwstage);
+    p.ws_wsplit2 = reinterpret_cast<uint16_t*>(ws + L.off_wsplit2);
     if (n_q == 0) {
         // no read: every history row gets a zero gradient (nothing to add)
         if (accumulate) return ok();

@@ -24,12 +24,16 @@
 //               across the wave, renormalises each read's softmax over its own
 //               scores (a single source gets alpha = 1 exactly), forms ds, and
 //               writes A1, A2 (row-major and transposed), C3 and kappa.
-//   bwd_dhist   one wave per (token, 256-column slice of d): accumulates
-//               dv for row tiles in registers while the reads' dout and w
-//               rows stream through a prefetch ring (coefficients are uniform
-//               across the wave, so they come through the scalar cache),
-//               then adds the source-coupling terms with a forward (prefix)
-//               and a backward (suffix) pass over each block, and stores dhist.
+//   bwd_dhist   fp32 history gradients (and calls the matrix-core kernel of
+//               bwd_dhist_mfma.hip does not take): one wave per (token,
+//               256-column slice of d): accumulates dv for row tiles in
+//               registers while the reads' dout and w rows stream through a
+//               prefetch ring (coefficients are uniform across the wave, so
+//               they come through the scalar cache), then adds the
+//               source-coupling terms with a forward (prefix) and a backward
+//               (suffix) pass over each block, and stores dhist.  bf16
+//               gradients go to bwd_dhist_mfma.hip, which forms the same sums
+//               as one small matrix product per token.
 //   bwd_dw_part one wave per (128-column slice, chunk of 32 tokens):
 //               per-chunk partial dw for tiles of 32 reads on the matrix cores
 //               (fp32 MFMA), the chunk's (token, row) pairs streamed through a
@@ -1032,6 +1036,7 @@ BwdLayout bwd_layout(int64_t S, int64_t n_hist, int64_t T, int64_t d, int64_t n_
     L.off_wsplit = take((3 * n_q * d + 1) / 2);  // bf16
     L.n_dw_groups = L.n_chunks < 16 ? L.n_chunks : 16;
     L.off_dwstage = take(L.n_dw_groups * n_q * d);
+    L.off_wsplit2 = take((bwd_wsplit2_elems(n_q, d) + 1) / 2);  // bf16
     L.bytes = off;
     return L;
 }
@@ -1157,14 +1162,17 @@ hipError_t launch_rest(const BwdParams& p, int n_chunks, int groups, hipStream_t
     // XCD-aware numbering (xcd_group): 8 slices ceil(T / 8) workgroups
     const unsigned slices = (unsigned)((p.d + kSlice - 1) / kSlice);
     const unsigned dh_blocks = (unsigned)((p.T + kNumXcd - 1) / kNumXcd) * kNumXcd * slices;
-    if (p.n_hist <= 8)
+    hipError_t e = hipSuccess;
+    if (std::is_same<TO, bf16_t>::value && bwd_dhist_mfma_applies(p))  // bf16 gradients
+        e = launch_bwd_dhist_mfma(p, stream);
+    else if (p.n_hist <= 8)
         hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 8, 4>), dim3(dh_blocks), dim3(64),
                            0, stream, p);
     else  // 16-row tiles: 125 VGPRs, four waves per SIMD (32-row tiles: 192, two
           // waves, 1 ms slower at 49 rows / d = 1024 although they stream fewer reads)
         hipLaunchKernelGGL((bwd_dhist_kernel<TI, TG, TO, 16, 4>), dim3(dh_blocks),
                            dim3(64), 0, stream, p);
-    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned dw_slices = (unsigned)((p.d + kDwSlice - 1) / kDwSlice);
     const unsigned dw_blocks = (unsigned)((n_chunks + kNumXcd - 1) / kNumXcd) * kNumXcd * dw_slices;

@@ -1,0 +1,331 @@
+// bwd_dhist_mfma.hip -- the backward's history gradient on the matrix cores.
+//
+// For one token t the history gradient (the derivative of the read of
+// "DepthBench reading notes" sec. 2.3, block reading of sec. 2.5; the
+// coefficients are formed by the coefficient kernels of bwd.hip) is
+//   dv_i = sum_l A1[l][i] g_l + sum_l A2[l][i] w_l - sum_m coef(i, m) v_m,
+// with coef(i, m) = C3[c] + K(max(i, m)) for rows i, m of one block c (v_0 a
+// block of its own; K(m) the kappa of the reads whose partial sum holds row
+// m, summed) and 0 across blocks.  Columns k of d are independent, so per
+// token this is one small matrix product over K = reads (g), reads (w),
+// rows (v):  D[k][i] = sum over K of Aop[k][K] B[K][i],  B = A1 ++ A2 ++ -coef.
+// It runs on v_mfma_f32_32x32x16_bf16.  The history rows and upstream
+// gradients are bf16 already; the fp32 coefficients enter as bf16 hi + lo
+// and w as bf16 hi + mid, each exact to about 2^-17 relative (w's mid part
+// meets A2's hi part only).  That is far below the bf16 rounding of the
+// result, which is why only bf16 gradients take this kernel; fp32 gradients
+// keep the fp32 vector kernel of bwd.hip.
+//
+// One workgroup of eight waves per token.  The token's B operands are split
+// and laid out as matrix fragments in LDS once.  The A operands are rows of
+// dout, w and the history, read 16 rows (one 16-step) at a time: the waves
+// load the step's rows for 512 columns of d together, one 1 KB row segment
+// per load (a load that spans several rows, each in its own page, stalls the
+// address unit), into an LDS tile; after a barrier every lane reads back the
+// column it needs for its MFMA operand (a transposed read), and a second
+// barrier frees the tile.  Wave w owns columns 64 w .. 64 w + 63 of each
+// 512-column pass: two 32-column output tiles.  Loads run two steps ahead.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace attnres {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kDmWaves = 8;
+constexpr int kDmMaxNT = 3;            // row tiles of 32 (at most 96 history rows)
+constexpr int kDmMaxLds = 128 * 1024;  // LDS bytes a workgroup may use
+constexpr int kDmRing = 2;             // 16-steps in flight per wave
+constexpr int kDmCols = 64 * kDmWaves;  // columns of d per pass of a workgroup
+constexpr int kDmRow = kDmCols + 8;     // bf16 per row of the LDS step tile (8 padding)
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16x2(x, 0.f) & 0xffffu; }
+
+// x = hi + lo + r with hi, lo bf16 (round to nearest even) and |r| <= 2^-17 |x|
+__device__ __forceinline__ void split2(float x, uint32_t& hi, uint32_t& lo) {
+    hi = bf16_bits(x);
+    lo = bf16_bits(x - __uint_as_float(hi << 16));
+}
+
+__device__ __forceinline__ int block_of_row(int j, int S) { return j == 0 ? 0 : (j - 1) / S + 1; }
+
+// w split into two bf16 parts, row-major: wsp[0] = hi, wsp[1] = mid
+__global__ __launch_bounds__(256) void split_w2_kernel(const float* w, int64_t n, uint16_t* wsp) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    uint32_t hi, mid;
+    split2(w[i], hi, mid);
+    wsp[i] = (uint16_t)hi;
+    wsp[n + i] = (uint16_t)mid;
+}
+
+template <int NT, int RING>
+__global__ __launch_bounds__(512) void bwd_dhist_mfma_kernel(BwdParams p, int kq, int kh) {
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), ln = tid & 63;
+    const int h = ln >> 5, m = ln & 31;
+    const int64_t t = blockIdx.x;
+    const int nks = 2 * kq + kh;  // 16-steps: g, then w, then v
+    const int S = p.S;
+    const int q_end = p.q_begin + p.n_q;
+
+    extern __shared__ float lds[];
+    u32x4* frag = reinterpret_cast<u32x4*>(lds);                   // [nks][NT][hi, lo][64 lanes]
+    float* cf = lds + (size_t)nks * NT * 2 * 64 * 4;               // [n_hist] C3[block] + K(row)
+    const int cf_floats = (p.n_hist + 3) & ~3;                     // then the step tile
+
+    // ---- per-row coupling coefficient C3[c] + K(j) --------------------------
+    const float* C3 = p.ws_c3 + t * p.n_blk;
+    const float* kap = p.ws_kappa + t * p.n_q;
+    for (int j = tid; j < p.n_hist; j += blockDim.x) {
+        const int c = block_of_row(j, S);
+        float K = 0.f;
+        if (c > 0) {
+            const int Lc = c * S - 1 < q_end - 1 ? c * S - 1 : q_end - 1;
+            for (int l = j > p.q_begin ? j : p.q_begin; l <= Lc; ++l) K += kap[l - p.q_begin];
+        }
+        cf[j] = C3[c] + K;
+    }
+    __syncthreads();
+
+    // ---- B operands: lane (hh, i) of fragment (ks, nt) holds K = 8 hh + j ---
+    const float* A1 = p.ws_a1 + t * (int64_t)p.n_q * p.nh8;
+    const float* A2 = p.ws_a2 + t * (int64_t)p.n_q * p.nh8;
+    for (int e = tid; e < nks * NT * 64; e += blockDim.x) {
+        const int L = e & 63, fn = e >> 6;
+        const int nt = fn % NT, ks = fn / NT;
+        const int hh = L >> 5, i = 32 * nt + (L & 31);
+        float v[8];
+        if (ks < 2 * kq) {
+            const float* A = ks < kq ? A1 : A2;
+            const int k0 = 16 * (ks < kq ? ks : ks - kq);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int lq = k0 + 8 * hh + j;
+                v[j] = (lq < p.n_q && i < p.n_hist) ? A[(int64_t)lq * p.nh8 + i] : 0.f;
+            }
+        } else {
+            const int r0 = 16 * (ks - 2 * kq);
+            const int ci = i < p.n_hist ? block_of_row(i, S) : -1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = r0 + 8 * hh + j;
+                v[j] = (r < p.n_hist && ci >= 0 && block_of_row(r, S) == ci) ? -cf[r > i ? r : i]
+                                                                            : 0.f;
+            }
+        }
+        u32x4 hi4, lo4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t h0, l0, h1, l1;
+            split2(v[2 * q], h0, l0);
+            split2(v[2 * q + 1], h1, l1);
+            hi4[q] = h0 | (h1 << 16);
+            lo4[q] = l0 | (l1 << 16);
+        }
+        frag[(fn * 2 + 0) * 64 + L] = hi4;
+        frag[(fn * 2 + 1) * 64 + L] = lo4;
+    }
+    __syncthreads();
+
+    // ---- A operands -----------------------------------------------------------
+    // Wave w loads rows 2 w and 2 w + 1 of each 16-step across the pass; lane
+    // (h, m) of output tile kk then takes column 64 w + 32 kk + m of the
+    // step's rows 8 h .. 8 h + 7 (K = 8 h + j is row 8 h + j).
+    const int64_t row_elems = p.T * (int64_t)p.d;
+    const bf16_t* dout_t = static_cast<const bf16_t*>(p.dout) + t * p.d;
+    const bf16_t* hist_t = static_cast<const bf16_t*>(p.hist) + t * p.d;
+    const bf16_t* wsp = reinterpret_cast<const bf16_t*>(p.ws_wsplit2);  // [hi, mid][n_q][d]
+    // the step tile: 16 rows x kDmCols bf16, rows padded to kDmRow (the two
+    // half-waves read rows eight apart, 32 banks apart)
+    uint16_t* tb = reinterpret_cast<uint16_t*>(cf + cf_floats);
+
+    struct Slot {
+        u32x4 x, y;  // this wave's two rows of the step
+    };
+    // A row past the operand's last row, or a step past the end, gets an
+    // empty range (zeros); columns past d read zeros from the row's range.
+    auto gather = [&](const bf16_t* base, int64_t stride, int nrows, int r0, uint32_t coff, Slot& sl) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int row = r0 + 2 * wave + k;
+            const bool ok = row < nrows;
+            const rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<bf16_t*>(base + (ok ? row : 0) * stride), (short)0, ok ? 2 * p.d : 0,
+                (int)kRsrcWord3);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr, coff, 0, 0);
+            if (k == 0) sl.x = v; else sl.y = v;
+        }
+    };
+    auto bfrag = [&](int ks, int nt, int part) {
+        return __builtin_bit_cast(bf16x8_t, frag[((ks * NT + nt) * 2 + part) * 64 + ln]);
+    };
+
+    // Steps per pass: g (kq), w hi (kq), w mid (kq), v (kh).  A ring of RING
+    // register slots runs over all passes: step sigma + RING is issued as soon
+    // as step sigma has gone to LDS.
+    const int n_pass = (p.d + kDmCols - 1) / kDmCols;
+    const int nsteps = 3 * kq + kh;
+    const int total = n_pass * nsteps;
+    const int64_t wpart = (int64_t)p.n_q * p.d;
+    int i_pass = 0, i_st = 0;  // the next step to issue
+    auto issue = [&](Slot& sl) {  // selects only: the loads share one block
+        const bool isg = i_st < kq, isw = !isg && i_st < 3 * kq, mid = i_st >= 2 * kq;
+        const bf16_t* base = isg ? dout_t : (isw ? wsp + (mid ? wpart : 0) : hist_t);
+        const int64_t stride = isw ? (int64_t)p.d : row_elems;
+        int nrows = isg || isw ? p.n_q : p.n_hist;
+        nrows = i_pass < n_pass ? nrows : 0;  // past the last pass
+        const int r0 = 16 * (i_st - (isg ? 0 : (isw ? (mid ? 2 * kq : kq) : 3 * kq)));
+        gather(base, stride, nrows, r0, (uint32_t)(i_pass * kDmCols * 2 + 16 * ln), sl);
+        const bool wrap = i_st == nsteps - 1;
+        i_st = wrap ? 0 : i_st + 1;
+        i_pass += wrap ? 1 : 0;
+    };
+
+    f32x16 acc[2][NT];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[kk][nt][r] = 0.f;
+    Slot ring[RING];
+#pragma unroll
+    for (int u = 0; u < RING; ++u) issue(ring[u]);
+    bf16_t* dh_t = static_cast<bf16_t*>(p.dhist) + t * p.d;
+    int c_pass = 0, c_st = 0;  // the step being consumed
+    // whole rounds of RING steps; steps past the last one carry zeros
+    for (int s0 = 0; s0 < total; s0 += RING) {
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+            *reinterpret_cast<u32x4*>(tb + (2 * wave) * kDmRow + 8 * ln) = ring[u].x;
+            *reinterpret_cast<u32x4*>(tb + (2 * wave + 1) * kDmRow + 8 * ln) = ring[u].y;
+            issue(ring[u]);
+            __syncthreads();  // the step's 16 rows are in LDS
+            bf16x8_t a[2];
+            {
+                u32x4 t0, t1;
+                const uint16_t* tc = tb + 64 * wave + m;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = 8 * h + 2 * q;  // rows r, r + 1 (elements 2 q, 2 q + 1)
+                    t0[q] = (uint32_t)tc[r * kDmRow] | ((uint32_t)tc[(r + 1) * kDmRow] << 16);
+                    t1[q] = (uint32_t)tc[r * kDmRow + 32] | ((uint32_t)tc[(r + 1) * kDmRow + 32] << 16);
+                }
+                // the operands exist here (an empty statement the compiler
+                // cannot move them across): every wave has read the tile when
+                // the next barrier lets the next step write it
+                asm volatile("" : "+v"(t0), "+v"(t1));
+                a[0] = __builtin_bit_cast(bf16x8_t, t0);
+                a[1] = __builtin_bit_cast(bf16x8_t, t1);
+            }
+            __syncthreads();
+            // B fragments: A1 (g steps), A2 (w steps; the mid part of w only
+            // against A2 hi), -coef (v steps)
+            int ksb;
+            bool two = true;
+            if (c_st < kq) {
+                ksb = c_st;
+            } else if (c_st < 3 * kq) {
+                const bool mid = c_st >= 2 * kq;
+                ksb = c_st - (mid ? kq : 0);
+                two = !mid;
+            } else {
+                ksb = c_st - kq;
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const bf16x8_t b0 = bfrag(ksb, nt, 0);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    acc[kk][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b0, acc[kk][nt], 0, 0, 0);
+                if (two) {
+                    const bf16x8_t b1 = bfrag(ksb, nt, 1);
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+                        acc[kk][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b1, acc[kk][nt], 0, 0, 0);
+                }
+            }
+            if (c_st == nsteps - 1) {
+                // lane (h, m), register r of tile kk: column c_pass kDmCols + 64 w +
+                // 32 kk + 8 (r / 4) + 4 h + r % 4, row 32 nt + m
+                const int cb = c_pass * kDmCols + 64 * wave;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int i = 32 * nt + m;
+                    if (i < p.n_hist) {
+                        bf16_t* rowp = dh_t + i * row_elems;
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                const int c0 = cb + 32 * kk + 8 * g + 4 * h;
+                                if (c0 < p.d)
+                                    *reinterpret_cast<uint2*>(rowp + c0) = make_uint2(
+                                        pack_bf16x2(acc[kk][nt][4 * g], acc[kk][nt][4 * g + 1]),
+                                        pack_bf16x2(acc[kk][nt][4 * g + 2], acc[kk][nt][4 * g + 3]));
+                            }
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[kk][nt][r] = 0.f;
+                }
+                c_st = 0;
+                ++c_pass;
+            } else {
+                ++c_st;
+            }
+        }
+    }
+}
+
+int dm_nt(const BwdParams& p) { return (p.n_hist + 31) / 32; }
+
+size_t dm_lds(const BwdParams& p) {
+    const int kq = (p.n_q + 15) / 16, kh = (p.n_hist + 15) / 16;
+    return (size_t)(2 * kq + kh) * dm_nt(p) * 2 * 64 * 16 + (size_t)((p.n_hist + 3) & ~3) * 4 +
+           (size_t)16 * kDmRow * 2;
+}
+
+}  // namespace
+
+int64_t bwd_wsplit2_elems(int64_t n_q, int64_t d) { return 2 * n_q * d; }
+
+bool bwd_dhist_mfma_applies(const BwdParams& p) {
+    if (p.hist_dt != ATTNRES_BF16 || p.dout_dt != ATTNRES_BF16 || p.dhist_dt != ATTNRES_BF16)
+        return false;
+    if (p.accumulate || p.n_q < 1 || dm_nt(p) > kDmMaxNT) return false;
+    const size_t lds = dm_lds(p);
+    return lds <= (size_t)kDmMaxLds && lds <= (size_t)device_max_lds();
+}
+
+hipError_t launch_bwd_dhist_mfma(const BwdParams& p, hipStream_t stream) {
+    const int kq = (p.n_q + 15) / 16, kh = (p.n_hist + 15) / 16;
+    const int64_t nw = (int64_t)p.n_q * p.d;
+    hipLaunchKernelGGL(split_w2_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream, p.w,
+                       nw, p.ws_wsplit2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = dm_lds(p);
+    const void* kern;
+    switch (dm_nt(p)) {
+        case 1: kern = reinterpret_cast<const void*>(&bwd_dhist_mfma_kernel<1, kDmRing>); break;
+        case 2: kern = reinterpret_cast<const void*>(&bwd_dhist_mfma_kernel<2, kDmRing>); break;
+        default: kern = reinterpret_cast<const void*>(&bwd_dhist_mfma_kernel<3, kDmRing>); break;
+    }
+    e = prepare_dynamic_lds(kern, (int)lds);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)p.T), block(64 * kDmWaves);
+    switch (dm_nt(p)) {
+        case 1: hipLaunchKernelGGL((bwd_dhist_mfma_kernel<1, kDmRing>), grid, block, lds, stream, p, kq, kh); break;
+        case 2: hipLaunchKernelGGL((bwd_dhist_mfma_kernel<2, kDmRing>), grid, block, lds, stream, p, kq, kh); break;
+        default: hipLaunchKernelGGL((bwd_dhist_mfma_kernel<3, kDmRing>), grid, block, lds, stream, p, kq, kh); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace attnres

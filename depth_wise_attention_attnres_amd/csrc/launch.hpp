@@ -72,7 +72,8 @@ struct BwdLayout {
     int64_t nx;        // most sources a read can see
     int64_t n_chunks;  // token chunks of the dw partial sums
     int64_t n_dw_groups;  // chunk groups of the first dw reduction stage
-    int64_t off_a1, off_a2, off_a2t, off_c3, off_kappa, off_dwpart, off_wsplit, off_dwstage;
+    int64_t off_a1, off_a2, off_a2t, off_c3, off_kappa, off_dwpart, off_wsplit, off_dwstage,
+        off_wsplit2;
     int64_t bytes;
 };
 BwdLayout bwd_layout(int64_t S, int64_t n_hist, int64_t T, int64_t d, int64_t n_q);
@@ -97,10 +98,17 @@ struct BwdParams {
     float* ws_dwpart;   // [n_chunks][n_q][d]
     float* ws_dwstage;  // [n_dw_groups][n_q][d]
     uint16_t* ws_wsplit;  // [3][n_q][d] bf16: w = hi + mid + lo (matrix-core scores)
+    uint16_t* ws_wsplit2;  // [2][n_q][d] bf16: w = hi + mid (matrix-core history gradient)
 };
 hipError_t launch_bwd(const BwdParams& p, int n_chunks, int n_dw_groups, hipStream_t stream);
 // whether some coefficient kernel takes the call (its LDS fits the device)
 bool bwd_fits(const BwdParams& p);
+// the history gradient on the matrix cores (bwd_dhist_mfma.hip): bf16 history,
+// upstream gradient and history gradient; whether the call qualifies, the
+// launch, and the size of its w split (bf16 elements)
+bool bwd_dhist_mfma_applies(const BwdParams& p);
+hipError_t launch_bwd_dhist_mfma(const BwdParams& p, hipStream_t stream);
+int64_t bwd_wsplit2_elems(int64_t n_q, int64_t d);
 // Size of the static device array that serves as the backward's workspace for
 // callers that cannot allocate, and its address on the current device (taken
 // once per device; bwd_scratch.hip).
