@@ -1174,11 +1174,15 @@ hipError_t launch_rest(const BwdParams& p, int n_chunks, int groups, hipStream_t
                            dim3(64), 0, stream, p);
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned dw_slices = (unsigned)((p.d + kDwSlice - 1) / kDwSlice);
-    const unsigned dw_blocks = (unsigned)((n_chunks + kNumXcd - 1) / kNumXcd) * kNumXcd * dw_slices;
-    hipLaunchKernelGGL((bwd_dw_part_kernel<TI, 8>), dim3(dw_blocks), dim3(64), 0,
-                       stream, p);
-    e = hipGetLastError();
+    if (bwd_dw_mfma_applies(p)) {  // bf16 history, at most 64 reads
+        e = launch_bwd_dw_mfma(p, kChunkTokens, stream);
+    } else {
+        const unsigned dw_slices = (unsigned)((p.d + kDwSlice - 1) / kDwSlice);
+        const unsigned dw_blocks = (unsigned)((n_chunks + kNumXcd - 1) / kNumXcd) * kNumXcd * dw_slices;
+        hipLaunchKernelGGL((bwd_dw_part_kernel<TI, 8>), dim3(dw_blocks), dim3(64), 0,
+                           stream, p);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     const int64_t total = (int64_t)p.n_q * p.d;
     hipLaunchKernelGGL(bwd_dw_sum_kernel, dim3((unsigned)((total + 255) / 256), (unsigned)groups),

@@ -17,7 +17,8 @@
 // keep the fp32 vector kernel of bwd.hip.
 //
 // One workgroup of eight waves per token.  The token's B operands are split
-// and laid out as matrix fragments in LDS once.  The A operands are rows of
+// and laid out as matrix fragments in LDS once; K is packed (the four row
+// sets back to back, padded only at the end).  The A operands are rows of
 // dout, w and the history, read 16 rows (one 16-step) at a time: the waves
 // load the step's rows for 512 columns of d together, one 1 KB row segment
 // per load (a load that spans several rows, each in its own page, stalls the
@@ -63,18 +64,20 @@ __global__ __launch_bounds__(256) void split_w2_kernel(const float* w, int64_t n
 }
 
 template <int NT, int RING>
-__global__ __launch_bounds__(512) void bwd_dhist_mfma_kernel(BwdParams p, int kq, int kh) {
+__global__ __launch_bounds__(512) void bwd_dhist_mfma_kernel(BwdParams p, int nsteps) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), ln = tid & 63;
     const int h = ln >> 5, m = ln & 31;
     const int64_t t = blockIdx.x;
-    const int nks = 2 * kq + kh;  // 16-steps: g, then w, then v
+    // K runs over the reads' dout rows, w's hi and mid rows, then the history
+    // rows, packed (not padded per operand): nsteps 16-steps of K
+    const int k_w = p.n_q, k_m = 2 * p.n_q, k_v = 3 * p.n_q;
     const int S = p.S;
     const int q_end = p.q_begin + p.n_q;
 
     extern __shared__ float lds[];
-    u32x4* frag = reinterpret_cast<u32x4*>(lds);                   // [nks][NT][hi, lo][64 lanes]
-    float* cf = lds + (size_t)nks * NT * 2 * 64 * 4;               // [n_hist] C3[block] + K(row)
+    u32x4* frag = reinterpret_cast<u32x4*>(lds);                   // [nsteps][NT][hi, lo][64 lanes]
+    float* cf = lds + (size_t)nsteps * NT * 2 * 64 * 4;            // [n_hist] C3[block] + K(row)
     const int cf_floats = (p.n_hist + 3) & ~3;                     // then the step tile
 
     // ---- per-row coupling coefficient C3[c] + K(j) --------------------------
@@ -91,31 +94,34 @@ __global__ __launch_bounds__(512) void bwd_dhist_mfma_kernel(BwdParams p, int kq
     }
     __syncthreads();
 
-    // ---- B operands: lane (hh, i) of fragment (ks, nt) holds K = 8 hh + j ---
+    // ---- B operands: lane (hh, i) of fragment (ks, nt) holds K = 16 ks + 8 hh + j:
+    // A1 (dout rows), A2 (w hi rows; w mid rows against A2's hi part only:
+    // their lo fragment is 0), -coef (history rows)
     const float* A1 = p.ws_a1 + t * (int64_t)p.n_q * p.nh8;
     const float* A2 = p.ws_a2 + t * (int64_t)p.n_q * p.nh8;
-    for (int e = tid; e < nks * NT * 64; e += blockDim.x) {
+    for (int e = tid; e < nsteps * NT * 64; e += blockDim.x) {
         const int L = e & 63, fn = e >> 6;
         const int nt = fn % NT, ks = fn / NT;
         const int hh = L >> 5, i = 32 * nt + (L & 31);
+        const int ci = i < p.n_hist ? block_of_row(i, S) : -1;
         float v[8];
-        if (ks < 2 * kq) {
-            const float* A = ks < kq ? A1 : A2;
-            const int k0 = 16 * (ks < kq ? ks : ks - kq);
+        bool lo_zero[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int lq = k0 + 8 * hh + j;
-                v[j] = (lq < p.n_q && i < p.n_hist) ? A[(int64_t)lq * p.nh8 + i] : 0.f;
+        for (int j = 0; j < 8; ++j) {
+            const int k = 16 * ks + 8 * hh + j;
+            float x = 0.f;
+            if (ci >= 0) {
+                if (k < k_w) {
+                    x = A1[(int64_t)k * p.nh8 + i];
+                } else if (k < k_v) {
+                    x = A2[(int64_t)(k < k_m ? k - k_w : k - k_m) * p.nh8 + i];
+                } else if (k - k_v < p.n_hist) {
+                    const int r = k - k_v;
+                    x = block_of_row(r, S) == ci ? -cf[r > i ? r : i] : 0.f;
+                }
             }
-        } else {
-            const int r0 = 16 * (ks - 2 * kq);
-            const int ci = i < p.n_hist ? block_of_row(i, S) : -1;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int r = r0 + 8 * hh + j;
-                v[j] = (r < p.n_hist && ci >= 0 && block_of_row(r, S) == ci) ? -cf[r > i ? r : i]
-                                                                            : 0.f;
-            }
+            v[j] = x;
+            lo_zero[j] = k >= k_m && k < k_v;
         }
         u32x4 hi4, lo4;
 #pragma unroll
@@ -123,6 +129,8 @@ __global__ __launch_bounds__(512) void bwd_dhist_mfma_kernel(BwdParams p, int kq
             uint32_t h0, l0, h1, l1;
             split2(v[2 * q], h0, l0);
             split2(v[2 * q + 1], h1, l1);
+            if (lo_zero[2 * q]) l0 = 0u;
+            if (lo_zero[2 * q + 1]) l1 = 0u;
             hi4[q] = h0 | (h1 << 16);
             lo4[q] = l0 | (l1 << 16);
         }
@@ -146,40 +154,37 @@ __global__ __launch_bounds__(512) void bwd_dhist_mfma_kernel(BwdParams p, int kq
     struct Slot {
         u32x4 x, y;  // this wave's two rows of the step
     };
-    // A row past the operand's last row, or a step past the end, gets an
-    // empty range (zeros); columns past d read zeros from the row's range.
-    auto gather = [&](const bf16_t* base, int64_t stride, int nrows, int r0, uint32_t coff, Slot& sl) {
+    // Row k of K: dout row k, w hi / mid row, or history row.  A row past
+    // the end of K, or a step past the last, gets an empty range (zeros);
+    // columns past d read zeros from the row's range.
+    const bf16_t* w_mid = wsp + (int64_t)p.n_q * p.d;
+    const int k_end = k_v + p.n_hist;
+    auto gather = [&](int k0, bool live, uint32_t coff, Slot& sl) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int row = r0 + 2 * wave + k;
-            const bool ok = row < nrows;
+        for (int e = 0; e < 2; ++e) {
+            const int k = k0 + 2 * wave + e;
+            const bool ok = live && k < k_end;
+            const bf16_t* base = k < k_w ? dout_t + (int64_t)k * row_elems
+                                 : k < k_m ? wsp + (int64_t)(k - k_w) * p.d
+                                 : k < k_v ? w_mid + (int64_t)(k - k_m) * p.d
+                                           : hist_t + (int64_t)(k - k_v) * row_elems;
             const rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<bf16_t*>(base + (ok ? row : 0) * stride), (short)0, ok ? 2 * p.d : 0,
-                (int)kRsrcWord3);
+                const_cast<bf16_t*>(ok ? base : hist_t), (short)0, ok ? 2 * p.d : 0, (int)kRsrcWord3);
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr, coff, 0, 0);
-            if (k == 0) sl.x = v; else sl.y = v;
+            if (e == 0) sl.x = v; else sl.y = v;
         }
     };
     auto bfrag = [&](int ks, int nt, int part) {
         return __builtin_bit_cast(bf16x8_t, frag[((ks * NT + nt) * 2 + part) * 64 + ln]);
     };
 
-    // Steps per pass: g (kq), w hi (kq), w mid (kq), v (kh).  A ring of RING
-    // register slots runs over all passes: step sigma + RING is issued as soon
-    // as step sigma has gone to LDS.
+    // nsteps 16-steps per pass.  A ring of RING register slots runs over all
+    // passes: step sigma + RING is issued as soon as step sigma has gone to LDS.
     const int n_pass = (p.d + kDmCols - 1) / kDmCols;
-    const int nsteps = 3 * kq + kh;
     const int total = n_pass * nsteps;
-    const int64_t wpart = (int64_t)p.n_q * p.d;
     int i_pass = 0, i_st = 0;  // the next step to issue
-    auto issue = [&](Slot& sl) {  // selects only: the loads share one block
-        const bool isg = i_st < kq, isw = !isg && i_st < 3 * kq, mid = i_st >= 2 * kq;
-        const bf16_t* base = isg ? dout_t : (isw ? wsp + (mid ? wpart : 0) : hist_t);
-        const int64_t stride = isw ? (int64_t)p.d : row_elems;
-        int nrows = isg || isw ? p.n_q : p.n_hist;
-        nrows = i_pass < n_pass ? nrows : 0;  // past the last pass
-        const int r0 = 16 * (i_st - (isg ? 0 : (isw ? (mid ? 2 * kq : kq) : 3 * kq)));
-        gather(base, stride, nrows, r0, (uint32_t)(i_pass * kDmCols * 2 + 16 * ln), sl);
+    auto issue = [&](Slot& sl) {
+        gather(16 * i_st, i_pass < n_pass, (uint32_t)(i_pass * kDmCols * 2 + 16 * ln), sl);
         const bool wrap = i_st == nsteps - 1;
         i_st = wrap ? 0 : i_st + 1;
         i_pass += wrap ? 1 : 0;
@@ -223,32 +228,15 @@ __global__ __launch_bounds__(512) void bwd_dhist_mfma_kernel(BwdParams p, int kq
                 a[1] = __builtin_bit_cast(bf16x8_t, t1);
             }
             __syncthreads();
-            // B fragments: A1 (g steps), A2 (w steps; the mid part of w only
-            // against A2 hi), -coef (v steps)
-            int ksb;
-            bool two = true;
-            if (c_st < kq) {
-                ksb = c_st;
-            } else if (c_st < 3 * kq) {
-                const bool mid = c_st >= 2 * kq;
-                ksb = c_st - (mid ? kq : 0);
-                two = !mid;
-            } else {
-                ksb = c_st - kq;
-            }
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const bf16x8_t b0 = bfrag(ksb, nt, 0);
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    acc[kk][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b0, acc[kk][nt], 0, 0, 0);
-                if (two) {
-                    const bf16x8_t b1 = bfrag(ksb, nt, 1);
+                for (int part = 0; part < 2; ++part) {
+                    const bf16x8_t b = bfrag(c_st, nt, part);
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk)
-                        acc[kk][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b1, acc[kk][nt], 0, 0, 0);
+                        acc[kk][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b, acc[kk][nt], 0, 0, 0);
                 }
-            }
             if (c_st == nsteps - 1) {
                 // lane (h, m), register r of tile kk: column c_pass kDmCols + 64 w +
                 // 32 kk + 8 (r / 4) + 4 h + r % 4, row 32 nt + m
@@ -285,9 +273,10 @@ __global__ __launch_bounds__(512) void bwd_dhist_mfma_kernel(BwdParams p, int kq
 
 int dm_nt(const BwdParams& p) { return (p.n_hist + 31) / 32; }
 
+int dm_steps(const BwdParams& p) { return (3 * p.n_q + p.n_hist + 15) / 16; }
+
 size_t dm_lds(const BwdParams& p) {
-    const int kq = (p.n_q + 15) / 16, kh = (p.n_hist + 15) / 16;
-    return (size_t)(2 * kq + kh) * dm_nt(p) * 2 * 64 * 16 + (size_t)((p.n_hist + 3) & ~3) * 4 +
+    return (size_t)dm_steps(p) * dm_nt(p) * 2 * 64 * 16 + (size_t)((p.n_hist + 3) & ~3) * 4 +
            (size_t)16 * kDmRow * 2;
 }
 
@@ -304,7 +293,7 @@ bool bwd_dhist_mfma_applies(const BwdParams& p) {
 }
 
 hipError_t launch_bwd_dhist_mfma(const BwdParams& p, hipStream_t stream) {
-    const int kq = (p.n_q + 15) / 16, kh = (p.n_hist + 15) / 16;
+    const int nsteps = dm_steps(p);
     const int64_t nw = (int64_t)p.n_q * p.d;
     hipLaunchKernelGGL(split_w2_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream, p.w,
                        nw, p.ws_wsplit2);
@@ -321,9 +310,9 @@ hipError_t launch_bwd_dhist_mfma(const BwdParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)p.T), block(64 * kDmWaves);
     switch (dm_nt(p)) {
-        case 1: hipLaunchKernelGGL((bwd_dhist_mfma_kernel<1, kDmRing>), grid, block, lds, stream, p, kq, kh); break;
-        case 2: hipLaunchKernelGGL((bwd_dhist_mfma_kernel<2, kDmRing>), grid, block, lds, stream, p, kq, kh); break;
-        default: hipLaunchKernelGGL((bwd_dhist_mfma_kernel<3, kDmRing>), grid, block, lds, stream, p, kq, kh); break;
+        case 1: hipLaunchKernelGGL((bwd_dhist_mfma_kernel<1, kDmRing>), grid, block, lds, stream, p, nsteps); break;
+        case 2: hipLaunchKernelGGL((bwd_dhist_mfma_kernel<2, kDmRing>), grid, block, lds, stream, p, nsteps); break;
+        default: hipLaunchKernelGGL((bwd_dhist_mfma_kernel<3, kDmRing>), grid, block, lds, stream, p, nsteps); break;
     }
     return hipGetLastError();
 }

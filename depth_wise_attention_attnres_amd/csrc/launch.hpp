@@ -109,6 +109,10 @@ bool bwd_fits(const BwdParams& p);
 bool bwd_dhist_mfma_applies(const BwdParams& p);
 hipError_t launch_bwd_dhist_mfma(const BwdParams& p, hipStream_t stream);
 int64_t bwd_wsplit2_elems(int64_t n_q, int64_t d);
+// the per-chunk dw partials on the matrix cores (bwd_dw_mfma.hip): bf16
+// history, at most 64 reads; whether the call qualifies, the launch
+bool bwd_dw_mfma_applies(const BwdParams& p);
+hipError_t launch_bwd_dw_mfma(const BwdParams& p, int chunk_tokens, hipStream_t stream);
 // Size of the static device array that serves as the backward's workspace for
 // callers that cannot allocate, and its address on the current device (taken
 // once per device; bwd_scratch.hip).
