@@ -368,9 +368,10 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* ptr, bool ok) {
 // tile also forms the tile's |x_i|^2.  All waves load the operand slices and
 // then take (token, read) jobs wave, wave + 8, ... for the softmax.  n_q <= 64
 // (at most two read tiles), q_begin + n_q <= 128 (at most four row tiles).
-constexpr int kScStage = 64;                  // K elements per stage
+constexpr int kScStage = 128;                 // K elements per stage
+constexpr int kScChunks = kScStage / 8;       // 16-byte chunks per slice row and stage
 constexpr int kScRowLds = kScStage + 8;       // bf16 per LDS slice row (padded)
-constexpr int kScMaxPer = 6;                  // 16-byte chunks per thread and stage
+constexpr int kScMaxPer = 12;                 // 16-byte chunks per thread and stage
 constexpr int kScMaxSlices = kScMaxPer * 512 / (kScStage / 8);  // 384
 
 // LDS floats before the slices (P, Q, |x|^2, per-wave C3), rounded up to 16 bytes
@@ -420,17 +421,28 @@ __global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int n
     // K goes in stages of kScStage elements.  The stage's slices of each
     // token's rows (X) and upstream gradients (G), and of the three query
     // parts (W) -- TT (nr + n_q) + 3 n_q slices of kScStage bf16 each -- are
-    // brought into LDS with coalesced 16-byte loads (eight lanes per 128-byte
-    // slice), staged in registers while the previous stage multiplies, then
-    // every wave reads its matrix operands from LDS.  (Loaded straight from
+    // brought into LDS with coalesced 16-byte loads (sixteen lanes per
+    // 256-byte slice), staged in registers while the previous stage
+    // multiplies, then every wave reads its matrix operands from LDS.  A load
+    // instruction spans two history rows (each row in its own page; a load
+    // spanning many pages stalls the address unit).  (Loaded straight from
     // memory, each operand load touched 32 rows' cache lines for 32 bytes.)
     const int per_tok = nr + p.n_q;
     const int n_sl = TT * per_tok + 3 * p.n_q;
     bf16_t* sl = reinterpret_cast<bf16_t*>(lds + sc_lds_floats(TT, p.n_q, nr));  // [n_sl][kScRowLds]
     const int64_t wsz = (int64_t)p.n_q * p.d;
-    auto slice_src = [&](int r) -> const bf16_t* {  // start of slice r's row, or null (zeros)
+    // Loads walk the token slices interleaved (load slice rr * TT + tu is
+    // row rr of token tu), so one load instruction spans two rows; LDS keeps
+    // them token-major (slice tu * per_tok + rr), where the operand reads are
+    // free of bank conflicts.
+    auto lds_slice = [&](int r) {  // LDS slice of load slice r
+        if (r >= TT * per_tok) return r;
+        const int rr = r / TT;
+        return (r - rr * TT) * per_tok + rr;
+    };
+    auto slice_src = [&](int r) -> const bf16_t* {  // start of load slice r's row, or null (zeros)
         if (r < TT * per_tok) {
-            const int tu = r / per_tok, rr = r - tu * per_tok;
+            const int rr = r / TT, tu = r - rr * TT;
             if (tu >= ntok) return nullptr;
             const int64_t t = t0 + tu;
             if (rr < nr) return static_cast<const bf16_t*>(p.hist) + rr * row_elems + t * p.d;
@@ -440,7 +452,7 @@ __global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int n
         return reinterpret_cast<const bf16_t*>(p.ws_wsplit) + (int64_t)(r / p.n_q) * wsz +
                (int64_t)(r % p.n_q) * p.d;
     };
-    const int n_chunks = n_sl * (kScStage / 8);  // 16-byte chunks per stage (<= kScMaxPer * 512)
+    const int n_chunks = n_sl * kScChunks;  // 16-byte chunks per stage (<= kScMaxPer * 512)
     u32x4 stg[kScMaxPer];
     auto gload = [&](int k0) {
 #pragma unroll
@@ -448,7 +460,7 @@ __global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int n
             u32x4 v = {0u, 0u, 0u, 0u};
             const int idx = tid + 512 * c;
             if (idx < n_chunks) {
-                const int r = idx >> 3, k = k0 + 8 * (idx & 7);
+                const int r = idx / kScChunks, k = k0 + 8 * (idx % kScChunks);
                 const bf16_t* src = slice_src(r);
                 if (src != nullptr && k < p.d) v = *reinterpret_cast<const u32x4*>(src + k);
             }
@@ -460,7 +472,8 @@ __global__ __launch_bounds__(512) void bwd_scores_full_kernel(BwdParams p, int n
         for (int c = 0; c < kScMaxPer; ++c) {
             const int idx = tid + 512 * c;
             if (idx < n_chunks)
-                *reinterpret_cast<u32x4*>(sl + (idx >> 3) * kScRowLds + 8 * (idx & 7)) = stg[c];
+                *reinterpret_cast<u32x4*>(sl + lds_slice(idx / kScChunks) * kScRowLds + 8 * (idx % kScChunks)) =
+                    stg[c];
         }
     };
     auto frag = [&](int r, int k) {  // 8 bf16 of LDS slice r at element k
