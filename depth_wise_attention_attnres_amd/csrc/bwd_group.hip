@@ -26,10 +26,26 @@ constexpr int kBgWaves = 8;
 constexpr int kBgMinReads = 16;
 constexpr int kBgMaxSources = 13;  // v_0 + completed blocks a read of the call sees
 
-// LDS: sources [nb][d] fp32, their RMS scales [nbp], per-read C3 [n_q][nbp], counter
+// LDS: sources [nb][srow] fp32, their RMS scales [nbp], per-read C3 [n_q][nbp],
+// counter.  A source row holds, per 64-lane chunk group c2, two planes of
+// [64 lanes][4 floats] (elements 0-3 and 4-7 of each lane's 8): a lane's
+// 16-byte reads are then 16 bytes apart across the wave, free of bank
+// conflicts (8 contiguous floats per lane would put lanes 8 apart on the same
+// banks).
 __host__ __device__ inline int bg_nbp(int nb) { return (nb + 3) & ~3; }
-__host__ __device__ inline int64_t bg_lds_bytes(int nb, int d, int n_q) {
-    return (int64_t)nb * d * 4 + (int64_t)bg_nbp(nb) * 4 + (int64_t)n_q * bg_nbp(nb) * 4 + 16;
+__host__ __device__ inline int bg_srow(int nc) { return (nc + 63) / 64 * 512; }
+__host__ __device__ inline int64_t bg_lds_bytes(int nb, int nc, int n_q) {
+    return (int64_t)nb * bg_srow(nc) * 4 + (int64_t)bg_nbp(nb) * 4 + (int64_t)n_q * bg_nbp(nb) * 4 + 16;
+}
+// the two planes of lane ln's 8 elements of chunk group c2 in a source row
+__device__ __forceinline__ void bg_src_read(const float* row, int c2, int ln, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + (2 * c2) * 256 + 4 * ln);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(row + (2 * c2 + 1) * 256 + 4 * ln);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        x[q] = a[q];
+        x[4 + q] = b[q];
+    }
 }
 
 struct BgLane {
@@ -116,11 +132,10 @@ __device__ __forceinline__ void bg_group(const BwdParams& p, const float* src, c
 #pragma unroll
         for (int c2 = 0; c2 < NCH; ++c2) {
             if (!q.live[c2]) continue;
-            const int64_t off = 8 * (int64_t)(c2 * 64 + ln);
 #pragma unroll
             for (int c = 0; c < kW; ++c) {
                 float x[8];
-                lds_src(src, (int64_t)c * d + off, x);
+                bg_src_read(src + c * NCH * 512, c2, ln, x);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     v[c] = fmaf(wv[c2][e], x[e], v[c]);
@@ -221,7 +236,7 @@ __global__ __launch_bounds__(64 * kBgWaves) void bwd_scores_group_kernel(BwdPara
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     const int nbp = bg_nbp(nb);
     float* const src = reinterpret_cast<float*>(lds_raw);
-    float* const rsv = src + (int64_t)nb * p.d;
+    float* const rsv = src + (int64_t)nb * NCH * 512;
     float* const c3r = rsv + nbp;  // [n_q][nbp]: slot c of read lq = its C3 term for source c
     int* const counter = reinterpret_cast<int*>(c3r + (int64_t)p.n_q * nbp);
 
@@ -287,9 +302,9 @@ __global__ __launch_bounds__(64 * kBgWaves) void bwd_scores_group_kernel(BwdPara
 #pragma unroll
             for (int e = 0; e < 8; ++e) sq = fmaf(acc[c2][e], acc[c2][e], sq);
             if (q.live[c2]) {
-                float* dst = src + (int64_t)c * d + 8 * (c2 * 64 + ln);
+                float* dst = src + c * NCH * 512 + (2 * c2) * 256 + 4 * ln;
                 *reinterpret_cast<f32x4*>(dst) = f32x4{acc[c2][0], acc[c2][1], acc[c2][2], acc[c2][3]};
-                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[c2][4], acc[c2][5], acc[c2][6], acc[c2][7]};
+                *reinterpret_cast<f32x4*>(dst + 256) = f32x4{acc[c2][4], acc[c2][5], acc[c2][6], acc[c2][7]};
             }
         }
         sq = tg_sum<64>(sq);
@@ -351,7 +366,7 @@ int bg_sources(const BwdParams& p, size_t* lds) {
     const int nb = 1 + (p.q_begin + p.n_q - 1) / p.S;
     if (nb > kBgMaxSources) return 0;
     const int max_lds = device_max_lds();
-    const int64_t bytes = bg_lds_bytes(nb, p.d, p.n_q);
+    const int64_t bytes = bg_lds_bytes(nb, p.nc, p.n_q);
     if (bytes > max_lds) return 0;
     *lds = (size_t)bytes;
     return nb;

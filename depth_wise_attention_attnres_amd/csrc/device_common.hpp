@@ -243,17 +243,6 @@ __device__ __forceinline__ float wave_sum_transposed(const float (&v)[P], int la
     return x;
 }
 
-// 8 consecutive fp32 values of LDS, as two 16-byte reads
-__device__ __forceinline__ void lds_src(const float* src, int64_t off, float (&x)[8]) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(src + off);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(src + off + 4);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        x[q] = a[q];
-        x[4 + q] = b[q];
-    }
-}
-
 // Wave totals of KV values, as wave-uniform scalars: groups of up to 8 values
 // share one transposing reduction; value k of a group is read from the lane
 // that holds it (wave_sum_holder / wave_sum_index above).
