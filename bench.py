@@ -517,11 +517,10 @@ def extra_measurements(dev):
             # compulsory traffic of the backward: history and dout read, dhist written
             "bwd_algorithmic_GBps": (3 * n * T * d * 2) / (ms_b * 1e-3) / 1e9,
             "bwd_frac_of_hbm_peak": (3 * n * T * d * 2) / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            # the backward is bound by its arithmetic: algorithmic FMAs over the
-            # non-packed fp32 vector peak (packed fp32 is not used, so 78.6 TFLOP/s)
+            # useful arithmetic rate (the contractions run on the bf16 matrix
+            # cores with split fp32 operands, the per-read softmax work on the
+            # vector ALU; each kernel's own roofline is in its profile summary)
             "bwd_algorithmic_TFLOPs": 2 * bwd_fmas_per_token(n, n, S) * d * T / (ms_b * 1e-3) / 1e12,
-            "bwd_frac_of_fp32_vector_peak":
-                2 * bwd_fmas_per_token(n, n, S) * d * T / (ms_b * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
         }
         del ws
     return res
