@@ -26,6 +26,9 @@
 // column it needs for its MFMA operand (a transposed read), and a second
 // barrier frees the tile.  Wave w owns columns 64 w .. 64 w + 63 of each
 // 512-column pass: two 32-column output tiles.  Loads run two steps ahead.
+// The results leave the same way in reverse: 16 rows at a time through the
+// tile, one 1 KB row segment per store (a store spanning 32 rows, one per
+// lane pair, stalled like the loads).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -238,30 +241,40 @@ __global__ __launch_bounds__(512) void bwd_dhist_mfma_kernel(BwdParams p, int ns
                         acc[kk][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b, acc[kk][nt], 0, 0, 0);
                 }
             if (c_st == nsteps - 1) {
-                // lane (h, m), register r of tile kk: column c_pass kDmCols + 64 w +
-                // 32 kk + 8 (r / 4) + 4 h + r % 4, row 32 nt + m
-                const int cb = c_pass * kDmCols + 64 * wave;
+                // The pass's rows leave one 1 KB row segment per store: in rounds of 16
+                // rows through the step tile (free: every wave passed this step's second
+                // barrier).  Lane (h, m), register r of tile kk holds column 64 w + 32 kk +
+                // 8 (r / 4) + 4 h + r % 4 of row 32 nt + m.
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int i = 32 * nt + m;
-                    if (i < p.n_hist) {
-                        bf16_t* rowp = dh_t + i * row_elems;
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                        for (int kk = 0; kk < 2; ++kk)
+                    for (int half = 0; half < 2; ++half) {
+                        if ((m >> 4) == half) {
 #pragma unroll
-                            for (int g = 0; g < 4; ++g) {
-                                const int c0 = cb + 32 * kk + 8 * g + 4 * h;
-                                if (c0 < p.d)
-                                    *reinterpret_cast<uint2*>(rowp + c0) = make_uint2(
-                                        pack_bf16x2(acc[kk][nt][4 * g], acc[kk][nt][4 * g + 1]),
-                                        pack_bf16x2(acc[kk][nt][4 * g + 2], acc[kk][nt][4 * g + 3]));
-                            }
+                            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                                for (int g = 0; g < 4; ++g)
+                                    *reinterpret_cast<uint2*>(tb + (m & 15) * kDmRow + 64 * wave + 32 * kk + 8 * g + 4 * h) =
+                                        make_uint2(pack_bf16x2(acc[kk][nt][4 * g], acc[kk][nt][4 * g + 1]),
+                                                   pack_bf16x2(acc[kk][nt][4 * g + 2], acc[kk][nt][4 * g + 3]));
+                        }
+                        __syncthreads();
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {  // tile rows 2 w, 2 w + 1
+                            const int i = 32 * nt + 16 * half + 2 * wave + e;
+                            const int col = c_pass * kDmCols + 8 * ln;
+                            if (i < p.n_hist && col < p.d)
+                                *reinterpret_cast<u32x4*>(dh_t + i * row_elems + col) =
+                                    *reinterpret_cast<const u32x4*>(tb + (2 * wave + e) * kDmRow + 8 * ln);
+                        }
+                        __syncthreads();  // the tile is read before its next use
                     }
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc[kk][nt][r] = 0.f;
-                }
                 c_st = 0;
                 ++c_pass;
             } else {
