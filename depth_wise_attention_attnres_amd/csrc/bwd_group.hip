@@ -64,10 +64,6 @@ __device__ __forceinline__ void bg_group(const BwdParams& p, const float* src, c
     const int64_t row_elems = p.T * (int64_t)d;
     const int g0 = G * S;
 
-    float rsc[kW];
-#pragma unroll
-    for (int c = 0; c < kW; ++c) rsc[c] = rsv[c];
-
     float part[NCH][8];
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2)
@@ -121,7 +117,6 @@ __device__ __forceinline__ void bg_group(const BwdParams& p, const float* src, c
             wq[c2].to_float(wv[c2]);
             gq[c2].to_float(gv[c2]);
         }
-        if (l < lb) issue_wg(l + 1);
         const bool has_p = l > g0;
         if (has_p) add_row(rl);
         if (l < lb) issue_row(rl, l + 1);
@@ -149,6 +144,7 @@ __device__ __forceinline__ void bg_group(const BwdParams& p, const float* src, c
                 v[2 * kW + 2] = fmaf(part[c2][e], part[c2][e], v[2 * kW + 2]);
             }
         }
+        if (l < lb) issue_wg(l + 1);
         float tot[kV];
         wave_totals<0, kV>(v, tot, ln);
 
@@ -156,7 +152,7 @@ __device__ __forceinline__ void bg_group(const BwdParams& p, const float* src, c
         float s[kW + 1], a[kW + 1], r[kW + 1];
 #pragma unroll
         for (int c = 0; c < kW; ++c) {
-            r[c] = rsc[c];
+            r[c] = rsv[c];
             s[c] = r[c] * tot[c];
             a[c] = tot[kW + c];
         }
