@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libattnres.so")
 
-SOURCES = ["attnres_api.cpp", "lds_limit.cpp", "full_fwd.hip", "full_batch.hip", "block_fwd.hip", "block_batch.hip", "block_model.hip", "query_proj.hip", "bwd.hip", "bwd_dhist_mfma.hip", "bwd_dw_mfma.hip", "bwd_group.hip", "bwd_scratch.hip"]
+SOURCES = ["attnres_api.cpp", "lds_limit.cpp", "full_fwd.hip", "full_batch.hip", "full_batch_mfma.hip", "block_fwd.hip", "block_batch.hip", "block_model.hip", "query_proj.hip", "bwd.hip", "bwd_dhist_mfma.hip", "bwd_dw_mfma.hip", "bwd_group.hip", "bwd_scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -306,6 +306,7 @@ hipError_t dispatch_stream(const FwdParams& p, hipStream_t stream) {
 
 hipError_t launch_full_fwd(const FullFwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
                            hipStream_t stream) {
+    if (full_batch_mfma_applies(p, hist_dt, out_dt)) return launch_full_batch_mfma(p, stream);
     if (full_batch_applies(p, hist_dt)) return launch_full_batch(p, hist_dt, out_dt, stream);
     if (hist_dt == ATTNRES_BF16 && out_dt == ATTNRES_BF16)
         return dispatch_stream<bf16_t, bf16_t, false>(p, stream);

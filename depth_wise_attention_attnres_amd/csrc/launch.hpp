@@ -49,6 +49,10 @@ typedef FwdParams BlockFwdParams;
 
 hipError_t launch_full_fwd(const FullFwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
                            hipStream_t stream);
+// Full reads of a call with many reads over a bf16 history with bf16 outputs,
+// every row staged in LDS, both contractions on the matrix cores
+bool full_batch_mfma_applies(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt);
+hipError_t launch_full_batch_mfma(const FwdParams& p, hipStream_t stream);
 hipError_t launch_block_fwd(const BlockFwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
                             hipStream_t stream);
 // Full reads of a call with many reads, served from the token's rows staged in

@@ -204,3 +204,83 @@ def test_batch_edges(ar, oracle, dtype, n_hist, T, d, q_begin):
     ref, ref_lse = oracle.full_fwd(h64, w64[q_begin:], q_begin=q_begin, n_q=n_q)
     check_out(to_f64(out), ref, dtype)
     check_lse(to_f64(lse), ref_lse)
+
+
+# ---- the matrix-core kernel (full_batch_mfma.hip) ----------------------------
+# bf16 rows and bf16 outputs, d a multiple of 32, at most 96 rows and reads,
+# no fused pre-norm, and everything in LDS: rows (d + 8 bf16 each), the
+# weights' two bf16 parts per read (32 per started 32 rows, + 8), two tables
+# of one float per read and row tile, the RMS scales.
+
+def _mfma_lds(n_rows, n_q, d):
+    nrb, nks = (n_rows + 15) // 16, (n_rows + 31) // 32
+    return (n_rows * (d + 8) * 2 + 2 * n_q * (32 * nks + 8) * 2 + 2 * n_q * nrb * 4
+            + (n_rows + 3) // 4 * 4 * 4)
+
+
+def _mfma_qualifies(n_rows, n_q, d):
+    return (n_q >= 16 and d % 32 == 0 and d <= 2048 and n_rows <= 96
+            and _mfma_lds(n_rows, n_q, d) <= LDS_BYTES)
+
+
+# (n_hist, T, d, q_begin): chunks per lane 1 (d 32, 96), 2 (896), 3 (1536), 4 (2048);
+# one read tile and two row tiles (17 rows, 16 reads); ragged read and row tiles
+# (33 reads over 40 rows); the maximum of 96 rows and 96 reads; a read tile that
+# starts past row 0 sees every row tile
+MFMA_SHAPES = [(16, 37, 32, 0), (17, 20, 96, 1), (40, 23, 160, 7), (96, 5, 64, 0),
+               (65, 9, 896, 0), (40, 7, 1536, 3), (30, 13, 2048, 0), (70, 6, 256, 38)]
+
+
+@pytest.mark.parametrize("n_hist,T,d,q_begin", MFMA_SHAPES)
+def test_batch_mfma_shapes(ar, oracle, n_hist, T, d, q_begin):
+    n_q = n_hist - q_begin
+    assert _mfma_qualifies(n_hist, n_q, d)
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=3 * n_hist + d + q_begin, dtype="bf16")
+    out, lse = ar.full_fwd(h, w[q_begin:].contiguous(), q_begin=q_begin, n_q=n_q)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.full_fwd(h64, w64[q_begin:], q_begin=q_begin, n_q=n_q)
+    stats = check_out(to_f64(out), ref, "bf16")
+    check_lse(to_f64(lse), ref_lse)
+    # one rounding of an fp32 result: nearly every output is RNE(ref) exactly
+    assert stats["frac_equal_rne"] > 0.99, stats
+
+
+def test_batch_mfma_rows_past_reads_and_cache(ar, oracle):
+    # a history longer than the reads see (rows past the last read are never
+    # staged); reads 5..36 with rows 0..4 of the RMS cache valid from an
+    # earlier call, rows 5..36 formed and written by this one
+    n_hist, T, d = 45, 19, 320
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=29, dtype="bf16")
+    rinv = torch.full((n_hist, T), float("nan"), device=DEV)
+    ar.full_fwd(h, w[:5], q_begin=0, n_q=5, rinv=rinv)
+    assert _mfma_qualifies(37, 32, d)
+    out, lse = ar.full_fwd(h, w[5:37], q_begin=5, n_q=32, rinv=rinv, rinv_valid_rows=5)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.full_fwd(h64, w64[5:37], q_begin=5, n_q=32)
+    check_out(to_f64(out), ref, "bf16")
+    check_lse(to_f64(lse), ref_lse)
+    r = to_f64(rinv)
+    assert np.isfinite(r[:37]).all() and np.isnan(r[37:]).all()
+    np.testing.assert_allclose(r[:37], 1.0 / np.sqrt((h64[:37] ** 2).mean(axis=2) + 1e-6), rtol=2e-6)
+
+
+@pytest.mark.parametrize("q_begin", [0, 3])
+def test_batch_mfma_alpha_probe(ar, oracle, q_begin):
+    # weights in fp32 from the matrix-core scores; zero past each read's row
+    # and for history rows no read of the call sees
+    n_hist, T, d = 41, 17, 128
+    n_q = 35 - q_begin
+    assert _mfma_qualifies(q_begin + n_q, n_q, d)
+    h, w, hd, wd = _inputs(n_hist, T, d, seed=47 + q_begin, dtype="bf16", w_sigma=0.05)
+    w = w[q_begin:q_begin + n_q].contiguous()
+    alpha = torch.full((n_q, n_hist, T), float("nan"), device=DEV)
+    out, _ = ar.full_fwd(h, w, q_begin=q_begin, n_q=n_q, alpha=alpha)
+    torch.cuda.synchronize()
+    ref_out, _, ref = oracle.fwd(oracle.FULL, hd, wd[q_begin:q_begin + n_q], q_begin=q_begin, n_q=n_q,
+                                 want_alpha=True)
+    a = to_f64(alpha)
+    check_rel(a, ref.transpose(0, 2, 1), 1e-5, "alpha")
+    np.testing.assert_allclose(a.sum(1), 1.0, atol=1e-5)
+    for j in range(n_q):
+        assert (a[j, q_begin + j + 1:] == 0).all()
+    check_out(to_f64(out), ref_out, "bf16")
