@@ -41,7 +41,13 @@ constexpr int kBmMinReads = 16;
 constexpr int kBmMaxTiles = 6;       // reads and rows: at most 96 each (tiles of 16)
 constexpr int kBmJobTiles = 3;       // row tiles per score job
 constexpr int kBmJobsPerWave = 2;    // score jobs a wave holds through the softmax
-constexpr int kBmRowsInFlight = 8;   // rows per wave in flight while staging
+// Rows per wave a token's prefetch holds (kBmWaves times as many per token;
+// calls with more rows go to the vector kernel): 96 rows with one chunk per
+// lane, 80 with two (the registers of the prefetch come on top of the output
+// contraction's), 48 with three and 40 with four (the LDS holds 47 rows at
+// d = 1536 and 36 at d = 2048)
+template <int NCH>
+constexpr int bm_rows_in_flight() { return NCH == 1 ? 12 : (NCH == 2 ? 10 : (NCH == 3 ? 6 : 5)); }
 constexpr int kBmWRing = 4;          // K-steps of query fragments in flight
 constexpr int kBmMaxKs = (16 * kBmMaxTiles + 31) / 32;  // row steps of 32 in the output contraction
 
@@ -175,6 +181,12 @@ __device__ __forceinline__ void bm_scores(rsrc_t wr, uint32_t woff, const bf16_t
         if (kr + s < nk) step(wring[s], 32 * (kr + s));
 }
 
+// One workgroup per CU slot, looping over tokens t = blockIdx.x, + gridDim.x, ...
+// A token's rows come from registers loaded during the previous token's
+// output contraction (the first token's before the loop): the row loads of
+// token t + gridDim.x are issued once token t's score contraction is done, so
+// that no wait of that contraction (vector memory counts complete in issue
+// order) includes them, and they arrive while the outputs are formed.
 template <int NCH>
 __global__ __launch_bounds__(64 * kBmWaves) void full_batch_mfma_kernel(FwdParams p, int n_rows) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
@@ -189,262 +201,277 @@ __global__ __launch_bounds__(64 * kBmWaves) void full_batch_mfma_kernel(FwdParam
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ln = threadIdx.x & 63;
     const int g = ln >> 4, c16 = ln & 15;
-    const int64_t t = blockIdx.x;
     const int d = p.d, dst = L.dst, n_q = p.n_q;
     const int64_t row_elems = p.T * (int64_t)d;
-    const bf16_t* hist_tok = static_cast<const bf16_t*>(p.hist) + t * d;
     const uint64_t tok_bytes = (uint64_t)d * 2;
+    const cf32_ptr cache = const_view(p.rinv);
 
-    // weights start at zero: entries of rows a read's jobs do not cover stay so
-    for (int i = threadIdx.x; i < n_q * L.ast / 4; i += blockDim.x)
-        reinterpret_cast<u32x4*>(ap)[i] = u32x4{0u, 0u, 0u, 0u};
-
-    // ---- the token's rows into LDS, their RMS scales -------------------------
-    {
-        bool live[NCH];
-        uint32_t in_off[NCH];
+    // rows wave + kBmWaves u (u < U) of a token: this lane's 16-byte chunks
+    constexpr int U = bm_rows_in_flight<NCH>();
+    bool live[NCH];
+    uint32_t in_off[NCH];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int ch = c * 64 + ln;
-            live[c] = ch < p.nc;
-            in_off[c] = live[c] ? (uint32_t)(ch * 16) : kOOB;
+    for (int c = 0; c < NCH; ++c) {
+        const int ch = c * 64 + ln;
+        live[c] = ch < p.nc;
+        in_off[c] = live[c] ? (uint32_t)(ch * 16) : kOOB;
+    }
+    Chunk<bf16_t> pf[U][NCH];
+    auto prefetch = [&](int64_t tt) {
+        const bf16_t* htok = static_cast<const bf16_t*>(p.hist) + tt * d;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = wave + u * kBmWaves;
+            // rows past n_rows: a zero-length range (loads return zeros)
+            const rsrc_t rr = make_rsrc(htok + (i < n_rows ? i : 0) * row_elems, i < n_rows ? tok_bytes : 0);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) pf[u][c].template load<kAuxNT>(rr, in_off[c]);
         }
-        constexpr int U = kBmRowsInFlight;
-        const cf32_ptr cache = const_view(p.rinv);
-        for (int ib = wave; ib < n_rows; ib += kBmWaves * U) {
-            Chunk<bf16_t> ch[U][NCH];
+    };
+    if (blockIdx.x < p.T) prefetch(blockIdx.x);
+
+    for (int64_t t = blockIdx.x; t < p.T; t += gridDim.x) {
+        // weights start at zero: entries of rows a read's jobs do not cover stay so
+        for (int i = threadIdx.x; i < n_q * L.ast / 4; i += blockDim.x)
+            reinterpret_cast<u32x4*>(ap)[i] = u32x4{0u, 0u, 0u, 0u};
+
+        // ---- the token's rows into LDS, their RMS scales -------------------------
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = ib + u * kBmWaves;
-                if (i < n_rows) {
-                    const rsrc_t rr = make_rsrc(hist_tok + i * row_elems, tok_bytes);
+        for (int u = 0; u < U; ++u) {
+            const int i = wave + u * kBmWaves;
+            if (i < n_rows) {
 #pragma unroll
-                    for (int c = 0; c < NCH; ++c) ch[u][c].template load<kAuxNT>(rr, in_off[c]);
-                }
-            }
+                for (int c = 0; c < NCH; ++c)
+                    if (live[c]) *reinterpret_cast<u32x4*>(rows + (int64_t)i * dst + 8 * (c * 64 + ln)) = pf[u][c].v;
+                float r;
+                if (i < p.rinv_valid) {
+                    r = cache[(int64_t)i * p.T + t];
+                } else {
+                    float sq = 0.f;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = ib + u * kBmWaves;
-                if (i < n_rows) {
+                    for (int c = 0; c < NCH; ++c) {
+                        float x[8];
+                        pf[u][c].to_float(x);
 #pragma unroll
-                    for (int c = 0; c < NCH; ++c)
-                        if (live[c])
-                            *reinterpret_cast<u32x4*>(rows + (int64_t)i * dst + 8 * (c * 64 + ln)) = ch[u][c].v;
-                    float r;
-                    if (i < p.rinv_valid) {
-                        r = cache[(int64_t)i * p.T + t];
-                    } else {
-                        float sq = 0.f;
-#pragma unroll
-                        for (int c = 0; c < NCH; ++c) {
-                            float x[8];
-                            ch[u][c].to_float(x);
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) sq = fmaf(x[e], x[e], sq);
-                        }
-                        sq = tg_sum<64>(sq);
-                        r = fast_rsqrt(fmaf(sq, p.inv_d, p.eps));
-                        if (p.rinv != nullptr && ln == 0) p.rinv[(int64_t)i * p.T + t] = r;
+                        for (int e = 0; e < 8; ++e) sq = fmaf(x[e], x[e], sq);
                     }
-                    if (ln == 0) rs[i] = r;
+                    sq = tg_sum<64>(sq);
+                    r = fast_rsqrt(fmaf(sq, p.inv_d, p.eps));
+                    if (p.rinv != nullptr && ln == 0) p.rinv[(int64_t)i * p.T + t] = r;
+                }
+                if (ln == 0) rs[i] = r;
+            }
+        }
+        __syncthreads();
+
+        // ---- scores on the matrix cores ------------------------------------------
+        BmJob jobs[kBmJobsPerWave];
+        bool has[kBmJobsPerWave];
+        f32x4 sc[kBmJobsPerWave][kBmJobTiles];
+        const rsrc_t wr = make_rsrc(p.w, (uint64_t)n_q * d * 4);  // reads past n_q load zeros
+#pragma unroll
+        for (int q = 0; q < kBmJobsPerWave; ++q) {
+#pragma unroll
+            for (int u = 0; u < kBmJobTiles; ++u) sc[q][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            has[q] = bm_job(p, L.nrt, wave + kBmWaves * q, jobs[q]);
+            if (!has[q]) continue;
+            const BmJob J = jobs[q];
+            const int jq = 16 * J.a + c16;  // this lane's query row (A operand)
+            const uint32_t woff = jq < n_q ? (uint32_t)(jq * d + 8 * g) * 4u : kOOB;
+            int roff[kBmJobTiles];  // this lane's row (B operand), clamped to a staged row
+#pragma unroll
+            for (int u = 0; u < kBmJobTiles; ++u) {
+                int i = 16 * (J.b0 + u) + c16;
+                i = i < n_rows ? i : n_rows - 1;
+                roff[u] = i * dst + 8 * g;
+            }
+            switch (J.nb) {
+                case 1: bm_scores<1>(wr, woff, rows, roff, d, sc[q]); break;
+                case 2: bm_scores<2>(wr, woff, rows, roff, d, sc[q]); break;
+                default: bm_scores<3>(wr, woff, rows, roff, d, sc[q]); break;
+            }
+        }
+
+        // ---- softmax over each read's rows -----------------------------------------
+        // lane (g, c16), register r of job tile u: read j = 16 a + 4 g + r, row
+        // i = 16 (b0 + u) + c16; a 16-lane row of the wave holds one read's 16 rows
+#pragma unroll
+        for (int q = 0; q < kBmJobsPerWave; ++q) {
+            if (!has[q]) continue;
+            const BmJob J = jobs[q];
+#pragma unroll
+            for (int u = 0; u < kBmJobTiles; ++u) {
+                if (u >= J.nb) continue;
+                const int i = 16 * (J.b0 + u) + c16;
+                const float ri = rs[i < n_rows ? i : n_rows - 1] * kLog2e;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * J.a + 4 * g + r;
+                    const bool sees = j < n_q && i <= p.q_begin + j;
+                    const float s = sees ? ri * sc[q][u][r] : -INFINITY;
+                    sc[q][u][r] = s;
+                    const float mx = tg_max<16>(s);
+                    if (c16 == 0 && j < n_q) pm[j * L.nrb + J.b0 + u] = mx;
                 }
             }
         }
-    }
-    __syncthreads();
-
-    // ---- scores on the matrix cores ------------------------------------------
-    BmJob jobs[kBmJobsPerWave];
-    bool has[kBmJobsPerWave];
-    f32x4 sc[kBmJobsPerWave][kBmJobTiles];
-    const rsrc_t wr = make_rsrc(p.w, (uint64_t)n_q * d * 4);  // reads past n_q load zeros
+        __syncthreads();
+        float Mr[kBmJobsPerWave][4];
 #pragma unroll
-    for (int q = 0; q < kBmJobsPerWave; ++q) {
-#pragma unroll
-        for (int u = 0; u < kBmJobTiles; ++u) sc[q][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        has[q] = bm_job(p, L.nrt, wave + kBmWaves * q, jobs[q]);
-        if (!has[q]) continue;
-        const BmJob J = jobs[q];
-        const int jq = 16 * J.a + c16;  // this lane's query row (A operand)
-        const uint32_t woff = jq < n_q ? (uint32_t)(jq * d + 8 * g) * 4u : kOOB;
-        int roff[kBmJobTiles];  // this lane's row (B operand), clamped to a staged row
-#pragma unroll
-        for (int u = 0; u < kBmJobTiles; ++u) {
-            int i = 16 * (J.b0 + u) + c16;
-            i = i < n_rows ? i : n_rows - 1;
-            roff[u] = i * dst + 8 * g;
-        }
-        switch (J.nb) {
-            case 1: bm_scores<1>(wr, woff, rows, roff, d, sc[q]); break;
-            case 2: bm_scores<2>(wr, woff, rows, roff, d, sc[q]); break;
-            default: bm_scores<3>(wr, woff, rows, roff, d, sc[q]); break;
-        }
-    }
-
-    // ---- softmax over each read's rows -----------------------------------------
-    // lane (g, c16), register r of job tile u: read j = 16 a + 4 g + r, row
-    // i = 16 (b0 + u) + c16; a 16-lane row of the wave holds one read's 16 rows
-#pragma unroll
-    for (int q = 0; q < kBmJobsPerWave; ++q) {
-        if (!has[q]) continue;
-        const BmJob J = jobs[q];
-#pragma unroll
-        for (int u = 0; u < kBmJobTiles; ++u) {
-            if (u >= J.nb) continue;
-            const int i = 16 * (J.b0 + u) + c16;
-            const float ri = rs[i < n_rows ? i : n_rows - 1] * kLog2e;
+        for (int q = 0; q < kBmJobsPerWave; ++q) {
+            if (!has[q]) continue;
+            const BmJob J = jobs[q];
+            const int nb_a = bm_tile_rows(p, J.a);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int j = 16 * J.a + 4 * g + r;
-                const bool sees = j < n_q && i <= p.q_begin + j;
-                const float s = sees ? ri * sc[q][u][r] : -INFINITY;
-                sc[q][u][r] = s;
-                const float mx = tg_max<16>(s);
-                if (c16 == 0 && j < n_q) pm[j * L.nrb + J.b0 + u] = mx;
+                // the row tiles' maxima, all loads issued at once (a clamped
+                // index repeats the last tile, which leaves the max unchanged)
+                const int jc = j < n_q ? j : n_q - 1;
+                float M = -INFINITY;
+#pragma unroll
+                for (int b = 0; b < kBmMaxTiles; ++b) M = fmaxf(M, pm[jc * L.nrb + (b < nb_a ? b : nb_a - 1)]);
+                Mr[q][r] = j < n_q ? M : 0.f;  // reads past n_q: any finite value (weights unused)
+            }
+#pragma unroll
+            for (int u = 0; u < kBmJobTiles; ++u) {
+                if (u >= J.nb) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * J.a + 4 * g + r;
+                    const float e = fast_exp2(sc[q][u][r] - Mr[q][r]);  // -inf -> 0
+                    sc[q][u][r] = e;
+                    const float sm = tg_sum<16>(e);
+                    if (c16 == 0 && j < n_q) ps[j * L.nrb + J.b0 + u] = sm;
+                }
             }
         }
-    }
-    __syncthreads();
-    float Mr[kBmJobsPerWave][4];
+        __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kBmJobsPerWave; ++q) {
-        if (!has[q]) continue;
-        const BmJob J = jobs[q];
-        const int nb_a = bm_tile_rows(p, J.a);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = 16 * J.a + 4 * g + r;
-            float M = 0.f;  // reads past n_q: any finite value (their weights are unused)
-            if (j < n_q) {
-                M = -INFINITY;
-                for (int b = 0; b < nb_a; ++b) M = fmaxf(M, pm[j * L.nrb + b]);
-            }
-            Mr[q][r] = M;
-        }
-#pragma unroll
-        for (int u = 0; u < kBmJobTiles; ++u) {
-            if (u >= J.nb) continue;
+        for (int q = 0; q < kBmJobsPerWave; ++q) {
+            if (!has[q]) continue;
+            const BmJob J = jobs[q];
+            const int nb_a = bm_tile_rows(p, J.a);
+            float inv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int j = 16 * J.a + 4 * g + r;
-                const float e = fast_exp2(sc[q][u][r] - Mr[q][r]);  // -inf -> 0
-                sc[q][u][r] = e;
-                const float sm = tg_sum<16>(e);
-                if (c16 == 0 && j < n_q) ps[j * L.nrb + J.b0 + u] = sm;
-            }
-        }
-    }
-    __syncthreads();
+                const int jc = j < n_q ? j : n_q - 1;
+                float Z = 0.f;  // the row tiles' sums in tile order, all loads issued at once
 #pragma unroll
-    for (int q = 0; q < kBmJobsPerWave; ++q) {
-        if (!has[q]) continue;
-        const BmJob J = jobs[q];
-        const int nb_a = bm_tile_rows(p, J.a);
-        float inv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = 16 * J.a + 4 * g + r;
-            float Z = 1.f;
-            if (j < n_q) {
-                Z = 0.f;
-                for (int b = 0; b < nb_a; ++b) Z += ps[j * L.nrb + b];
-                if (J.b0 == 0 && c16 == 0 && p.lse != nullptr)
+                for (int b = 0; b < kBmMaxTiles; ++b) {
+                    const float v = ps[jc * L.nrb + (b < nb_a ? b : nb_a - 1)];
+                    Z += b < nb_a ? v : 0.f;
+                }
+                if (j < n_q && J.b0 == 0 && c16 == 0 && p.lse != nullptr)
                     p.lse[(int64_t)j * p.T + t] = (Mr[q][r] + fast_log2(Z)) * kLn2;
+                inv[r] = j < n_q ? 1.0f / Z : 0.f;
             }
-            inv[r] = 1.0f / Z;
-        }
 #pragma unroll
-        for (int u = 0; u < kBmJobTiles; ++u) {
-            if (u >= J.nb) continue;
-            const int i = 16 * (J.b0 + u) + c16;
-            const int kk = 32 * (i >> 5) + bm_kidx(i & 31);
+            for (int u = 0; u < kBmJobTiles; ++u) {
+                if (u >= J.nb) continue;
+                const int i = 16 * (J.b0 + u) + c16;
+                const int kk = 32 * (i >> 5) + bm_kidx(i & 31);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * J.a + 4 * g + r;
-                if (j >= n_q) continue;
-                const float a = sc[q][u][r] * inv[r];
-                const uint32_t hp = pack_bf16x2(a, 0.f) & 0xffffu;
-                const uint32_t lp = pack_bf16x2(a - __uint_as_float(hp << 16), 0.f) & 0xffffu;
-                ap[(int64_t)j * L.ast + kk] = (uint16_t)hp;
-                ap[(int64_t)(n_q + j) * L.ast + kk] = (uint16_t)lp;
-                if (p.alpha != nullptr && i < p.n_hist)
-                    p.alpha[((int64_t)j * p.n_hist + i) * p.T + t] = a;
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * J.a + 4 * g + r;
+                    if (j >= n_q) continue;
+                    const float a = sc[q][u][r] * inv[r];
+                    const uint32_t hp = pack_bf16x2(a, 0.f) & 0xffffu;
+                    const uint32_t lp = pack_bf16x2(a - __uint_as_float(hp << 16), 0.f) & 0xffffu;
+                    ap[(int64_t)j * L.ast + kk] = (uint16_t)hp;
+                    ap[(int64_t)(n_q + j) * L.ast + kk] = (uint16_t)lp;
+                    if (p.alpha != nullptr && i < p.n_hist)
+                        p.alpha[((int64_t)j * p.n_hist + i) * p.T + t] = a;
+                }
             }
         }
-    }
-    if (p.alpha != nullptr) {  // rows past the tiles a read sees
-        for (int k = threadIdx.x; k < n_q * p.n_hist; k += blockDim.x) {
-            const int j = k / p.n_hist, i = k - j * p.n_hist;
-            if (i >= 16 * bm_tile_rows(p, j / 16)) p.alpha[((int64_t)j * p.n_hist + i) * p.T + t] = 0.f;
+        if (p.alpha != nullptr) {  // rows past the tiles a read sees
+            for (int k = threadIdx.x; k < n_q * p.n_hist; k += blockDim.x) {
+                const int j = k / p.n_hist, i = k - j * p.n_hist;
+                if (i >= 16 * bm_tile_rows(p, j / 16)) p.alpha[((int64_t)j * p.n_hist + i) * p.T + t] = 0.f;
+            }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- outputs on the matrix cores --------------------------------------------
-    // wave w takes the column tiles [w ne / 8, (w + 1) ne / 8) (16 columns each).
-    // A column tile's row fragments are gathered once for every row step (the
-    // rows of step ks in column c16: 32 ks + 2 g + 8 q + h; past the last row
-    // the last row, whose weights are zero there or which no read tile uses),
-    // then each read tile in turn multiplies the steps it needs into one
-    // accumulator and stores it (a read past n_q reads the last read's weights
-    // and stores nothing).
-    const int ne = d / 16;
-    const int et0 = wave * ne / kBmWaves, et1 = (wave + 1) * ne / kBmWaves;
-    int goff[kBmMaxKs][8];
+        // ---- outputs on the matrix cores --------------------------------------------
+        // the next token's rows, in flight while this token's outputs are formed
+        if (t + gridDim.x < p.T) prefetch(t + gridDim.x);
+        // wave w takes the column tiles [w ne / 8, (w + 1) ne / 8) (16 columns each).
+        // A column tile's row fragments are gathered once for every row step (the
+        // rows of step ks in column c16: 32 ks + 2 g + 8 q + h; past the last row
+        // the last row, whose weights are zero there or which no read tile uses),
+        // then each read tile in turn multiplies the steps it needs into one
+        // accumulator and stores it (a read past n_q reads the last read's weights
+        // and stores nothing).
+        const int ne = d / 16;
+        const int et0 = wave * ne / kBmWaves, et1 = (wave + 1) * ne / kBmWaves;
+        int goff[kBmMaxKs][8];
 #pragma unroll
-    for (int ks = 0; ks < kBmMaxKs; ++ks)
+        for (int ks = 0; ks < kBmMaxKs; ++ks)
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int i = 32 * ks + 2 * g + 8 * (m >> 1) + (m & 1);
-            goff[ks][m] = (i < n_rows ? i : n_rows - 1) * dst + c16;
-        }
-    const int aplane = n_q * L.ast;  // elements from a weight's hi part to its lo part
-    for (int et = et0; et < et1; ++et) {
-        const int e0 = 16 * et;
-        bf16x8_t xa[kBmMaxKs];
-#pragma unroll
-        for (int ks = 0; ks < kBmMaxKs; ++ks) {
-            u32x4 av;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t lo = rows16[goff[ks][2 * q] + e0];
-                const uint32_t hi = rows16[goff[ks][2 * q + 1] + e0];
-                av[q] = lo | (hi << 16);
+            for (int m = 0; m < 8; ++m) {
+                const int i = 32 * ks + 2 * g + 8 * (m >> 1) + (m & 1);
+                goff[ks][m] = (i < n_rows ? i : n_rows - 1) * dst + c16;
             }
-            xa[ks] = __builtin_bit_cast(bf16x8_t, av);
-        }
-        for (int a = 0; a < L.nrt; ++a) {
-            const int ks_last = (bm_tile_rows(p, a) * 16 - 1) / 32;
-            const int j = 16 * a + c16;
-            const int jc = j < n_q ? j : n_q - 1;
-            const uint16_t* arow = ap + jc * L.ast + 8 * g;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int aplane = n_q * L.ast;  // elements from a weight's hi part to its lo part
+        for (int et = et0; et < et1; ++et) {
+            const int e0 = 16 * et;
+            bf16x8_t xa[kBmMaxKs];
 #pragma unroll
             for (int ks = 0; ks < kBmMaxKs; ++ks) {
-                if (ks > ks_last) break;
+                u32x4 av;
 #pragma unroll
-                for (int part = 0; part < 2; ++part) {
-                    const u32x4 bv = *reinterpret_cast<const u32x4*>(arow + part * aplane + 32 * ks);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[ks], __builtin_bit_cast(bf16x8_t, bv), acc, 0,
-                                                                  0, 0);
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = rows16[goff[ks][2 * q] + e0];
+                    const uint32_t hi = rows16[goff[ks][2 * q + 1] + e0];
+                    av[q] = lo | (hi << 16);
+                }
+                xa[ks] = __builtin_bit_cast(bf16x8_t, av);
+            }
+            for (int a = 0; a < L.nrt; ++a) {
+                const int ks_last = (bm_tile_rows(p, a) * 16 - 1) / 32;
+                const int j = 16 * a + c16;
+                const int jc = j < n_q ? j : n_q - 1;
+                const uint16_t* arow = ap + jc * L.ast + 8 * g;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < kBmMaxKs; ++ks) {
+                    if (ks > ks_last) break;
+#pragma unroll
+                    for (int part = 0; part < 2; ++part) {
+                        const u32x4 bv = *reinterpret_cast<const u32x4*>(arow + part * aplane + 32 * ks);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[ks], __builtin_bit_cast(bf16x8_t, bv), acc, 0,
+                                                                      0, 0);
+                    }
+                }
+                // lane (g, c16): columns e0 + 4 g .. + 3 of read j
+                if (j < n_q) {
+                    uint32_t* dstp = reinterpret_cast<uint32_t*>(static_cast<bf16_t*>(p.out) + (int64_t)j * row_elems +
+                                                                 t * d + e0 + 4 * g);
+                    dstp[0] = pack_bf16x2(acc[0], acc[1]);
+                    dstp[1] = pack_bf16x2(acc[2], acc[3]);
                 }
             }
-            // lane (g, c16): columns e0 + 4 g .. + 3 of read j
-            if (j < n_q) {
-                uint32_t* dstp = reinterpret_cast<uint32_t*>(static_cast<bf16_t*>(p.out) + (int64_t)j * row_elems +
-                                                             t * d + e0 + 4 * g);
-                dstp[0] = pack_bf16x2(acc[0], acc[1]);
-                dstp[1] = pack_bf16x2(acc[2], acc[3]);
-            }
         }
+        __syncthreads();  // the next token may overwrite the rows and weights
     }
 }
 
 template <int NCH>
 hipError_t launch_bm(const FwdParams& p, int n_rows, size_t lds, hipStream_t stream) {
-    const hipError_t e = prepare_dynamic_lds((const void*)full_batch_mfma_kernel<NCH>, lds);
+    const void* kern = (const void*)full_batch_mfma_kernel<NCH>;
+    hipError_t e = prepare_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(full_batch_mfma_kernel<NCH>, dim3((unsigned)p.T), dim3(64 * kBmWaves), lds, stream, p,
+    // as many workgroups as the device holds at once, each looping over tokens
+    int dev = 0, ncu = 0, per_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kBmWaves, lds)) != hipSuccess)
+        return e;
+    const int64_t slots = (int64_t)ncu * (per_cu > 0 ? per_cu : 1);
+    const int64_t grid = p.T < slots ? p.T : slots;
+    hipLaunchKernelGGL(full_batch_mfma_kernel<NCH>, dim3((unsigned)grid), dim3(64 * kBmWaves), lds, stream, p,
                        n_rows);
     return hipGetLastError();
 }
@@ -455,6 +482,13 @@ int64_t bm_plan(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt)
     if (p.qtok != nullptr || p.normed != nullptr || p.n_q < kBmMinReads) return 0;
     if (p.d % 32 != 0 || p.nc > 4 * 64) return 0;
     const int n_rows = p.q_begin + p.n_q;
+    // one round of row loads per wave covers the token
+    const int nch = (p.nc + 63) / 64;
+    const int rows_per_round = kBmWaves * (nch == 1   ? bm_rows_in_flight<1>()
+                                           : nch == 2 ? bm_rows_in_flight<2>()
+                                           : nch == 3 ? bm_rows_in_flight<3>()
+                                                      : bm_rows_in_flight<4>());
+    if (n_rows > rows_per_round) return 0;
     if (n_rows > 16 * kBmMaxTiles || p.n_q > 16 * kBmMaxTiles) return 0;
     if (p.T * 64 * kBmWaves >= ((int64_t)1 << 32)) return 0;
     const BmLayout L = bm_layout(n_rows, p.n_q, p.d);

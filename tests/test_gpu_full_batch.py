@@ -207,10 +207,11 @@ def test_batch_edges(ar, oracle, dtype, n_hist, T, d, q_begin):
 
 
 # ---- the matrix-core kernel (full_batch_mfma.hip) ----------------------------
-# bf16 rows and bf16 outputs, d a multiple of 32, at most 96 rows and reads,
-# no fused pre-norm, and everything in LDS: rows (d + 8 bf16 each), the
-# weights' two bf16 parts per read (32 per started 32 rows, + 8), two tables
-# of one float per read and row tile, the RMS scales.
+# bf16 rows and bf16 outputs, d a multiple of 32, at most 96 reads, at most
+# 96 / 80 / 48 / 40 rows with 1 / 2 / 3 / 4 chunks of 8 per lane (a token's
+# rows are prefetched in registers), no fused pre-norm, and everything in LDS:
+# rows (d + 8 bf16 each), the weights' two bf16 parts per read (32 per started
+# 32 rows, + 8), two tables of one float per read and row tile, the RMS scales.
 
 def _mfma_lds(n_rows, n_q, d):
     nrb, nks = (n_rows + 15) // 16, (n_rows + 31) // 32
@@ -219,7 +220,9 @@ def _mfma_lds(n_rows, n_q, d):
 
 
 def _mfma_qualifies(n_rows, n_q, d):
-    return (n_q >= 16 and d % 32 == 0 and d <= 2048 and n_rows <= 96
+    nch = (d // 8 + 63) // 64
+    max_rows = {1: 96, 2: 80, 3: 48, 4: 40}.get(nch, 0)
+    return (n_q >= 16 and n_q <= 96 and d % 32 == 0 and n_rows <= max_rows
             and _mfma_lds(n_rows, n_q, d) <= LDS_BYTES)
 
 
