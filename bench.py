@@ -332,7 +332,6 @@ def _time(fn, stream, reps, warm):
     return a.elapsed_time(b) / reps
 
 
-FP32_VECTOR_PEAK_TFLOPS = 78.6  # 256 CUs x 64 lanes x 2 FLOP x 2.4 GHz, no packed fp32
 
 
 def bwd_fmas_per_token(n_hist, n_q, S):
@@ -449,12 +448,16 @@ def extra_measurements(dev):
             ms = _time(lambda: ar.full_fwd(h, w, out=out, lse=lse), stream, 5, 2)
             flops = 2.0 * full_fwd_fmas_per_token(n, n) * d * T
             nbytes = 2 * n * T * d * 2 + n * T * 4
+            # bf16 rows and outputs: both contractions on the bf16 matrix cores
+            # (split fp32 operands), the softmax and the operand splits on the
+            # vector ALU; the useful arithmetic rate and the HBM fraction of the
+            # algorithmic bytes (each row read once, each output written once)
             res[name + "_batched"] = {
                 "what": f"Full AttnRes forward, all {n} reads in one call",
                 "ms": ms, "tokens_per_s": T / (ms * 1e-3),
                 "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
-                "algorithmic_TFLOPs": flops / (ms * 1e-3) / 1e12,
-                "frac_of_fp32_vector_peak": flops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+                "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "algorithmic_TFLOPs": flops / (ms * 1e-3) / 1e12}
         del h, w, out, lse
         torch.cuda.empty_cache()
 
@@ -510,9 +513,8 @@ def extra_measurements(dev):
             "fwd_ms": ms_f, "bwd_ms": ms_b,
             "fwd_bwd_tokens_per_s": T / ((ms_f + ms_b) * 1e-3),
             "fwd_algorithmic_GBps": (2 * n * T * d * 2) / (ms_f * 1e-3) / 1e9,
-            **({"fwd_algorithmic_TFLOPs": 2 * full_fwd_fmas_per_token(n, n) * d * T / (ms_f * 1e-3) / 1e12,
-                "fwd_frac_of_fp32_vector_peak":
-                    2 * full_fwd_fmas_per_token(n, n) * d * T / (ms_f * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+            "fwd_frac_of_hbm_peak": (2 * n * T * d * 2) / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            **({"fwd_algorithmic_TFLOPs": 2 * full_fwd_fmas_per_token(n, n) * d * T / (ms_f * 1e-3) / 1e12}
                if variant == ar.FULL else {}),
             # compulsory traffic of the backward: history and dout read, dhist written
             "bwd_algorithmic_GBps": (3 * n * T * d * 2) / (ms_b * 1e-3) / 1e9,
