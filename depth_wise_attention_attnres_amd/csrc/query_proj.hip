@@ -22,8 +22,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // computes 64 x 64 as 2 x 2 fragments of 32 x 32, so each operand fragment
 // read from LDS feeds two matrix instructions.  K goes in stages of 64
 // elements through double-buffered LDS: the workgroup loads a stage's 128
-// token rows and 128 W rows (contiguous in k, 16 bytes per lane)
-// while it multiplies the previous stage; one barrier per stage.
+// token rows and 128 W rows (contiguous in k, 16 bytes per lane) two stages
+// ahead while it multiplies; one barrier per stage.  (Passing the fp32 results
+// through LDS for 16-byte stores measured slower: one more barrier and round
+// trip against 4-byte stores that already fill 128-byte lines per wave.)
 constexpr int kTileM = 128, kTileN = 128, kStageK = 64;
 constexpr int kLdsRow = kStageK + 8;  // bf16 elements per LDS row (padded: staggers the banks)
 
@@ -51,29 +53,33 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
     // (idx / kCh, idx % kCh), idx = tid + 256 c, of each operand tile
     constexpr int kCh = kStageK / 8;                 // 16-byte chunks per row
     constexpr int kPer = kTileM * kCh / 256;         // chunks per thread and operand
-    u32x4 sa[kPer], sb[kPer];
-    auto gload = [&](int k0) {
+    // Buffer loads over the tile's token rows and output rows: a chunk past T,
+    // d or the last column loads zeros, without branches (a load inside a
+    // branch makes every later wait drain all loads in flight).  Two register
+    // slots: a stage's loads are issued two stages before its LDS store.
+    const int n_tok = T - t0 < kTileM ? (int)(T - t0) : kTileM;
+    const int n_out = d - o0 < kTileN ? d - o0 : kTileN;
+    const rsrc_t ra_x = make_rsrc(xj + t0 * d, (uint64_t)n_tok * d * 2);
+    const rsrc_t rb_w = make_rsrc(wj + (int64_t)o0 * d, (uint64_t)n_out * d * 2);
+    u32x4 sa[2][kPer], sb[2][kPer];
+    auto gload = [&](int slot, int k0) {
 #pragma unroll
         for (int c = 0; c < kPer; ++c) {
             const int idx = tid + 256 * c;
             const int row = idx / kCh, kc = idx % kCh;
             const int k = k0 + 8 * kc;
-            const int64_t tok = t0 + row;
-            const int out = o0 + row;
-            u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-            if (tok < T && k < d) va = *reinterpret_cast<const u32x4*>(xj + tok * d + k);
-            if (out < d && k < d) vb = *reinterpret_cast<const u32x4*>(wj + (int64_t)out * d + k);
-            sa[c] = va;
-            sb[c] = vb;
+            const uint32_t off = k < d ? (uint32_t)(row * d + k) * 2u : kOOB;
+            sa[slot][c] = __builtin_amdgcn_raw_buffer_load_b128(ra_x, off, 0, 0);
+            sb[slot][c] = __builtin_amdgcn_raw_buffer_load_b128(rb_w, off, 0, 0);
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf, int slot) {
 #pragma unroll
         for (int c = 0; c < kPer; ++c) {
             const int idx = tid + 256 * c;
             const int row = idx / kCh, kc = idx % kCh;
-            *reinterpret_cast<u32x4*>(&lds_a[buf][row * kLdsRow + 8 * kc]) = sa[c];
-            *reinterpret_cast<u32x4*>(&lds_b[buf][row * kLdsRow + 8 * kc]) = sb[c];
+            *reinterpret_cast<u32x4*>(&lds_a[buf][row * kLdsRow + 8 * kc]) = sa[slot][c];
+            *reinterpret_cast<u32x4*>(&lds_b[buf][row * kLdsRow + 8 * kc]) = sb[slot][c];
         }
     };
 
@@ -86,32 +92,41 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
             for (int r = 0; r < 16; ++r) acc[fa][fb][r] = 0.f;
 
     const int n_stages = (d + kStageK - 1) / kStageK;
-    gload(0);
-    lstore(0);
+    gload(0, 0);
+    gload(1, kStageK);  // past d: zeros, never stored
+    lstore(0, 0);
     __syncthreads();
-    for (int st = 0; st < n_stages; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < n_stages) gload((st + 1) * kStageK);
+    // step st: slot st % 2 (stored already) takes stage st + 2's loads, the
+    // MFMAs read buffer st % 2, then stage st + 1 goes from slot (st + 1) % 2
+    // into the other buffer, last read before the previous barrier
+    for (int st0 = 0; st0 < n_stages; st0 += 2) {
 #pragma unroll
-        for (int sub = 0; sub < kStageK / 16; ++sub) {
-            bf16x8_t fa_op[2], fb_op[2];
+        for (int u = 0; u < 2; ++u) {
+            const int st = st0 + u;
+            if (st >= n_stages) break;
+            gload(u, (st + 2) * kStageK);
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                const int ra = 64 * wr + 32 * f + m, rb = 64 * wc + 32 * f + m;
-                fa_op[f] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_a[buf][ra * kLdsRow + 16 * sub + 8 * h]));
-                fb_op[f] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_b[buf][rb * kLdsRow + 16 * sub + 8 * h]));
+            for (int sub = 0; sub < kStageK / 16; ++sub) {
+                bf16x8_t fa_op[2], fb_op[2];
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const int ra = 64 * wr + 32 * f + m, rb = 64 * wc + 32 * f + m;
+                    fa_op[f] = __builtin_bit_cast(
+                        bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_a[u][ra * kLdsRow + 16 * sub + 8 * h]));
+                    fb_op[f] = __builtin_bit_cast(
+                        bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_b[u][rb * kLdsRow + 16 * sub + 8 * h]));
+                }
+#pragma unroll
+                for (int fa = 0; fa < 2; ++fa)
+#pragma unroll
+                    for (int fb = 0; fb < 2; ++fb)
+                        acc[fa][fb] =
+                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_op[fa], fb_op[fb], acc[fa][fb], 0, 0, 0);
             }
-#pragma unroll
-            for (int fa = 0; fa < 2; ++fa)
-#pragma unroll
-                for (int fb = 0; fb < 2; ++fb)
-                    acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_op[fa], fb_op[fb], acc[fa][fb], 0, 0, 0);
-        }
-        if (st + 1 < n_stages) {
-            lstore(buf ^ 1);  // the other buffer: last read before the previous barrier
-            __syncthreads();
+            if (st + 1 < n_stages) {
+                lstore(u ^ 1, u ^ 1);
+                __syncthreads();
+            }
         }
     }
     // lane j, register r of fragment (fa, fb) holds token t0 + 64 wr + 32 fa + i,
