@@ -22,8 +22,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // computes 64 x 64 as 2 x 2 fragments of 32 x 32, so each operand fragment
 // read from LDS feeds two matrix instructions.  K goes in stages of 64
 // elements through double-buffered LDS: the workgroup loads a stage's 128
-// token rows and 128 W rows (contiguous in k, 16 bytes per lane) two stages
-// ahead while it multiplies; one barrier per stage.  (Passing the fp32 results
+// token rows and 128 W rows (contiguous in k, 16 bytes per lane) three stages
+// ahead of its multiplication; one barrier per stage.  (Passing the fp32 results
 // through LDS for 16-byte stores measured slower: one more barrier and round
 // trip against 4-byte stores that already fill 128-byte lines per wave.)
 constexpr int kTileM = 128, kTileN = 128, kStageK = 64;
@@ -55,13 +55,13 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
     constexpr int kPer = kTileM * kCh / 256;         // chunks per thread and operand
     // Buffer loads over the tile's token rows and output rows: a chunk past T,
     // d or the last column loads zeros, without branches (a load inside a
-    // branch makes every later wait drain all loads in flight).  Two register
+    // branch makes every later wait drain all loads in flight).  Three register
     // slots: a stage's loads are issued two stages before its LDS store.
     const int n_tok = T - t0 < kTileM ? (int)(T - t0) : kTileM;
     const int n_out = d - o0 < kTileN ? d - o0 : kTileN;
     const rsrc_t ra_x = make_rsrc(xj + t0 * d, (uint64_t)n_tok * d * 2);
     const rsrc_t rb_w = make_rsrc(wj + (int64_t)o0 * d, (uint64_t)n_out * d * 2);
-    u32x4 sa[2][kPer], sb[2][kPer];
+    u32x4 sa[3][kPer], sb[3][kPer];
     auto gload = [&](int slot, int k0) {
 #pragma unroll
         for (int c = 0; c < kPer; ++c) {
@@ -94,17 +94,19 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
     const int n_stages = (d + kStageK - 1) / kStageK;
     gload(0, 0);
     gload(1, kStageK);  // past d: zeros, never stored
+    gload(2, 2 * kStageK);
     lstore(0, 0);
     __syncthreads();
-    // step st: slot st % 2 (stored already) takes stage st + 2's loads, the
-    // MFMAs read buffer st % 2, then stage st + 1 goes from slot (st + 1) % 2
-    // into the other buffer, last read before the previous barrier
-    for (int st0 = 0; st0 < n_stages; st0 += 2) {
+    // step st: slot st % 3 (stored already) takes stage st + 3's loads, the
+    // MFMAs read buffer st % 2, then stage st + 1 goes from slot (st + 1) % 3
+    // into the other buffer, last read before the previous barrier (unrolled
+    // by 6 so that slots and buffers are compile-time registers and offsets)
+    for (int st0 = 0; st0 < n_stages; st0 += 6) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 6; ++u) {
             const int st = st0 + u;
             if (st >= n_stages) break;
-            gload(u, (st + 2) * kStageK);
+            gload(u % 3, (st + 3) * kStageK);
 #pragma unroll
             for (int sub = 0; sub < kStageK / 16; ++sub) {
                 bf16x8_t fa_op[2], fb_op[2];
@@ -112,9 +114,9 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
                 for (int f = 0; f < 2; ++f) {
                     const int ra = 64 * wr + 32 * f + m, rb = 64 * wc + 32 * f + m;
                     fa_op[f] = __builtin_bit_cast(
-                        bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_a[u][ra * kLdsRow + 16 * sub + 8 * h]));
+                        bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_a[u % 2][ra * kLdsRow + 16 * sub + 8 * h]));
                     fb_op[f] = __builtin_bit_cast(
-                        bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_b[u][rb * kLdsRow + 16 * sub + 8 * h]));
+                        bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_b[u % 2][rb * kLdsRow + 16 * sub + 8 * h]));
                 }
 #pragma unroll
                 for (int fa = 0; fa < 2; ++fa)
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
                             __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_op[fa], fb_op[fb], acc[fa][fb], 0, 0, 0);
             }
             if (st + 1 < n_stages) {
-                lstore(u ^ 1, u ^ 1);
+                lstore((u + 1) % 2, (u + 1) % 3);
                 __syncthreads();
             }
         }
