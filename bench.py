@@ -506,8 +506,9 @@ def extra_measurements(dev):
         else:
             fwd = lambda: ar.block_fwd(h, w, S, out=out, lse=lse)
         bwd = lambda: ar.bwd(variant, h, w, g, S=S, dhist=dh, dw=dw, workspace=ws)
-        ms_f = _time(fwd, stream, 5, 2)
-        ms_b = _time(bwd, stream, 3, 1)
+        # ten calls after three warm-up calls each (a few ms per call)
+        ms_f = _time(fwd, stream, 10, 3)
+        ms_b = _time(bwd, stream, 10, 3)
         res[f"{wl.name}_{name}"] = {
             "what": f"{name} forward (all reads, one call) + backward, bf16 in/out, fp32 dw",
             "fwd_ms": ms_f, "bwd_ms": ms_b,
