@@ -27,6 +27,10 @@
 // keeps 16 significant bits (error below 2^-17 of the weight), far below the
 // rounding of the bf16 output; the scores, which also give the fp32
 // log-sum-exp, keep all 24.  Outputs leave as 4 consecutive bf16 per lane.
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -458,18 +462,41 @@ __global__ __launch_bounds__(64 * kBmWaves) void full_batch_mfma_kernel(FwdParam
     }
 }
 
+// Workgroups of `kern` with `lds` bytes of LDS the current device holds at
+// once (CUs times workgroups per CU), looked up once per (kernel, device, LDS).
+hipError_t bm_slots(const void* kern, size_t lds, int64_t* slots) {
+    static std::mutex mu;
+    static std::map<std::tuple<const void*, int, size_t>, int64_t> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const auto key = std::make_tuple(kern, dev, lds);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = cache.find(key);
+        if (it != cache.end()) {
+            *slots = it->second;
+            return hipSuccess;
+        }
+    }
+    int ncu = 0, per_cu = 0;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kBmWaves, lds)) != hipSuccess)
+        return e;
+    *slots = (int64_t)(ncu > 0 ? ncu : 1) * (per_cu > 0 ? per_cu : 1);
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = *slots;
+    return hipSuccess;
+}
+
 template <int NCH>
 hipError_t launch_bm(const FwdParams& p, int n_rows, size_t lds, hipStream_t stream) {
     const void* kern = (const void*)full_batch_mfma_kernel<NCH>;
     hipError_t e = prepare_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;
     // as many workgroups as the device holds at once, each looping over tokens
-    int dev = 0, ncu = 0, per_cu = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kBmWaves, lds)) != hipSuccess)
-        return e;
-    const int64_t slots = (int64_t)ncu * (per_cu > 0 ? per_cu : 1);
+    int64_t slots = 0;
+    if ((e = bm_slots(kern, lds, &slots)) != hipSuccess) return e;
     const int64_t grid = p.T < slots ? p.T : slots;
     hipLaunchKernelGGL(full_batch_mfma_kernel<NCH>, dim3((unsigned)grid), dim3(64 * kBmWaves), lds, stream, p,
                        n_rows);
