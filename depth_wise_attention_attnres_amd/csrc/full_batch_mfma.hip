@@ -18,11 +18,14 @@
 //            tables (fixed order), then the weights alpha, split into two
 //            bf16 parts and stored as the B operand of:
 //   outputs  h_j[e] = sum_i alpha[j][i] v_i[e], m = column e, n = read j, k
-//            over rows in steps of 32.  The rows are gathered down a column
-//            (16-bit LDS reads); within a step, k = 8 g + 2 q + h stands for
-//            row 2 g + 8 q + h (g = lane group, q = register, h = half), so
-//            that the four lane groups of a gather hit disjoint LDS banks; the
-//            weights are stored in the same order.
+//            over rows in steps of 32.  A column of rows comes from two
+//            transposing LDS reads (ds_read_b64_tr_b16: within 16 lanes, lane c
+//            receives element c mod 4 of the 8-byte chunks that lanes 4 e + c / 4,
+//            e = 0..3, fetch), so lane 4 e + q fetches columns 4 q .. 4 q + 3 of
+//            row 8 g + 2 e + s for read s = 0, 1 (g = lane group); within a step,
+//            k = 8 g + 4 s + e stands for that row, which puts the four rows a
+//            16-lane group reads 8 banks apart.  The weights are stored in the
+//            same order.
 // bf16 x bf16 products are exact in fp32.  The weights' two-part bf16 split
 // keeps 16 significant bits (error below 2^-17 of the weight), far below the
 // rounding of the bf16 output; the scores, which also give the fp32
@@ -133,8 +136,12 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8_t& hi, bf16x8
     lo = __builtin_bit_cast(bf16x8_t, l);
 }
 
-// k index, within a step of 32 rows, of row u (0..31) of the step
-__device__ __forceinline__ int bm_kidx(int u) { return 8 * ((u & 7) >> 1) + 2 * (u >> 3) + (u & 1); }
+// k index, within a step of 32 rows, of row u (0..31) of the step: row
+// 8 g + 2 e + s is k = 8 g + 4 s + e
+__device__ __forceinline__ int bm_kidx(int u) { return 8 * (u >> 3) + 4 * (u & 1) + ((u & 7) >> 1); }
+
+typedef short bm_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bm_v4s bm_lds_v4s;
 
 // The dots of one score job with NB row tiles: acc[u] += W (16 reads x d) times
 // row tile u (d x 16 rows), in K-steps of 32.  The query fragments of the next
@@ -402,21 +409,21 @@ __global__ __launch_bounds__(64 * kBmWaves) void full_batch_mfma_kernel(FwdParam
         // the next token's rows, in flight while this token's outputs are formed
         if (t + gridDim.x < p.T) prefetch(t + gridDim.x);
         // wave w takes the column tiles [w ne / 8, (w + 1) ne / 8) (16 columns each).
-        // A column tile's row fragments are gathered once for every row step (the
-        // rows of step ks in column c16: 32 ks + 2 g + 8 q + h; past the last row
-        // the last row, whose weights are zero there or which no read tile uses),
-        // then each read tile in turn multiplies the steps it needs into one
-        // accumulator and stores it (a read past n_q reads the last read's weights
-        // and stores nothing).
+        // A column tile's row fragments are read once for every row step (lane
+        // 4 e + q of lane group g fetches columns 4 q .. 4 q + 3 of row
+        // 32 ks + 8 g + 2 e + s for read s; past the last row the last row, whose
+        // weights are zero there or which no read tile uses), then each read tile
+        // in turn multiplies the steps it needs into one accumulator and stores
+        // it (a read past n_q reads the last read's weights and stores nothing).
         const int ne = d / 16;
         const int et0 = wave * ne / kBmWaves, et1 = (wave + 1) * ne / kBmWaves;
-        int goff[kBmMaxKs][8];
+        int toff[kBmMaxKs][2];
 #pragma unroll
         for (int ks = 0; ks < kBmMaxKs; ++ks)
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int i = 32 * ks + 2 * g + 8 * (m >> 1) + (m & 1);
-                goff[ks][m] = (i < n_rows ? i : n_rows - 1) * dst + c16;
+            for (int sr = 0; sr < 2; ++sr) {
+                const int i = 32 * ks + 8 * g + 2 * (c16 >> 2) + sr;
+                toff[ks][sr] = (i < n_rows ? i : n_rows - 1) * dst + 4 * (c16 & 3);
             }
         const int aplane = n_q * L.ast;  // elements from a weight's hi part to its lo part
         for (int et = et0; et < et1; ++et) {
@@ -424,14 +431,11 @@ __global__ __launch_bounds__(64 * kBmWaves) void full_batch_mfma_kernel(FwdParam
             bf16x8_t xa[kBmMaxKs];
 #pragma unroll
             for (int ks = 0; ks < kBmMaxKs; ++ks) {
-                u32x4 av;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t lo = rows16[goff[ks][2 * q] + e0];
-                    const uint32_t hi = rows16[goff[ks][2 * q + 1] + e0];
-                    av[q] = lo | (hi << 16);
-                }
-                xa[ks] = __builtin_bit_cast(bf16x8_t, av);
+                const bm_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (bm_lds_v4s*)(const_cast<uint16_t*>(rows16) + toff[ks][0] + e0));
+                const bm_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (bm_lds_v4s*)(const_cast<uint16_t*>(rows16) + toff[ks][1] + e0));
+                xa[ks] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
             for (int a = 0; a < L.nrt; ++a) {
                 const int ks_last = (bm_tile_rows(p, a) * 16 - 1) / 32;
