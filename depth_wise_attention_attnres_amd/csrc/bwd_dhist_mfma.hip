@@ -37,6 +37,8 @@ namespace attnres {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short bm_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bm_v4s bm_lds_v4s;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kDmWaves = 8;
@@ -215,14 +217,22 @@ __global__ __launch_bounds__(512) void bwd_dhist_mfma_kernel(BwdParams p, int ns
             __syncthreads();  // the step's 16 rows are in LDS
             bf16x8_t a[2];
             {
-                u32x4 t0, t1;
-                const uint16_t* tc = tb + 64 * wave + m;
+                // rows 8 h + 4 s + e (e = 0..3) of column 64 w + 32 kk + m from
+                // transposing reads (ds_read_b64_tr_b16: within 16 lanes, lane c
+                // receives element c mod 4 of the 8-byte chunks that lanes
+                // 4 e + c / 4 fetch): lane 4 e + q of a 16-lane group fetches
+                // columns 4 q .. 4 q + 3 of the group's 16 of row 8 h + 4 s + e
+                bm_v4s tr[2][2];
+                const int c16 = ln & 15;
+                const uint16_t* tq = tb + (8 * h + (c16 >> 2)) * kDmRow + 64 * wave + 16 * ((ln >> 4) & 1) + 4 * (c16 & 3);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = 8 * h + 2 * q;  // rows r, r + 1 (elements 2 q, 2 q + 1)
-                    t0[q] = (uint32_t)tc[r * kDmRow] | ((uint32_t)tc[(r + 1) * kDmRow] << 16);
-                    t1[q] = (uint32_t)tc[r * kDmRow + 32] | ((uint32_t)tc[(r + 1) * kDmRow + 32] << 16);
-                }
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int sr = 0; sr < 2; ++sr)
+                        tr[kk][sr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (bm_lds_v4s*)(const_cast<uint16_t*>(tq) + 4 * sr * kDmRow + 32 * kk));
+                u32x4 t0 = __builtin_bit_cast(u32x4, __builtin_shufflevector(tr[0][0], tr[0][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                u32x4 t1 = __builtin_bit_cast(u32x4, __builtin_shufflevector(tr[1][0], tr[1][1], 0, 1, 2, 3, 4, 5, 6, 7));
                 // the operands exist here (an empty statement the compiler
                 // cannot move them across): every wave has read the tile when
                 // the next barrier lets the next step write it

@@ -31,6 +31,8 @@ namespace attnres {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short dw_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dw_v4s dw_lds_v4s;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kDwWaves = 8;
@@ -150,14 +152,22 @@ __global__ __launch_bounds__(512) void bwd_dw_mfma_kernel(BwdParams p) {
             __syncthreads();  // the step is in LDS
             bf16x8_t a[2];
             {
-                u32x4 t0, t1;
-                const uint16_t* tc = tile + 64 * wave + m;
+                // tokens 8 h + 4 s + e (e = 0..3) of column 64 w + 32 kk + m from
+                // transposing reads (ds_read_b64_tr_b16: within 16 lanes, lane c
+                // receives element c mod 4 of the 8-byte chunks that lanes
+                // 4 e + c / 4 fetch): lane 4 e + q of a 16-lane group fetches
+                // columns 4 q .. 4 q + 3 of the group's 16 of token 8 h + 4 s + e
+                dw_v4s tr[2][2];
+                const int c16 = ln & 15;
+                const uint16_t* tq = tile + (8 * h + (c16 >> 2)) * kDwRow + 64 * wave + 16 * ((ln >> 4) & 1) + 4 * (c16 & 3);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = 8 * h + 2 * q;  // tokens r, r + 1 (elements 2 q, 2 q + 1)
-                    t0[q] = (uint32_t)tc[r * kDwRow] | ((uint32_t)tc[(r + 1) * kDwRow] << 16);
-                    t1[q] = (uint32_t)tc[r * kDwRow + 32] | ((uint32_t)tc[(r + 1) * kDwRow + 32] << 16);
-                }
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int sr = 0; sr < 2; ++sr)
+                        tr[kk][sr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (dw_lds_v4s*)(const_cast<uint16_t*>(tq) + 4 * sr * kDwRow + 32 * kk));
+                u32x4 t0 = __builtin_bit_cast(u32x4, __builtin_shufflevector(tr[0][0], tr[0][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                u32x4 t1 = __builtin_bit_cast(u32x4, __builtin_shufflevector(tr[1][0], tr[1][1], 0, 1, 2, 3, 4, 5, 6, 7));
                 // the operands exist here (an empty statement the compiler
                 // cannot move them across): every wave has read the tile when
                 // the next barrier lets the next step write it
