@@ -21,6 +21,8 @@
 //             softmax over [frozen sources, partial] (equal to the two-phase
 //             merge), and the weighted sum, rounded once and stored.
 // Lane `ln` owns the 16-byte chunks ln, ln + 64, ... of d.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -63,6 +65,17 @@ __device__ __forceinline__ void bb_lds_read(const float* sl, int c2, int c, floa
 // Lane ln owns chunks ch = c2 * 64 + ln (c2 < NCH) of d; chunks past d are
 // dead: their global loads return zeros and their stores are dropped (buffer
 // range checks), and they skip LDS.
+//
+// Every read needs two passes over its frozen sources: the dots (for the
+// softmax), then the weighted sum.  The sources do not change within a group,
+// so the weighted sum of read l and the dots of read l + 1 share one pass:
+// each source chunk is read from LDS once and feeds both (one LDS read per
+// source, chunk and read instead of two).  Inside the pass, chunk c2 of the
+// partial sum first serves read l's output, then takes row l + 1 and serves
+// read l + 1's dots; the row and query of read l + 2 are requested when the
+// pass ends, one pass ahead of their use.  (Requested chunk by chunk inside the
+// pass, as soon as each register is free, they push the four-chunk variant
+// past 128 VGPRs into spills.)
 template <typename TO, int NCH, int NBMAX, int G>
 __device__ __forceinline__ void bb_group(const FwdParams& p, const float* sl, const float* rsv,
                                         const bf16_t* hist_tok, int64_t t, int ln, int la, int lb) {
@@ -75,99 +88,124 @@ __device__ __forceinline__ void bb_group(const FwdParams& p, const float* sl, co
     const uint32_t w_off = (uint32_t)ln * 32;    // fp32 chunk c2: + 2048 c2
     const uint32_t out_off = (uint32_t)ln * 8 * sizeof(TO);
 
-    float rs2[G + 1];  // RMS scales of the frozen sources, log2 units
-#pragma unroll
-    for (int c = 0; c <= G; ++c) rs2[c] = rsv[c] * kLog2e;
-
     float part[NCH][8];
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) part[c2][e] = 0.f;
-    auto add_row = [&](const Chunk<bf16_t> (&r)[NCH]) {
-#pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2) {
-            float x[8];
-            r[c2].to_float(x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part[c2][e] += x[e];
-        }
+    // row i (its loads read zeros without touching memory when !live)
+    auto row_rsrc = [&](int i, bool live) {
+        return make_rsrc(hist_tok + (live ? i : 0) * row_elems, live ? tok_bytes : 0);
     };
-    auto issue_row = [&](Chunk<bf16_t> (&r)[NCH], int i) {
-        const rsrc_t rr = make_rsrc(hist_tok + i * row_elems, tok_bytes);
-#pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2) r[c2].load(rr, in_off + 1024u * c2);
+    // query of read l (one per read, or one per read and token)
+    auto w_rsrc = [&](int l, bool live) {
+        const int64_t jq = (live ? l : la) - p.q_begin;
+        const float* wrow = p.qtok != nullptr ? p.qtok + (jq * p.T + t) * d : p.w + jq * d;
+        return make_rsrc(wrow, live ? (uint64_t)d * 4 : 0);
     };
     // rows g0+1 .. la-1 (the part of the partial sum before the first read), four at a time
     for (int i0 = g0 + 1; i0 < la; i0 += 4) {
         Chunk<bf16_t> cb[4][NCH];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i0 + u < la) issue_row(cb[u], i0 + u);
+        for (int u = 0; u < 4; ++u) {
+            const rsrc_t rr = row_rsrc(i0 + u, i0 + u < la);
+#pragma unroll
+            for (int c2 = 0; c2 < NCH; ++c2) cb[u][c2].load(rr, in_off + 1024u * c2);
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            if (i0 + u < la) add_row(cb[u]);
+#pragma unroll
+            for (int c2 = 0; c2 < NCH; ++c2) {
+                float x[8];
+                cb[u][c2].to_float(x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part[c2][e] += x[e];
+            }
     }
-    Chunk<bf16_t> rl[NCH];  // row l of the current read, in flight
-    if (la > g0) issue_row(rl, la);
-    // query of the current read, in flight; its fp32 bits are used in place,
-    // and the next read's query is requested once the dots are done
+    // row and query of the next read to be scored, in flight
+    Chunk<bf16_t> rl[NCH];
     Chunk<float> wq[NCH];
-    auto issue_w = [&](int l) {
-        const int64_t jq = l - p.q_begin;  // one query per read, or one per read and token
-        const float* wrow = p.qtok != nullptr ? p.qtok + (jq * p.T + t) * d : p.w + jq * d;
-        const rsrc_t wr = make_rsrc(wrow, (uint64_t)d * 4);
+    {
+        const rsrc_t rr = row_rsrc(la, la > g0);  // read g0 has no partial sum
+        const rsrc_t wr = w_rsrc(la, true);
 #pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2) wq[c2].load(wr, w_off + 2048u * c2);
-    };
-    issue_w(la);
+        for (int c2 = 0; c2 < NCH; ++c2) {
+            rl[c2].load(rr, in_off + 1024u * c2);
+            wq[c2].load(wr, w_off + 2048u * c2);
+        }
+    }
 
-    for (int l = la; l <= lb; ++l) {
-        const bool has_p = l > g0;
-        if (has_p) add_row(rl);             // row l joins the partial sum
-        if (l < lb) issue_row(rl, l + 1);   // the next read's row (always past g0)
-
-        // dots with the frozen sources and the partial sum
-        // (source by source, each fenced off for the scheduler, so that only
-        // one source's chunks are in registers at a time)
-        float v[kV];
+    float a[G + 1];  // weights of the frozen sources and of the partial sum
+    float ap = 0.f;
+    // One pass over the sources: read lo's weighted sum (OUT) and/or the dots of
+    // read lo + 1 (DOT; for the first read, lo + 1 = la and there is no output).
+    // Row lo + 1 joins the partial sum in a DOT pass; its registers and the
+    // query's then take row and query lo + 2.
+    auto pass = [&](auto out_tag, auto dot_tag, int lo, float (&v)[kV]) {
+        constexpr bool OUT = decltype(out_tag)::value;
+        constexpr bool DOT = decltype(dot_tag)::value;
+        const int ln2 = lo + 2;
+        const bool live2 = ln2 <= lb;
+        const rsrc_t rr2 = row_rsrc(ln2, DOT && live2);
+        const rsrc_t wr2 = w_rsrc(ln2, DOT && live2);
+        const rsrc_t orr = make_rsrc(static_cast<TO*>(p.out) + (int64_t)((OUT ? lo : la) - p.q_begin) * row_elems + t * d,
+                                     OUT ? (uint64_t)d * sizeof(TO) : 0);
 #pragma unroll
         for (int j = 0; j < kV; ++j) v[j] = 0.f;
 #pragma unroll
         for (int c2 = 0; c2 < NCH; ++c2) {
-            float wv[8];
-            wq[c2].to_float(wv);
+            const int ch = c2 * 64 + ln;
+            float o[8];
+            if constexpr (OUT) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                v[G + 1] = fmaf(wv[e], part[c2][e], v[G + 1]);
-                v[G + 2] = fmaf(part[c2][e], part[c2][e], v[G + 2]);
+                for (int e = 0; e < 8; ++e) o[e] = ap * part[c2][e];
             }
-        }
+            float wv[8];
+            if constexpr (DOT) {
+                float x[8];
+                rl[c2].to_float(x);
 #pragma unroll
-        for (int c = 0; c <= G; ++c) {
+                for (int e = 0; e < 8; ++e) part[c2][e] += x[e];
+                wq[c2].to_float(wv);
 #pragma unroll
-            for (int c2 = 0; c2 < NCH; ++c2) {
-                const int ch = c2 * 64 + ln;
-                if (ch < p.nc) {
-                    float wv[8], x[8];
-                    wq[c2].to_float(wv);
-                    bb_lds_read<NCH, NBMAX>(sl, c2, c, x);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[c] = fmaf(wv[e], x[e], v[c]);
+                for (int e = 0; e < 8; ++e) {
+                    v[G + 1] = fmaf(wv[e], part[c2][e], v[G + 1]);
+                    v[G + 2] = fmaf(part[c2][e], part[c2][e], v[G + 2]);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
+            if (ch < p.nc) {
+#pragma unroll
+                for (int c = 0; c <= G; ++c) {
+                    float x[8];
+                    bb_lds_read<NCH, NBMAX>(sl, c2, c, x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if constexpr (OUT) o[e] = fmaf(a[c], x[e], o[e]);
+                        if constexpr (DOT) v[c] = fmaf(wv[e], x[e], v[c]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if constexpr (OUT) store_chunk((TO*)nullptr, orr, out_off + 8u * sizeof(TO) * 64u * c2, o);
         }
-        if (l < lb) issue_w(l + 1);
+        if constexpr (DOT) {
+#pragma unroll
+            for (int c2 = 0; c2 < NCH; ++c2) {
+                rl[c2].load(rr2, in_off + 1024u * c2);
+                wq[c2].load(wr2, w_off + 2048u * c2);
+            }
+        }
+    };
+    // the exact softmax over [v_0, b_1..b_G, partial] of read l from its dots
+    auto coeffs = [&](int l, const float (&v)[kV]) {
+        const bool has_p = l > g0;
         float tot[kV];
         wave_totals<0, kV>(v, tot, ln);
-
-        // exact softmax over [v_0, b_1..b_G, partial]
         float s[G + 1];
         float M = -INFINITY;
 #pragma unroll
         for (int c = 0; c <= G; ++c) {
-            s[c] = rs2[c] * tot[c];
+            s[c] = rsv[c] * kLog2e * tot[c];  // RMS scales from LDS, when the read is scored
             M = fmaxf(M, s[c]);
         }
         float sp = -INFINITY;
@@ -175,7 +213,6 @@ __device__ __forceinline__ void bb_group(const FwdParams& p, const float* sl, co
             sp = fast_rsqrt(fmaf(tot[G + 2], p.inv_d, p.eps)) * tot[G + 1] * kLog2e;
             M = fmaxf(M, sp);
         }
-        float a[G + 1];
         float Z = 0.f;
 #pragma unroll
         for (int c = 0; c <= G; ++c) {
@@ -187,30 +224,8 @@ __device__ __forceinline__ void bb_group(const FwdParams& p, const float* sl, co
         const float inv = 1.0f / Z;
 #pragma unroll
         for (int c = 0; c <= G; ++c) a[c] *= inv;
-        const float ap = ep * inv;
-
-        // the weighted sum
+        ap = ep * inv;
         const int64_t j = l - p.q_begin;
-        const rsrc_t orr = make_rsrc(static_cast<TO*>(p.out) + j * row_elems + t * d,
-                                     (uint64_t)d * sizeof(TO));
-#pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2) {
-            const int ch = c2 * 64 + ln;
-            float o[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = ap * part[c2][e];
-            if (ch < p.nc) {
-#pragma unroll
-                for (int c = 0; c <= G; ++c) {
-                    float x[8];
-                    bb_lds_read<NCH, NBMAX>(sl, c2, c, x);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) o[e] = fmaf(a[c], x[e], o[e]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            store_chunk((TO*)nullptr, orr, out_off + 8u * sizeof(TO) * 64u * c2, o);
-        }
         if (p.lse != nullptr && ln == 0) p.lse[j * p.T + t] = (M + fast_log2(Z)) * kLn2;
         if (p.alpha != nullptr) {  // weight probe in source order, zeros past the sources
             const int ns = G + 1 + (has_p ? 1 : 0);
@@ -223,7 +238,17 @@ __device__ __forceinline__ void bb_group(const FwdParams& p, const float* sl, co
                 p.alpha[(j * p.n_hist + x) * p.T + t] = ax;
             }
         }
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    float v[kV];
+    pass(no{}, yes{}, la - 1, v);  // dots of read la
+    coeffs(la, v);
+    for (int l = la; l < lb; ++l) {
+        pass(yes{}, yes{}, l, v);  // output of read l, dots of read l + 1
+        coeffs(l + 1, v);
     }
+    pass(yes{}, no{}, lb, v);  // output of read lb
 }
 
 template <typename TO, int NCH, int NBMAX, int G = 0>
@@ -235,6 +260,60 @@ __device__ __forceinline__ void bb_dispatch(int g, const FwdParams& p, const flo
         else
             bb_dispatch<TO, NCH, NBMAX, G + 1>(g, p, sl, rsv, hist_tok, t, ln, la, lb);
     }
+}
+
+// Source c of a token (v_0 for c = 0, else the sum of block c's rows) in fp32
+// into the LDS planes at `src`, and its RMS scale into rsv[c].  Rows are
+// requested four at a time.
+template <int NCH, int NBMAX>
+__device__ __forceinline__ void bb_form_source(const FwdParams& p, float* src, float* rsv, const bf16_t* hist_tok,
+                                               int c, int ln) {
+    const int S = p.S;
+    const int64_t row_elems = p.T * (int64_t)p.d;
+    const uint64_t tok_bytes = (uint64_t)p.d * 2;
+    const int i0 = c == 0 ? 0 : (c - 1) * S + 1;
+    const int i1 = c == 0 ? 0 : c * S;  // inclusive; c * S <= last read < n_hist
+    float acc[NCH][8];
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[c2][e] = 0.f;
+    for (int ib = i0; ib <= i1; ib += 4) {
+        Chunk<bf16_t> ch[4][NCH];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (ib + u <= i1) {
+                const rsrc_t rr = make_rsrc(hist_tok + (ib + u) * row_elems, tok_bytes);
+#pragma unroll
+                for (int c2 = 0; c2 < NCH; ++c2) ch[u][c2].load(rr, (uint32_t)ln * 16 + 1024u * c2);
+            }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (ib + u <= i1) {
+#pragma unroll
+                for (int c2 = 0; c2 < NCH; ++c2) {
+                    float x[8];
+                    ch[u][c2].to_float(x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[c2][e] += x[e];
+                }
+            }
+    }
+    float sq = 0.f;
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq = fmaf(acc[c2][e], acc[c2][e], sq);
+        if (c2 * 64 + ln < p.nc) {  // the two planes of the chunk (see BbLds)
+            float* dst = src + 4 * ln;
+            *reinterpret_cast<f32x4*>(dst + BbLds<NCH, NBMAX>::at(0, c2, c)) =
+                f32x4{acc[c2][0], acc[c2][1], acc[c2][2], acc[c2][3]};
+            *reinterpret_cast<f32x4*>(dst + BbLds<NCH, NBMAX>::at(1, c2, c)) =
+                f32x4{acc[c2][4], acc[c2][5], acc[c2][6], acc[c2][7]};
+        }
+    }
+    sq = tg_sum<64>(sq);
+    if (ln == 0) rsv[c] = fast_rsqrt(fmaf(sq, p.inv_d, p.eps));
 }
 
 template <typename TO, int NCH, int NBMAX>
@@ -250,59 +329,13 @@ void block_batch_kernel(FwdParams p, int nb) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ln = threadIdx.x & 63;
     const int64_t t = blockIdx.x;
-    const int d = p.d, S = p.S;
-    const int64_t row_elems = p.T * (int64_t)d;
-    const bf16_t* hist_tok = static_cast<const bf16_t*>(p.hist) + t * d;
-    const uint64_t tok_bytes = (uint64_t)d * 2;
+    const int S = p.S;
+    const bf16_t* hist_tok = static_cast<const bf16_t*>(p.hist) + t * p.d;
 
     if (threadIdx.x == 0) *counter = 0;
 
     // ---- prologue: frozen sources v_0, b_1, ... in fp32, their RMS scales ------
-    for (int c = wave; c < nb; c += kBbWaves) {
-        const int i0 = c == 0 ? 0 : (c - 1) * S + 1;
-        const int i1 = c == 0 ? 0 : c * S;  // inclusive; c * S <= last read < n_hist
-        float acc[NCH][8];
-#pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[c2][e] = 0.f;
-        for (int ib = i0; ib <= i1; ib += 4) {
-            Chunk<bf16_t> ch[4][NCH];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (ib + u <= i1) {
-                    const rsrc_t rr = make_rsrc(hist_tok + (ib + u) * row_elems, tok_bytes);
-#pragma unroll
-                    for (int c2 = 0; c2 < NCH; ++c2) ch[u][c2].load(rr, (uint32_t)ln * 16 + 1024u * c2);
-                }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (ib + u <= i1) {
-#pragma unroll
-                    for (int c2 = 0; c2 < NCH; ++c2) {
-                        float x[8];
-                        ch[u][c2].to_float(x);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[c2][e] += x[e];
-                    }
-                }
-        }
-        float sq = 0.f;
-#pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sq = fmaf(acc[c2][e], acc[c2][e], sq);
-            if (c2 * 64 + ln < p.nc) {  // the two planes of the chunk (see BbLds)
-                float* dst = src + 4 * ln;
-                *reinterpret_cast<f32x4*>(dst + ((0 * NCH + c2) * NBMAX + c) * 256) =
-                    f32x4{acc[c2][0], acc[c2][1], acc[c2][2], acc[c2][3]};
-                *reinterpret_cast<f32x4*>(dst + ((1 * NCH + c2) * NBMAX + c) * 256) =
-                    f32x4{acc[c2][4], acc[c2][5], acc[c2][6], acc[c2][7]};
-            }
-        }
-        sq = tg_sum<64>(sq);
-        if (ln == 0) rsv[c] = fast_rsqrt(fmaf(sq, p.inv_d, p.eps));
-    }
+    for (int c = wave; c < nb; c += kBbWaves) bb_form_source<NCH, NBMAX>(p, src, rsv, hist_tok, c, ln);
     __syncthreads();
 
     // ---- block groups, latest group first ---------------------------------------

@@ -466,33 +466,6 @@ __global__ __launch_bounds__(64 * kBmWaves) void full_batch_mfma_kernel(FwdParam
     }
 }
 
-// Workgroups of `kern` with `lds` bytes of LDS the current device holds at
-// once (CUs times workgroups per CU), looked up once per (kernel, device, LDS).
-hipError_t bm_slots(const void* kern, size_t lds, int64_t* slots) {
-    static std::mutex mu;
-    static std::map<std::tuple<const void*, int, size_t>, int64_t> cache;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    const auto key = std::make_tuple(kern, dev, lds);
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        const auto it = cache.find(key);
-        if (it != cache.end()) {
-            *slots = it->second;
-            return hipSuccess;
-        }
-    }
-    int ncu = 0, per_cu = 0;
-    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kBmWaves, lds)) != hipSuccess)
-        return e;
-    *slots = (int64_t)(ncu > 0 ? ncu : 1) * (per_cu > 0 ? per_cu : 1);
-    std::lock_guard<std::mutex> lock(mu);
-    cache[key] = *slots;
-    return hipSuccess;
-}
-
 template <int NCH>
 hipError_t launch_bm(const FwdParams& p, int n_rows, size_t lds, hipStream_t stream) {
     const void* kern = (const void*)full_batch_mfma_kernel<NCH>;
@@ -500,7 +473,7 @@ hipError_t launch_bm(const FwdParams& p, int n_rows, size_t lds, hipStream_t str
     if (e != hipSuccess) return e;
     // as many workgroups as the device holds at once, each looping over tokens
     int64_t slots = 0;
-    if ((e = bm_slots(kern, lds, &slots)) != hipSuccess) return e;
+    if ((e = resident_workgroups(kern, 64 * kBmWaves, lds, &slots)) != hipSuccess) return e;
     const int64_t grid = p.T < slots ? p.T : slots;
     hipLaunchKernelGGL(full_batch_mfma_kernel<NCH>, dim3((unsigned)grid), dim3(64 * kBmWaves), lds, stream, p,
                        n_rows);

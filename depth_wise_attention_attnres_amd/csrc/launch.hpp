@@ -179,5 +179,9 @@ int device_max_lds();
 // it under each other), and returns hipErrorInvalidValue if `bytes` exceeds
 // that maximum.
 hipError_t prepare_dynamic_lds(const void* kernel, size_t bytes);
+// Workgroups of `threads` threads and `lds` bytes of dynamic LDS that the
+// current device holds at once (CUs times workgroups per CU), for persistent
+// grids; looked up once per (kernel, device, threads, LDS).
+hipError_t resident_workgroups(const void* kernel, int threads, size_t lds, int64_t* slots);
 
 }  // namespace attnres

@@ -7,8 +7,10 @@
 // lowered; each call only checks that its own size fits.
 #include <hip/hip_runtime.h>
 
+#include <map>
 #include <mutex>
 #include <set>
+#include <tuple>
 #include <utility>
 
 #include "launch.hpp"
@@ -43,6 +45,30 @@ hipError_t prepare_dynamic_lds(const void* kernel, size_t bytes) {
     e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     if (e == hipSuccess) g_raised.insert({kernel, dev});
     return e;
+}
+
+hipError_t resident_workgroups(const void* kernel, int threads, size_t lds, int64_t* slots) {
+    static std::mutex mu;
+    static std::map<std::tuple<const void*, int, int, size_t>, int64_t> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const auto key = std::make_tuple(kernel, dev, threads, lds);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = cache.find(key);
+        if (it != cache.end()) {
+            *slots = it->second;
+            return hipSuccess;
+        }
+    }
+    int ncu = 0, per_cu = 0;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds)) != hipSuccess) return e;
+    *slots = (int64_t)(ncu > 0 ? ncu : 1) * (per_cu > 0 ? per_cu : 1);
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = *slots;
+    return hipSuccess;
 }
 
 }  // namespace attnres

@@ -76,6 +76,33 @@ def test_block_group_kernel(ar, oracle, odt, n_hist, T, d, S, q_begin):
     check_lse(to_f64(lse), ref_lse)
 
 
+# The per-group Block kernel on many tokens (several hundred workgroups, ragged
+# counts) at every element against the oracle: reads starting inside a group,
+# four chunks per lane at the 128K workload's d and S; then four chunks per lane
+# with more than nine sources (the 13-source instantiation).
+@pytest.mark.parametrize("n_hist,T,d,S,q_begin", [(33, 805, 256, 4, 0), (49, 601, 1024, 4, 3),
+                                                  (65, 700, 2048, 8, 0), (40, 523, 520, 5, 13)])
+def test_block_group_kernel_many_tokens(ar, oracle, n_hist, T, d, S, q_begin):
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=T + d + S, dtype="bf16", w_sigma=0.05)
+    n_q = n_hist - q_begin
+    out, lse = ar.block_fwd(h, w[q_begin:].contiguous(), S, q_begin=q_begin, n_q=n_q)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.block_fwd(h64, w64[q_begin:], S, q_begin=q_begin, n_q=n_q)
+    check_out(to_f64(out), ref, "bf16")
+    check_lse(to_f64(lse), ref_lse)
+
+
+@pytest.mark.parametrize("n_hist,T,d,S", [(65, 9, 2048, 6), (49, 5, 1600, 4)])
+def test_block_group_kernel_four_chunks_many_sources(ar, oracle, n_hist, T, d, S):
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=T * 3 + S, dtype="bf16", w_sigma=0.05)
+    assert 10 <= 1 + (n_hist - 1) // S <= 13
+    out, lse = ar.block_fwd(h, w, S)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.block_fwd(h64, w64, S)
+    check_out(to_f64(out), ref, "bf16")
+    check_lse(to_f64(lse), ref_lse)
+
+
 def test_block_S1_matches_full_kernel(ar):
     h, w, _, _ = _inputs(12, 300, 512, seed=4, dtype="f32")
     ob, lb = ar.block_fwd(h, w, 1)
