@@ -116,6 +116,7 @@ PROFILE_WORKLOADS = {
     "bwd_L24_d1024_block_S4": "Block AttnRes (S=4) backward, 48 sublayers + embedding, d=1024, 16384 tokens",
     "block_S8_d2048_128k_model_order": "Block AttnRes S=8 in model order (phase 1 per group, phase 2 per row)",
     "full_L32_d896_batched": "Full AttnRes forward, all 65 reads in one call (rows staged in LDS)",
+    "proj_L32_d896": "input-dependent query q_l = W_l v_l of all 65 reads, d=896, 16384 tokens",
 }
 
 
@@ -139,6 +140,23 @@ def profile_run(name):
         dw = torch.empty((n, d), dtype=torch.float32, device=dev)
         for _ in range(2):
             ar.bwd(variant, h, w, g, S=S, dhist=dh, dw=dw, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"profile run done: {name} ({PROFILE_WORKLOADS[name]}), history copy "
+              f"{h.numel() * h.element_size()} bytes", flush=True)
+        return
+    if name == "proj_L32_d896":
+        wl = WORKLOADS["full_L32_d896"]
+        h, _, _ = device_inputs(wl, dev)
+        n, T, d = h.shape
+        dst = torch.empty_like(h)
+        dst.copy_(h)
+        del dst
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(wl.seed + 101)
+        W = (torch.randn((n, d, d), generator=gen, device=dev) * (0.05 / d ** 0.5)).to(torch.bfloat16)
+        q = torch.empty((n, T, d), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            ar.query_proj(h, W, q=q)
         torch.cuda.synchronize()
         print(f"profile run done: {name} ({PROFILE_WORKLOADS[name]}), history copy "
               f"{h.numel() * h.element_size()} bytes", flush=True)

@@ -18,32 +18,43 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 }  // namespace
 
-// Workgroup tile: 128 tokens x 128 outputs; wave (wr, wc) of the 2 x 2 waves
-// computes 64 x 64 as 2 x 2 fragments of 32 x 32, so each operand fragment
-// read from LDS feeds two matrix instructions.  K goes in stages of 64
-// elements through double-buffered LDS: the workgroup loads a stage's 128
-// token rows and 128 W rows (contiguous in k, 16 bytes per lane) three stages
-// ahead of its multiplication; one barrier per stage.  (Passing the fp32 results
+// Workgroup tile: 256 tokens x 128 outputs; wave (wr, wc) of the 2 x 2 waves
+// computes 128 x 64 as 4 x 2 fragments of 32 x 32, so each token fragment read
+// from LDS feeds two matrix instructions and each W fragment four (6 LDS reads
+// per 8 instructions; 64 x 64 per wave took 4 per 4).  K goes in stages of 32
+// elements through double-buffered LDS (60 KB: two workgroups per CU): the
+// workgroup loads a stage's 256 token rows and 128 W rows (contiguous in k, 16
+// bytes per lane) three stages ahead of its multiplication; one barrier per
+// stage.  (Measured on the L=32 / d=896 workload, all 65 reads: 128 x 128
+// tiles with 64-wide stages 2.82-2.90 ms, with 32-wide stages at three waves
+// per SIMD 2.75-2.95 ms, this tile 2.78-2.81 ms.  Passing the fp32 results
 // through LDS for 16-byte stores measured slower: one more barrier and round
 // trip against 4-byte stores that already fill 128-byte lines per wave.)
-constexpr int kTileM = 128, kTileN = 128, kStageK = 64;
+constexpr int kTileM = 256, kTileN = 128, kStageK = 32;
+constexpr int kFa = kTileM / 64, kFb = kTileN / 64;  // 32 x 32 fragments per wave (2 x 2 waves)
 constexpr int kLdsRow = kStageK + 8;  // bf16 elements per LDS row (padded: staggers the banks)
 
-__global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q,
-                                                         int64_t T, int d, int tiles_t, int tiles_o) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, int d, int tiles_t,
+                       int tiles_o, int64_t n_groups) {
     __shared__ __attribute__((aligned(16))) bf16_t lds_a[2][kTileM * kLdsRow];
     __shared__ __attribute__((aligned(16))) bf16_t lds_b[2][kTileN * kLdsRow];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, ln = tid & 63;
     const int h = ln >> 5, m = ln & 31;
     const int wr = wave >> 1, wc = wave & 1;
-    // blockIdx.x = (read j, token tile, output tile), output tiles fastest so
-    // that the workgroups sharing a token tile run together and reuse it in L2
-    const int64_t blk = blockIdx.x;
-    const int to = (int)(blk % tiles_o);
-    const int64_t rest = blk / tiles_o;
-    const int tt = (int)(rest % tiles_t);
-    const int64_t j = rest / tiles_t;
+    // The tiles_o workgroups of one (read j, token tile) read the same token
+    // rows, and the token tiles of one read share W_j: a group is numbered so
+    // that its members run on one XCD, together, and consecutive groups on an
+    // XCD take consecutive token tiles of the same read (numbered in XCD order
+    // the members landed on different XCDs, each of whose L2 fetched the token
+    // tile again: 8.9x the input bytes fetched).
+    int64_t grp;
+    int to;
+    xcd_group(blockIdx.x, tiles_o, grp, to);
+    if (grp >= n_groups) return;  // (the grid is rounded up to whole XCD rounds)
+    const int tt = (int)(grp % tiles_t);
+    const int64_t j = grp / tiles_t;
     const int64_t t0 = (int64_t)tt * kTileM;
     const int o0 = to * kTileN;
     const bf16_t* xj = x + j * T * d;
@@ -52,7 +63,8 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
     // global -> LDS: thread tid moves the 16-byte chunks (row, kc) =
     // (idx / kCh, idx % kCh), idx = tid + 256 c, of each operand tile
     constexpr int kCh = kStageK / 8;                 // 16-byte chunks per row
-    constexpr int kPer = kTileM * kCh / 256;         // chunks per thread and operand
+    constexpr int kPerA = kTileM * kCh / 256;        // chunks per thread of the token tile
+    constexpr int kPerB = kTileN * kCh / 256;        // and of the W tile
     // Buffer loads over the tile's token rows and output rows: a chunk past T,
     // d or the last column loads zeros, without branches (a load inside a
     // branch makes every later wait drain all loads in flight).  Three register
@@ -61,33 +73,33 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
     const int n_out = d - o0 < kTileN ? d - o0 : kTileN;
     const rsrc_t ra_x = make_rsrc(xj + t0 * d, (uint64_t)n_tok * d * 2);
     const rsrc_t rb_w = make_rsrc(wj + (int64_t)o0 * d, (uint64_t)n_out * d * 2);
-    u32x4 sa[3][kPer], sb[3][kPer];
+    u32x4 sa[3][kPerA], sb[3][kPerB];
     auto gload = [&](int slot, int k0) {
 #pragma unroll
-        for (int c = 0; c < kPer; ++c) {
+        for (int c = 0; c < kPerA; ++c) {
             const int idx = tid + 256 * c;
             const int row = idx / kCh, kc = idx % kCh;
             const int k = k0 + 8 * kc;
             const uint32_t off = k < d ? (uint32_t)(row * d + k) * 2u : kOOB;
             sa[slot][c] = __builtin_amdgcn_raw_buffer_load_b128(ra_x, off, 0, 0);
-            sb[slot][c] = __builtin_amdgcn_raw_buffer_load_b128(rb_w, off, 0, 0);
+            if (c < kPerB) sb[slot][c] = __builtin_amdgcn_raw_buffer_load_b128(rb_w, off, 0, 0);
         }
     };
     auto lstore = [&](int buf, int slot) {
 #pragma unroll
-        for (int c = 0; c < kPer; ++c) {
+        for (int c = 0; c < kPerA; ++c) {
             const int idx = tid + 256 * c;
             const int row = idx / kCh, kc = idx % kCh;
             *reinterpret_cast<u32x4*>(&lds_a[buf][row * kLdsRow + 8 * kc]) = sa[slot][c];
-            *reinterpret_cast<u32x4*>(&lds_b[buf][row * kLdsRow + 8 * kc]) = sb[slot][c];
+            if (c < kPerB) *reinterpret_cast<u32x4*>(&lds_b[buf][row * kLdsRow + 8 * kc]) = sb[slot][c];
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[kFa][kFb];
 #pragma unroll
-    for (int fa = 0; fa < 2; ++fa)
+    for (int fa = 0; fa < kFa; ++fa)
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
+        for (int fb = 0; fb < kFb; ++fb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fa][fb][r] = 0.f;
 
@@ -109,19 +121,23 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
             gload(u % 3, (st + 3) * kStageK);
 #pragma unroll
             for (int sub = 0; sub < kStageK / 16; ++sub) {
-                bf16x8_t fa_op[2], fb_op[2];
+                bf16x8_t fa_op[kFa], fb_op[kFb];
 #pragma unroll
-                for (int f = 0; f < 2; ++f) {
-                    const int ra = 64 * wr + 32 * f + m, rb = 64 * wc + 32 * f + m;
+                for (int f = 0; f < kFa; ++f) {
+                    const int ra = (kTileM / 2) * wr + 32 * f + m;
                     fa_op[f] = __builtin_bit_cast(
                         bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_a[u % 2][ra * kLdsRow + 16 * sub + 8 * h]));
+                }
+#pragma unroll
+                for (int f = 0; f < kFb; ++f) {
+                    const int rb = (kTileN / 2) * wc + 32 * f + m;
                     fb_op[f] = __builtin_bit_cast(
                         bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_b[u % 2][rb * kLdsRow + 16 * sub + 8 * h]));
                 }
 #pragma unroll
-                for (int fa = 0; fa < 2; ++fa)
+                for (int fa = 0; fa < kFa; ++fa)
 #pragma unroll
-                    for (int fb = 0; fb < 2; ++fb)
+                    for (int fb = 0; fb < kFb; ++fb)
                         acc[fa][fb] =
                             __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_op[fa], fb_op[fb], acc[fa][fb], 0, 0, 0);
             }
@@ -131,17 +147,17 @@ __global__ __launch_bounds__(256) void query_proj_kernel(const bf16_t* x, const 
             }
         }
     }
-    // lane j, register r of fragment (fa, fb) holds token t0 + 64 wr + 32 fa + i,
-    // output o0 + 64 wc + 32 fb + m, with i = 8 (r / 4) + 4 h + r % 4
+    // lane j, register r of fragment (fa, fb) holds token t0 + (kTileM / 2) wr +
+    // 32 fa + i, output o0 + (kTileN / 2) wc + 32 fb + m, i = 8 (r / 4) + 4 h + r % 4
 #pragma unroll
-    for (int fa = 0; fa < 2; ++fa)
+    for (int fa = 0; fa < kFa; ++fa)
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb) {
-            const int out = o0 + 64 * wc + 32 * fb + m;
+        for (int fb = 0; fb < kFb; ++fb) {
+            const int out = o0 + (kTileN / 2) * wc + 32 * fb + m;
             if (out < d) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t ti = t0 + 64 * wr + 32 * fa + 8 * (r / 4) + 4 * h + r % 4;
+                    const int64_t ti = t0 + (kTileM / 2) * wr + 32 * fa + 8 * (r / 4) + 4 * h + r % 4;
                     if (ti < T) q[(j * T + ti) * d + out] = acc[fa][fb][r];
                 }
             }
@@ -152,10 +168,11 @@ hipError_t launch_query_proj(const void* x, const void* W, float* q, int64_t n_q
                              hipStream_t stream) {
     const int tiles_t = (int)((T + kTileM - 1) / kTileM);
     const int tiles_o = (d + kTileN - 1) / kTileN;
-    const int64_t blocks = n_q * tiles_t * (int64_t)tiles_o;
+    const int64_t n_groups = n_q * tiles_t;  // (read, token tile) pairs
+    const int64_t blocks = (int64_t)kNumXcd * tiles_o * ((n_groups + kNumXcd - 1) / kNumXcd);
     hipLaunchKernelGGL(query_proj_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), q, T, d,
-                       tiles_t, tiles_o);
+                       tiles_t, tiles_o, n_groups);
     return hipGetLastError();
 }
 

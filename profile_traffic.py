@@ -46,6 +46,8 @@ def main():
                          "bench.py --profile run: trace, HBM counters per dispatch, SQ counters")
     ap.add_argument("--copy-bytes", type=float, help="bytes read (= written) by the calibration copy")
     ap.add_argument("--alg-bytes", type=float, help="algorithmic bytes of one run of the workload")
+    ap.add_argument("--alg-flops", type=float, help="algorithmic FLOPs of one run (matrix-core kernels)")
+    ap.add_argument("--flops-peak", type=float, default=2500.0, help="dense peak in TFLOP/s for --alg-flops")
     ap.add_argument("--sq", nargs="*", default=[], help="counter CSVs of SQ passes")
     ap.add_argument("--name", default="full_fwd_stream_L32_d896")
     ap.add_argument("--kernel", default="full_fwd_stream_kernel")
@@ -186,7 +188,11 @@ def kernel_summary(args):
                      f"{float(r['TotalDurationNs']):.0f} |")
     gbs = args.alg_bytes / (total_ns * 1e-9) / 1e9
     lines += ["", f"One run: {total_ns / 1e6:.2f} ms of kernel time; algorithmic bytes "
-              f"{args.alg_bytes / 1e9:.2f} GB -> {gbs:.0f} GB/s = {gbs / 80:.1f}% of 8 TB/s.", "",
+              f"{args.alg_bytes / 1e9:.2f} GB -> {gbs:.0f} GB/s = {gbs / 80:.1f}% of 8 TB/s." +
+              (f" Algorithmic FLOPs {args.alg_flops / 1e12:.3f} T -> "
+               f"{args.alg_flops / (total_ns * 1e-9) / 1e12:.0f} TFLOP/s = "
+               f"{100 * args.alg_flops / (total_ns * 1e-9) / 1e12 / args.flops_peak:.1f}% of the "
+               f"{args.flops_peak:.0f} TFLOP/s dense peak." if args.alg_flops else ""), "",
               "## HBM traffic of one run (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
               f"Calibration on the history copy ({args.copy_bytes / 1e9:.2f} GB read and written): "
               f"FETCH_SIZE x {f_fac:.3f}, WRITE_SIZE x {w_fac:.3f}.", "",
