@@ -24,7 +24,11 @@ def _bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("n_q,T,d", [(1, 5, 8), (3, 70, 64), (2, 100, 136), (2, 33, 2048), (1, 129, 896)])
+# small and ragged shapes, then several 256-token tiles per read with (read,
+# token tile) group counts that are not multiples of the 8 XCD rounds, ragged
+# last token and output tiles, and d = 2048 (16 output tiles)
+@pytest.mark.parametrize("n_q,T,d", [(1, 5, 8), (3, 70, 64), (2, 100, 136), (2, 33, 2048), (1, 129, 896),
+                                     (9, 700, 136), (3, 1037, 896), (2, 513, 2048), (11, 256, 64)])
 def test_query_proj_matches_oracle(ar, oracle, n_q, T, d):
     rng = np.random.default_rng(n_q * 7 + d)
     x = _bf16(rng.standard_normal((n_q, T, d)))
