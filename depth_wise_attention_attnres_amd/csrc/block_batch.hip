@@ -144,11 +144,12 @@ __device__ __forceinline__ void bb_group(const FwdParams& p, const float* sl, co
     auto pass = [&](auto out_tag, auto dot_tag, int lo, float (&v)[kV]) {
         constexpr bool OUT = decltype(out_tag)::value;
         constexpr bool DOT = decltype(dot_tag)::value;
-        const int ln2 = lo + 2;
-        const bool live2 = ln2 <= lb;
-        const rsrc_t rr2 = row_rsrc(ln2, DOT && live2);
-        const rsrc_t wr2 = w_rsrc(ln2, DOT && live2);
-        const rsrc_t orr = make_rsrc(static_cast<TO*>(p.out) + (int64_t)((OUT ? lo : la) - p.q_begin) * row_elems + t * d,
+        const int l2 = lo + 2;  // the read whose row and query are requested next
+        const bool live2 = l2 <= lb;
+        const rsrc_t rr2 = row_rsrc(l2, DOT && live2);
+        const rsrc_t wr2 = w_rsrc(l2, DOT && live2);
+        const int64_t jo = (OUT ? lo : la) - p.q_begin;  // output row of read lo
+        const rsrc_t orr = make_rsrc(static_cast<TO*>(p.out) + jo * row_elems + t * d,
                                      OUT ? (uint64_t)d * sizeof(TO) : 0);
 #pragma unroll
         for (int j = 0; j < kV; ++j) v[j] = 0.f;
