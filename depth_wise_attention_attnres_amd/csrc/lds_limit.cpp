@@ -1,4 +1,5 @@
-// lds_limit.cpp -- dynamic-LDS limits of the kernels that stage data in LDS.
+// lds_limit.cpp -- dynamic-LDS limits of the kernels that stage data in LDS,
+// and the resident-workgroup counts that size persistent grids.
 //
 // A kernel's dynamic-LDS limit is an attribute of the function, shared by the
 // whole process.  Setting it per call to what that call needs would let one
@@ -47,6 +48,9 @@ hipError_t prepare_dynamic_lds(const void* kernel, size_t bytes) {
     return e;
 }
 
+// A persistent grid holds as many workgroups as the device runs at once; the
+// count depends only on (kernel, device, threads, LDS), so it is queried once
+// and cached under a lock (read-only afterwards).
 hipError_t resident_workgroups(const void* kernel, int threads, size_t lds, int64_t* slots) {
     static std::mutex mu;
     static std::map<std::tuple<const void*, int, int, size_t>, int64_t> cache;

@@ -39,10 +39,11 @@
  * Memory and execution:
  *   * All tensor pointers are device pointers owned by the caller; the library
  *     allocates no device memory and keeps no state between calls apart from
- *     the thread-local error string and the dynamic-LDS limit of its
- *     LDS-staged kernels, which it raises to the device maximum once per
- *     kernel and device (never lowered).  The backward's scratch is
- *     caller-supplied.
+ *     the thread-local error string, the dynamic-LDS limit of its LDS-staged
+ *     kernels, which it raises to the device maximum once per kernel and
+ *     device (never lowered), and a cache of how many workgroups of each
+ *     persistent kernel a device holds at once (queried once).  The
+ *     backward's scratch is caller-supplied.
  *   * d must be a multiple of 8 (8 <= d <= 4096); hist, out, dout, dhist and w
  *     must be 16-byte aligned, lse / rinv / dw 4-byte aligned.
  *   * T < 2^22 tokens and n_hist * T * d <= 2^40 elements per call
@@ -55,7 +56,7 @@
  *   * T == 0 or n_q == 0 is a valid empty call: nothing is launched.
  *   * NaN / Inf inputs propagate; they are not checked.
  *   * Thread-safe: calls share no mutable state apart from the one-time LDS
- *     limit above, which is set under a lock.
+ *     limit and workgroup-count cache above, both set under a lock.
  *
  * Status: every entry point returns an attnres_status; attnres_last_error()
  * gives a human-readable detail of the last failure on the calling thread.
