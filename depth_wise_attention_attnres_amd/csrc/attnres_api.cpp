@@ -195,11 +195,11 @@ int attnres_query_proj(const void* x, attnres_dtype x_dtype, int64_t n_q, int64_
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: only bf16 x and W (the matrix-core path)", fn);
     if (T > attnres::kMaxTokens)
         return fail(ATTNRES_ERR_UNSUPPORTED, "%s: T = %" PRId64 " exceeds 2^22 - 1 tokens per call", fn, T);
-    // one 256-work-item workgroup per 256 x 128 tile, the (read, token tile)
+    // one 512-work-item workgroup per 256 x 256 tile, the (read, token tile)
     // groups rounded up to a multiple of 8 (one round per XCD); 32-bit
-    // work-item count (checked on 128-token tiles: a bound, not the grid)
-    if (8 * ((d + 127) / 128) * ((n_q * ((T + 127) / 128) + 7) / 8) >= ((int64_t)1 << 24))
-        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: too many tiles for one launch (n_q x T x d >= 2^38)", fn);
+    // work-item count
+    if (8 * ((d + 255) / 256) * ((n_q * ((T + 255) / 256) + 7) / 8) >= ((int64_t)1 << 23))
+        return fail(ATTNRES_ERR_UNSUPPORTED, "%s: too many tiles for one launch (n_q x T x d >= 2^39)", fn);
     if (n_q == 0 || T == 0) return ok();
     if (x == nullptr || W == nullptr || q == nullptr) return fail(ATTNRES_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     if (!aligned(x, 16) || !aligned(W, 16) || !aligned(q, 16))

@@ -18,31 +18,37 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 }  // namespace
 
-// Workgroup tile: 256 tokens x 128 outputs; wave (wr, wc) of the 2 x 2 waves
+// Workgroup tile: 256 tokens x 256 outputs; wave (wr, wc) of the 2 x 4 waves
 // computes 128 x 64 as 4 x 2 fragments of 32 x 32, so each token fragment read
 // from LDS feeds two matrix instructions and each W fragment four (6 LDS reads
-// per 8 instructions; 64 x 64 per wave took 4 per 4).  K goes in stages of 32
-// elements through double-buffered LDS (60 KB: two workgroups per CU): the
-// workgroup loads a stage's 256 token rows and 128 W rows (contiguous in k, 16
-// bytes per lane) three stages ahead of its multiplication; one barrier per
-// stage.  (Measured on the L=32 / d=896 workload, all 65 reads: 128 x 128
-// tiles with 64-wide stages 2.82-2.90 ms, with 32-wide stages at three waves
-// per SIMD 2.75-2.95 ms, this tile 2.78-2.81 ms.  Passing the fp32 results
-// through LDS for 16-byte stores measured slower: one more barrier and round
-// trip against 4-byte stores that already fill 128-byte lines per wave.)
-constexpr int kTileM = 256, kTileN = 128, kStageK = 32;
-constexpr int kFa = kTileM / 64, kFb = kTileN / 64;  // 32 x 32 fragments per wave (2 x 2 waves)
+// per 8 instructions).  K goes in stages of 32 elements through
+// double-buffered LDS (80 KB, one workgroup of 8 waves per CU): the workgroup
+// loads a stage's 256 token rows and 256 W rows (contiguous in k, 16 bytes per
+// lane) three stages ahead of its multiplication; one barrier per stage.  The
+// call is bound by moving the operands into the CUs, not by the matrix cores
+// (timed without the matrix instructions it takes 95% as long, without the
+// operand loads 60%): every token tile crosses L2 once per output tile and
+// every W tile once per token tile, so the tile is as large as the registers
+// allow (256 x 128 tiles: 2.78-2.92 ms; this tile 2.53-2.59 ms, on the L=32 /
+// d=896 workload, all 65 reads).  Passing the fp32 results through LDS for
+// 16-byte stores measured slower: one more barrier and round trip against
+// 4-byte stores that already fill 128-byte lines per wave.
+constexpr int kTileM = 256, kTileN = 256, kStageK = 32;
+constexpr int kWavesM = 2, kWavesN = 4, kThreads = 64 * kWavesM * kWavesN;
+// 32 x 32 fragments per wave along tokens and outputs
+constexpr int kFa = kTileM / kWavesM / 32, kFb = kTileN / kWavesN / 32;
 constexpr int kLdsRow = kStageK + 8;  // bf16 elements per LDS row (padded: staggers the banks)
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, int d, int tiles_t,
                        int tiles_o, int64_t n_groups) {
-    __shared__ __attribute__((aligned(16))) bf16_t lds_a[2][kTileM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) bf16_t lds_b[2][kTileN * kLdsRow];
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    auto lds_a = reinterpret_cast<bf16_t (*)[kTileM * kLdsRow]>(lds_raw);
+    auto lds_b = reinterpret_cast<bf16_t (*)[kTileN * kLdsRow]>(lds_raw + 2 * kTileM * kLdsRow * sizeof(bf16_t));
     const int tid = threadIdx.x;
     const int wave = tid >> 6, ln = tid & 63;
     const int h = ln >> 5, m = ln & 31;
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wr = wave / kWavesN, wc = wave % kWavesN;
     // The tiles_o workgroups of one (read j, token tile) read the same token
     // rows, and the token tiles of one read share W_j: a group is numbered so
     // that its members run on one XCD, together, and consecutive groups on an
@@ -61,10 +67,10 @@ void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, in
     const bf16_t* wj = W + j * (int64_t)d * d;
 
     // global -> LDS: thread tid moves the 16-byte chunks (row, kc) =
-    // (idx / kCh, idx % kCh), idx = tid + 256 c, of each operand tile
+    // (idx / kCh, idx % kCh), idx = tid + kThreads c, of each operand tile
     constexpr int kCh = kStageK / 8;                 // 16-byte chunks per row
-    constexpr int kPerA = kTileM * kCh / 256;        // chunks per thread of the token tile
-    constexpr int kPerB = kTileN * kCh / 256;        // and of the W tile
+    constexpr int kPerA = kTileM * kCh / kThreads;   // chunks per thread of the token tile
+    constexpr int kPerB = kTileN * kCh / kThreads;   // and of the W tile
     // Buffer loads over the tile's token rows and output rows: a chunk past T,
     // d or the last column loads zeros, without branches (a load inside a
     // branch makes every later wait drain all loads in flight).  Three register
@@ -77,7 +83,7 @@ void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, in
     auto gload = [&](int slot, int k0) {
 #pragma unroll
         for (int c = 0; c < kPerA; ++c) {
-            const int idx = tid + 256 * c;
+            const int idx = tid + kThreads * c;
             const int row = idx / kCh, kc = idx % kCh;
             const int k = k0 + 8 * kc;
             const uint32_t off = k < d ? (uint32_t)(row * d + k) * 2u : kOOB;
@@ -88,7 +94,7 @@ void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, in
     auto lstore = [&](int buf, int slot) {
 #pragma unroll
         for (int c = 0; c < kPerA; ++c) {
-            const int idx = tid + 256 * c;
+            const int idx = tid + kThreads * c;
             const int row = idx / kCh, kc = idx % kCh;
             *reinterpret_cast<u32x4*>(&lds_a[buf][row * kLdsRow + 8 * kc]) = sa[slot][c];
             if (c < kPerB) *reinterpret_cast<u32x4*>(&lds_b[buf][row * kLdsRow + 8 * kc]) = sb[slot][c];
@@ -104,6 +110,9 @@ void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, in
             for (int r = 0; r < 16; ++r) acc[fa][fb][r] = 0.f;
 
     const int n_stages = (d + kStageK - 1) / kStageK;
+    // a wave whose output columns all lie past d (the last output tile when
+    // d is not a multiple of the tile) only helps stage the operands
+    const bool cols_live = o0 + (kTileN / kWavesN) * wc < d;
     gload(0, 0);
     gload(1, kStageK);  // past d: zeros, never stored
     gload(2, 2 * kStageK);
@@ -121,16 +130,17 @@ void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, in
             gload(u % 3, (st + 3) * kStageK);
 #pragma unroll
             for (int sub = 0; sub < kStageK / 16; ++sub) {
+                if (!cols_live) break;  // (wave-uniform) this wave's outputs lie past d
                 bf16x8_t fa_op[kFa], fb_op[kFb];
 #pragma unroll
                 for (int f = 0; f < kFa; ++f) {
-                    const int ra = (kTileM / 2) * wr + 32 * f + m;
+                    const int ra = (kTileM / kWavesM) * wr + 32 * f + m;
                     fa_op[f] = __builtin_bit_cast(
                         bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_a[u % 2][ra * kLdsRow + 16 * sub + 8 * h]));
                 }
 #pragma unroll
                 for (int f = 0; f < kFb; ++f) {
-                    const int rb = (kTileN / 2) * wc + 32 * f + m;
+                    const int rb = (kTileN / kWavesN) * wc + 32 * f + m;
                     fb_op[f] = __builtin_bit_cast(
                         bf16x8_t, *reinterpret_cast<const u32x4*>(&lds_b[u % 2][rb * kLdsRow + 16 * sub + 8 * h]));
                 }
@@ -153,11 +163,11 @@ void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, in
     for (int fa = 0; fa < kFa; ++fa)
 #pragma unroll
         for (int fb = 0; fb < kFb; ++fb) {
-            const int out = o0 + (kTileN / 2) * wc + 32 * fb + m;
+            const int out = o0 + (kTileN / kWavesN) * wc + 32 * fb + m;
             if (out < d) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t ti = t0 + (kTileM / 2) * wr + 32 * fa + 8 * (r / 4) + 4 * h + r % 4;
+                    const int64_t ti = t0 + (kTileM / kWavesM) * wr + 32 * fa + 8 * (r / 4) + 4 * h + r % 4;
                     if (ti < T) q[(j * T + ti) * d + out] = acc[fa][fb][r];
                 }
             }
@@ -170,7 +180,10 @@ hipError_t launch_query_proj(const void* x, const void* W, float* q, int64_t n_q
     const int tiles_o = (d + kTileN - 1) / kTileN;
     const int64_t n_groups = n_q * tiles_t;  // (read, token tile) pairs
     const int64_t blocks = (int64_t)kNumXcd * tiles_o * ((n_groups + kNumXcd - 1) / kNumXcd);
-    hipLaunchKernelGGL(query_proj_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+    constexpr size_t lds = (size_t)2 * (kTileM + kTileN) * kLdsRow * sizeof(bf16_t);
+    const hipError_t e = prepare_dynamic_lds((const void*)query_proj_kernel, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(query_proj_kernel, dim3((unsigned)blocks), dim3(kThreads), lds, stream,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W), q, T, d,
                        tiles_t, tiles_o, n_groups);
     return hipGetLastError();

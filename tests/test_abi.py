@@ -242,7 +242,7 @@ def test_query_proj_and_full_fwd_q_validation(ar):
     assert lib.attnres_query_proj(P, BF16, 2, 16, 64, P2, BF16, P3 + 4, None) == ALIGN
     assert lib.attnres_query_proj(P, BF16, 0, 16, 64, None, BF16, None, None) == OK
     assert lib.attnres_query_proj(P, 7, 2, 16, 64, P2, BF16, P3, None) == INVALID
-    # one launch: at most 2^24 tiles of 128 x 128 (2^32 work-items), and T < 2^22
+    # one launch: at most 2^23 tiles of 256 x 256 (2^32 work-items), and T < 2^22
     assert lib.attnres_query_proj(P, BF16, 64, 1 << 21, 4096, P2, BF16, P3, None) == UNSUPPORTED
     assert "tiles" in ar.last_error()
     assert lib.attnres_query_proj(P, BF16, 1, 1 << 22, 64, P2, BF16, P3, None) == UNSUPPORTED
