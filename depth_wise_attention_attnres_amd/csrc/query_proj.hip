@@ -66,8 +66,8 @@ void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, in
     const bf16_t* xj = x + j * T * d;
     const bf16_t* wj = W + j * (int64_t)d * d;
 
-    // global -> LDS: thread tid moves kPerA chunks of 16 bytes of the token
-    // tile and kPerB of the W tile per stage (stage_chunk below)
+    // global -> LDS: thread tid moves the 16-byte chunks (row, kc) =
+    // (idx / kCh, idx % kCh), idx = tid + kThreads c, of each operand tile
     constexpr int kCh = kStageK / 8;                 // 16-byte chunks per row
     constexpr int kPerA = kTileM * kCh / kThreads;   // chunks per thread of the token tile
     constexpr int kPerB = kTileN * kCh / kThreads;   // and of the W tile
@@ -79,23 +79,12 @@ void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, in
     const int n_out = d - o0 < kTileN ? d - o0 : kTileN;
     const rsrc_t ra_x = make_rsrc(xj + t0 * d, (uint64_t)n_tok * d * 2);
     const rsrc_t rb_w = make_rsrc(wj + (int64_t)o0 * d, (uint64_t)n_out * d * 2);
-    // chunk c of this thread: row and 16-byte column of the stage.  A wave's
-    // 64 lanes take 16 rows x kCh chunks, 16 consecutive lanes 16 rows of one
-    // column, so that every 8 lanes' LDS stores fall in distinct banks (rows
-    // kLdsRow apart); the wave's load still covers the same 16 row segments.
-    static_assert(kCh == 4, "a wave stages 16 rows of 4 chunks");
-    auto stage_chunk = [&](int c, int& row, int& kc) {
-        const int idx = tid + kThreads * c;
-        const int lane = idx & 63;
-        row = 16 * (idx >> 6) + (lane & 15);
-        kc = lane >> 4;
-    };
     u32x4 sa[3][kPerA], sb[3][kPerB];
     auto gload = [&](int slot, int k0) {
 #pragma unroll
         for (int c = 0; c < kPerA; ++c) {
-            int row, kc;
-            stage_chunk(c, row, kc);
+            const int idx = tid + kThreads * c;
+            const int row = idx / kCh, kc = idx % kCh;
             const int k = k0 + 8 * kc;
             const uint32_t off = k < d ? (uint32_t)(row * d + k) * 2u : kOOB;
             sa[slot][c] = __builtin_amdgcn_raw_buffer_load_b128(ra_x, off, 0, 0);
@@ -105,8 +94,8 @@ void query_proj_kernel(const bf16_t* x, const bf16_t* W, float* q, int64_t T, in
     auto lstore = [&](int buf, int slot) {
 #pragma unroll
         for (int c = 0; c < kPerA; ++c) {
-            int row, kc;
-            stage_chunk(c, row, kc);
+            const int idx = tid + kThreads * c;
+            const int row = idx / kCh, kc = idx % kCh;
             *reinterpret_cast<u32x4*>(&lds_a[buf][row * kLdsRow + 8 * kc]) = sa[slot][c];
             if (c < kPerB) *reinterpret_cast<u32x4*>(&lds_b[buf][row * kLdsRow + 8 * kc]) = sb[slot][c];
         }
