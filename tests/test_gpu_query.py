@@ -148,3 +148,22 @@ def test_block_fwd_q_workload_sampled(ar, oracle):
     stats = check_out(to_f64(out.index_select(1, idx)), ref, "bf16")
     check_lse(to_f64(lse.index_select(1, idx)), ref_lse)
     print(f"block_fwd_q 128K sampled: {stats}", flush=True)
+
+
+def test_query_proj_workload_sampled(ar, oracle):
+    # the projection of all 65 reads of the L=32 / d=896 / 16384-token history
+    # at full size (the launch bench.py times: 64 token tiles per read, a
+    # ragged last output tile), W ~ N(0, 0.05^2 / d) as in the benchmark;
+    # sampled tokens against the oracle (tokens are independent)
+    from depth_wise_attention_attnres_amd.workloads import WORKLOADS, device_inputs, token_sample
+    wl = WORKLOADS["full_L32_d896"]
+    h, _, _ = device_inputs(wl, DEV)
+    n, T, d = h.shape
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(wl.seed + 101)
+    W = (torch.randn((n, d, d), generator=gen, device=DEV) * (0.05 / d ** 0.5)).to(torch.bfloat16)
+    q = ar.query_proj(h, W)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(token_sample(T, 96, seed=wl.seed)).to(DEV)
+    ref = oracle.query_proj(to_f64(h.index_select(1, idx)), to_f64(W))
+    check_rel(to_f64(q.index_select(1, idx)), ref, 1e-5, "q")
