@@ -3,6 +3,7 @@
 // the thread-local error detail, then dispatch to the kernel launchers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cinttypes>
 #include <cmath>
 #include <cstdarg>
@@ -159,6 +160,25 @@ int full_fwd_impl(const char* fn, const void* hist, attnres_dtype hist_dtype, in
     p.out_dt = out_dtype;
     p.eps = eps;
     p.inv_d = 1.0f / (float)d;
+    // A call with more history rows than the matrix-core kernel stages: its
+    // leading reads (those that see few enough rows) go there, the rest to the
+    // kernel that takes the call otherwise.  The first part writes the RMS
+    // cache of the rows it reads, which the second then trusts.
+    const int n1 = attnres::full_batch_mfma_prefix(p, hist_dtype, out_dtype);
+    if (n1 > 0) {
+        attnres::FullFwdParams p1 = p;
+        p1.n_q = n1;
+        hipError_t e = attnres::launch_full_fwd(p1, hist_dtype, out_dtype, stream);
+        if (e != hipSuccess) return hip_status(fn, e);
+        const size_t out_elem = out_dtype == ATTNRES_BF16 ? 2 : 4;
+        p.q_begin += n1;
+        p.n_q -= n1;
+        p.w = w + (int64_t)n1 * d;
+        p.out = static_cast<char*>(out) + (size_t)n1 * (size_t)T * (size_t)d * out_elem;
+        if (lse != nullptr) p.lse = lse + (int64_t)n1 * T;
+        if (alpha != nullptr) p.alpha = alpha + (int64_t)n1 * n_hist * T;
+        if (rinv != nullptr) p.rinv_valid = std::max(p.rinv_valid, p.q_begin);
+    }
     return hip_status(fn, attnres::launch_full_fwd(p, hist_dtype, out_dtype, stream));
 }
 

@@ -30,6 +30,7 @@
 // keeps 16 significant bits (error below 2^-17 of the weight), far below the
 // rounding of the bf16 output; the scores, which also give the fp32
 // log-sum-exp, keep all 24.  Outputs leave as 4 consecutive bf16 per lane.
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -506,6 +507,17 @@ int64_t bm_plan(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt)
 
 bool full_batch_mfma_applies(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt) {
     return bm_plan(p, hist_dt, out_dt) > 0;
+}
+
+int full_batch_mfma_prefix(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt) {
+    if (bm_plan(p, hist_dt, out_dt) > 0) return 0;  // the kernel takes the whole call
+    FwdParams q = p;
+    // the most reads whose rows (0 .. q_begin + n - 1) the kernel stages
+    for (int n = std::min(p.n_q - 1, 16 * kBmMaxTiles - p.q_begin); n >= kBmMinReads; --n) {
+        q.n_q = n;
+        if (bm_plan(q, hist_dt, out_dt) > 0) return n;
+    }
+    return 0;
 }
 
 hipError_t launch_full_batch_mfma(const FwdParams& p, hipStream_t stream) {

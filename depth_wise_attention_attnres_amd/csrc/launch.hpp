@@ -53,6 +53,10 @@ hipError_t launch_full_fwd(const FullFwdParams& p, attnres_dtype hist_dt, attnre
 // every row staged in LDS, both contractions on the matrix cores
 bool full_batch_mfma_applies(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt);
 hipError_t launch_full_batch_mfma(const FwdParams& p, hipStream_t stream);
+// For a call that kernel cannot take whole (more history rows than it stages):
+// the most leading reads it can take (their rows 0 .. q_begin + n - 1 fit),
+// or 0 (the whole call fits, or no prefix of at least its minimum does)
+int full_batch_mfma_prefix(const FwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt);
 hipError_t launch_block_fwd(const BlockFwdParams& p, attnres_dtype hist_dt, attnres_dtype out_dt,
                             hipStream_t stream);
 // Full reads of a call with many reads, served from the token's rows staged in

@@ -40,6 +40,12 @@ int main() {
                             nullptr, nullptr, nullptr, nullptr) == ATTNRES_ERR_INVALID_ARG);
     EXPECT(attnres_full_fwd(P(1), B, 9, (int64_t)1 << 23, 64, F(2), 0, 9, 1e-6f, nullptr, 0, P(3), B,
                             nullptr, nullptr, nullptr, nullptr, nullptr) == ATTNRES_ERR_UNSUPPORTED);
+    {   // a call the stubs split between two launches (leading reads, then the rest)
+        const int before = g_launches;
+        EXPECT(attnres_full_fwd(P(1), B, 40, 16, 64, F(2), 0, 40, 1e-6f, F(4), 3, P(3), B, F(5),
+                                nullptr, nullptr, F(6), nullptr) == ATTNRES_OK);
+        EXPECT(g_launches == before + 2);
+    }
     EXPECT(attnres_full_fwd(P(1), B, 9, 16, 64, F(2), 0, 9, 1e-6f, F(4), 3, P(3), B, nullptr,
                             nullptr, nullptr, nullptr, nullptr) == ATTNRES_OK);
     EXPECT(attnres_full_fwd(P(1), B, 9, 16, 64, F(2), 0, 9, 1e-6f, nullptr, 3, P(3), B, nullptr,

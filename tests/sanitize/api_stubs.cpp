@@ -27,6 +27,10 @@ BwdLayout bwd_layout(int64_t S, int64_t n_hist, int64_t T, int64_t d, int64_t n_
     return L;
 }
 hipError_t launch_full_fwd(const FwdParams&, attnres_dtype, attnres_dtype, hipStream_t) { ++g_launches; return hipSuccess; }
+// split calls with many reads, so that the split path's offsets run under the sanitizers
+int full_batch_mfma_prefix(const FwdParams& p, attnres_dtype, attnres_dtype) {
+    return p.n_q >= 32 && p.qtok == nullptr && p.normed == nullptr ? p.n_q / 2 : 0;
+}
 hipError_t launch_block_fwd(const FwdParams&, attnres_dtype, attnres_dtype, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_query_proj(const void*, const void*, float*, int64_t, int64_t, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_block_phase1(const Phase1Params&, hipStream_t) { ++g_launches; return hipSuccess; }

@@ -287,3 +287,30 @@ def test_batch_mfma_alpha_probe(ar, oracle, q_begin):
     for j in range(n_q):
         assert (a[j, q_begin + j + 1:] == 0).all()
     check_out(to_f64(out), ref_out, "bf16")
+
+
+# A call with more history rows than the matrix-core kernel stages (80 at two
+# chunks per lane): its leading reads go to that kernel, the rest to the
+# vector kernel, which trusts the RMS cache rows the first part wrote.  Every
+# output, lse, weight probe and cache row against the oracle, from read 0 and
+# from a later first read, with and without an earlier valid cache prefix.
+@pytest.mark.parametrize("n_hist,T,d,q_begin,valid", [(100, 23, 640, 0, 0), (100, 19, 640, 30, 7),
+                                                      (141, 6, 640, 0, 0)])
+def test_batch_split_between_kernels(ar, oracle, n_hist, T, d, q_begin, valid):
+    n_q = n_hist - q_begin
+    h, w, h64, w64 = _inputs(n_hist, T, d, seed=n_hist + q_begin, dtype="bf16", w_sigma=0.05)
+    rinv = torch.full((n_hist, T), float("nan"), device=DEV)
+    if valid:
+        ar.full_fwd(h, w[:valid], q_begin=0, n_q=valid, rinv=rinv)
+    alpha = torch.full((n_q, n_hist, T), float("nan"), device=DEV)
+    out, lse = ar.full_fwd(h, w[q_begin:].contiguous(), q_begin=q_begin, n_q=n_q, rinv=rinv,
+                           rinv_valid_rows=valid, alpha=alpha)
+    torch.cuda.synchronize()
+    ref, ref_lse, ref_a = oracle.fwd(oracle.FULL, h64, w64[q_begin:], q_begin=q_begin, n_q=n_q,
+                                     want_alpha=True)
+    check_out(to_f64(out), ref, "bf16")
+    check_lse(to_f64(lse), ref_lse)
+    check_rel(to_f64(alpha), ref_a.transpose(0, 2, 1), 1e-5, "alpha")
+    r = to_f64(rinv)
+    r_ref = 1.0 / np.sqrt((h64 ** 2).mean(axis=2) + 1e-6)
+    np.testing.assert_allclose(r, r_ref, rtol=2e-6)
