@@ -291,11 +291,12 @@ def test_batch_mfma_alpha_probe(ar, oracle, q_begin):
 
 # A call with more history rows than the matrix-core kernel stages (80 at two
 # chunks per lane): its leading reads go to that kernel, the rest to the
-# vector kernel, which trusts the RMS cache rows the first part wrote.  Every
+# vector kernel (or, for fewer than 16 remaining reads, the streaming kernel),
+# which trusts the RMS cache rows the first part wrote.  Every
 # output, lse, weight probe and cache row against the oracle, from read 0 and
 # from a later first read, with and without an earlier valid cache prefix.
 @pytest.mark.parametrize("n_hist,T,d,q_begin,valid", [(100, 23, 640, 0, 0), (100, 19, 640, 30, 7),
-                                                      (141, 6, 640, 0, 0)])
+                                                      (141, 6, 640, 0, 0), (90, 17, 640, 0, 3)])
 def test_batch_split_between_kernels(ar, oracle, n_hist, T, d, q_begin, valid):
     n_q = n_hist - q_begin
     h, w, h64, w64 = _inputs(n_hist, T, d, seed=n_hist + q_begin, dtype="bf16", w_sigma=0.05)
