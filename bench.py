@@ -117,6 +117,7 @@ PROFILE_WORKLOADS = {
     "block_S8_d2048_128k_model_order": "Block AttnRes S=8 in model order (phase 1 per group, phase 2 per row)",
     "full_L32_d896_batched": "Full AttnRes forward, all 65 reads in one call (rows staged in LDS)",
     "proj_L32_d896": "input-dependent query q_l = W_l v_l of all 65 reads, d=896, 16384 tokens",
+    "full_L70_d640_batched": "Full AttnRes forward, all 141 reads in one call, d=640, 16384 tokens",
 }
 
 
@@ -161,7 +162,8 @@ def profile_run(name):
         print(f"profile run done: {name} ({PROFILE_WORKLOADS[name]}), history copy "
               f"{h.numel() * h.element_size()} bytes", flush=True)
         return
-    wl = WORKLOADS["full_L32_d896" if name == "full_L32_d896_batched" else "block_S8_d2048_128k"]
+    wl = WORKLOADS[{"full_L32_d896_batched": "full_L32_d896",
+                    "full_L70_d640_batched": "full_L70_d640"}.get(name, "block_S8_d2048_128k")]
     h, w, _ = device_inputs(wl, dev)
     n, T, d = h.shape
     dst = torch.empty_like(h)
@@ -169,7 +171,7 @@ def profile_run(name):
     del dst
     out = torch.empty_like(h)
     lse = torch.empty((n, T), dtype=torch.float32, device=dev)
-    if name == "full_L32_d896_batched":
+    if name in ("full_L32_d896_batched", "full_L70_d640_batched"):
         fn = lambda: ar.full_fwd(h, w, out=out, lse=lse)
     elif name == "block_S8_d2048_128k":
         fn = lambda: ar.block_fwd(h, w, wl.S, out=out, lse=lse)
