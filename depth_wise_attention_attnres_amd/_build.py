@@ -22,7 +22,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-    # packed fp32 VALU ops stay off (see the build notes in the design doc)
+    # packed fp32 VALU instructions stay off: the compiler would otherwise form
+    # them from plain float code, and the kernels are validated without them
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
     "-I", INCLUDE, "-I", CSRC,

@@ -1,6 +1,6 @@
 """Turn rocprofv3 outputs into the committed profile summaries.
 
-Inputs (CSV files written by rocprofv3 under gpurun_out/):
+Inputs (CSV files that rocprofv3 writes into its -d directory):
   --trace-stats  <..._kernel_stats.csv>       from  --kernel-trace --stats
   --fetch        <..._counter_collection.csv> from  --pmc FETCH_SIZE
   --write        <..._counter_collection.csv> from  --pmc WRITE_SIZE
@@ -108,10 +108,10 @@ def main():
     lines = [
         f"# {args.name}: Full AttnRes forward, read by read, L=32 / d=896 / 16384 tokens, bf16",
         "",
-        "Commands (run from /tmp with TMPDIR=/tmp on the GPU box; $R = the repo root):",
+        "Commands (run from /tmp with TMPDIR=/tmp on the machine that holds the GPU; $R = the repo root):",
         "",
         "```",
-        args.commands.strip() or "(see DESIGN.md)",
+        args.commands.strip() or "(commands not given)",
         "```",
         "",
         "## rocprofv3 --kernel-trace --stats",
@@ -179,7 +179,7 @@ def kernel_summary(args):
     st = [r for r in rows(args.trace_stats) if any(k in r["Name"] for k in args.kernel.split(","))]
     total_ns = sum(float(r["TotalDurationNs"]) for r in st) / 2  # per run (two runs)
     lines = [f"# {args.name}: {args.kernel_summary}", "",
-             "Commands (run from /tmp with TMPDIR=/tmp on the GPU box; $R = the repo root):", "",
+             "Commands (run from /tmp with TMPDIR=/tmp on the machine that holds the GPU; $R = the repo root):", "",
              "```", args.commands.strip(), "```", "",
              "## rocprofv3 --kernel-trace --stats", "",
              "| kernel | calls | average ns | total ns |", "|---|---|---|---|"]
@@ -219,7 +219,7 @@ def stats_only(args):
     lines = [
         f"# {args.name}: {args.stats_only}",
         "",
-        "Commands (run from /tmp with TMPDIR=/tmp on the GPU box; $R = the repo root):",
+        "Commands (run from /tmp with TMPDIR=/tmp on the machine that holds the GPU; $R = the repo root):",
         "",
         "```",
         args.commands.strip(),
