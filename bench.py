@@ -278,6 +278,35 @@ def main():
     launch_gbs = {str(l): bytes_per_launch[l] / (ev[l][0].elapsed_time(ev[l][1]) * 1e-3) / 1e9
                   for l in probe}
 
+    # diagnostic (with the extras): the same launches with a 1 GiB fill before
+    # each one, which leaves the caches full of dirty lines as a model's
+    # sublayer between two reads would; HIP events around each launch only (the
+    # fill lies outside them), the best of three sweeps per launch
+    cache_cleared = None
+    if not args.no_extra:
+        junk = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cleared = [float("inf")] * n
+        for _ in range(3):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+            for l in range(n):
+                junk.fill_(float(l))
+                evs[l][0].record(stream)
+                ar.full_fwd(hist, w_rows[l], q_begin=l, n_q=1, rinv=rinv, rinv_valid_rows=l,
+                            out=out_rows[l], lse=lse_rows[l])
+                evs[l][1].record(stream)
+            torch.cuda.synchronize()
+            cleared = [min(c, a.elapsed_time(b)) for c, (a, b) in zip(cleared, evs)]
+        del junk
+        cleared_ms = sum(cleared)
+        cleared_gbs = sum(bytes_per_launch) / (cleared_ms * 1e-3) / 1e9
+        cache_cleared = {
+            "what": "kernel time of one step's 65 launches, each after a 1 GiB fill (caches dirty)",
+            "kernel_ms_per_step": cleared_ms,
+            "achieved_GBps": cleared_gbs,
+            "frac": cleared_gbs / HBM_PEAK_GBS,
+        }
+
     # context: a plain device-to-device copy of the same size as one step's
     # history (read + write), the achievable streaming rate on this machine
     src = hist.view(-1)
@@ -330,6 +359,8 @@ def main():
         "wall_s_timed": wall,
         "device": torch.cuda.get_device_name(dev),
     }
+    if cache_cleared is not None:
+        result["cache_cleared"] = cache_cleared
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, hist, w)
     if not args.no_extra:
