@@ -308,7 +308,7 @@ def main():
         }
 
     # context: a plain device-to-device copy of the same size as one step's
-    # history (read + write), the achievable streaming rate on this machine
+    # history (read + write), the achievable streaming rate of this device
     src = hist.view(-1)
     dst = torch.empty_like(src)
     for _ in range(3):
